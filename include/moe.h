@@ -1,0 +1,198 @@
+/*
+ * moe.h — C ABI of libmoe.so: one expert-parallel rank's share of an MoE layer
+ * on one MI355X (gfx950), with the W token-owner ranks emulated as W
+ * receive buffers in HBM.
+ *
+ * Source: the reading-notes page "MoE 计算-通信细粒度重叠：用 Tile 级信号把 All-to-All
+ * 藏在 GEMM 背后" on Cui, Wingkvist and Ericsson, "Fine-grained Computation-
+ * Communication Overlap via Tile-level Signaling and Scheduling for Mixture-of-
+ * Experts" ("the tile-signal notes" below).  Section numbers are the notes'.
+ *
+ * Conventions for every entry point
+ *   - Returns a moe_status (0 = MOE_OK).  Arguments are validated on the host
+ *     before any HIP call; nothing is enqueued when validation fails.
+ *   - Device pointers are plain device addresses (hipMalloc or a torch
+ *     tensor's data_ptr()).  bf16 tensors are passed as uint16_t bit patterns
+ *     and must be 16-byte aligned; int32/uint32/float tensors 4-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call is asynchronous on it; nothing synchronises with the host
+ *     except moe_device_status.
+ *   - The caller owns every buffer.  The library allocates no device memory.
+ *     Its only state is a per-device cache of two CU-masked streams and a few
+ *     events for the overlapped combine (moe_release_streams frees them).
+ *   - Errors the device detects (an expert id out of range, a received-row
+ *     count that disagrees with the routing, a consumer wait that timed out)
+ *     are written to an error word inside the plan workspace and reported by
+ *     moe_device_status.
+ */
+#ifndef MOE_EXPERT_TILE_MOE_H
+#define MOE_EXPERT_TILE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,       /* bad shape, null or misaligned pointer, bad option */
+  MOE_ECAPACITY = 2,    /* a size exceeds what the plan workspace was sized for */
+  MOE_EHIP = 3,         /* a HIP runtime call failed */
+  MOE_ETIMEOUT = 4,     /* device: the consumer's bounded wait for a tile flag ran out */
+  MOE_EROUTING = 5,     /* device: expert id out of range, or R disagrees with the routing */
+  MOE_EUNSUPPORTED = 6  /* no GPU, or a device other than gfx950 */
+} moe_status;
+
+/* The pages' statement of the problem (tile-signal notes §4.4, input of the
+ * layout + schedule pseudo-code: routing, local rank, number of ranks, experts
+ * per rank, tile height tb_M) plus the layer sizes and the segment merge
+ * factor of §5.2. */
+typedef struct moe_shape {
+  int32_t world;            /* W: ranks, also the token owners; 1..64 */
+  int32_t rank;             /* r: the rank whose share is computed; 0..W-1 */
+  int32_t experts_per_rank; /* E_l; rank q hosts global experts [q*E_l, (q+1)*E_l); W*E_l <= 4096 */
+  int32_t top_k;            /* k; 1..min(32, W*E_l) */
+  int32_t hidden;           /* d; multiple of 256 */
+  int32_t ffn;              /* f; multiple of 128 */
+  int32_t tb_m;             /* row-band height tb_M; multiple of 32 in [32, 256] */
+  int32_t mgb;              /* bands merged into one middle segment (§5.2); 1..64 */
+  const int32_t* tokens;    /* HOST array [W]: tokens owned by each rank (T_o >= 0) */
+  int64_t recv_rows;        /* R: rows of x_recv = (owner, token, slot) triples routed to rank r */
+} moe_shape;
+
+/* Sizes the caller allocates (moe_query_sizes). */
+typedef struct moe_sizes {
+  size_t plan_bytes;        /* device plan workspace (int32 arrays, 256-byte aligned pieces) */
+  int64_t rows_cap;         /* rows to allocate for x_layout [rows_cap, d], h [rows_cap, f], y [rows_cap, d]:
+                               R + E_l*(W-1)*(tb_M-1), the padding bound of §4.3 per local expert */
+  int64_t bands_cap;        /* upper bound on row bands: floor(rows_cap / tb_M) + E_l*W */
+  int64_t flags_count;      /* uint32 tile flags for moe_expert_combine: bands_cap * tiles per band */
+  int64_t recv_rows_self;   /* T_r * k: rows of the rank's own receive buffer (input of moe_scale) */
+} moe_sizes;
+
+/* Byte offsets of the plan's arrays inside the workspace (all int32), for
+ * inspection and tests.  Layout of the header (int32 words at hdr):
+ *   [0] error (moe_status of the last device-detected error, 0 if none)
+ *   [1] M  total layout rows          [2] B  bands        [3] remote bands
+ *   [4] segments                      [5] remote segments
+ *   [6] gate/up tiles                 [7] down tiles      [8] consumer copy units
+ *   [9] received rows counted from the routing */
+typedef struct moe_plan_view {
+  size_t hdr;
+  size_t c;          /* [E_l][W] rows of local expert e from owner o */
+  size_t grp_off;    /* [E_l][W] start of group (e, o) inside X_e */
+  size_t m_e;        /* [E_l] rows of X_e, padding included */
+  size_t row_off;    /* [E_l + 1] start of X_e inside the layout */
+  size_t rb;         /* [E_l] remote row bands of expert e */
+  size_t order;      /* [E_l] experts in schedule order (rule (ii)) */
+  size_t base;       /* [W][E_l] owner o's (token, slot) pairs with expert below r*E_l + e */
+  size_t band_expert, band_dst, band_src_row, band_dst_off, band_valid;  /* [B], schedule order S */
+  size_t seg_first, seg_nbands, seg_dst, seg_dst_off, seg_src_row, seg_rows, seg_unit; /* [segments] (+1 for seg_unit) */
+  size_t src_index;  /* [rows_cap] received row of each layout row, -1 for padding (first M valid) */
+  size_t pos;        /* [T_r][k] row of the rank's own receive buffer holding slot (t, j) */
+} moe_plan_view;
+
+/* moe_expert_combine modes */
+enum {
+  MOE_MODE_OVERLAP = 0,   /* down GEMM and consumer run concurrently on disjoint CU sets (§5.3) */
+  MOE_MODE_SERIAL = 1,    /* down GEMM to completion, then the consumer on all CUs (serial baseline) */
+  MOE_MODE_COPY_ONLY = 2  /* only the consumer, on the caller's stream; flags must already equal `epoch` */
+};
+
+typedef struct moe_combine_opts {
+  int32_t mode;             /* MOE_MODE_* */
+  int32_t consumer_cus;     /* OVERLAP: CUs reserved for the consumer, multiple of 8 in [8, 128]; 0 = 32 */
+  int32_t consumer_blocks;  /* workgroups of the consumer; 0 = 2 per reserved CU (OVERLAP) or 1024 */
+  int32_t reserved;
+  int64_t spin_timeout_ns;  /* bound on the consumer's wait for one segment's flags; 0 = 2 s */
+  void* events[6];          /* optional hipEvent_t, recorded: [0]/[1] around the gate/up GEMM (caller's
+                               stream), [2]/[3] around the down GEMM, [4]/[5] around the consumer (on the
+                               stream each kernel runs on); NULL entries are skipped */
+} moe_combine_opts;
+
+/* Text of a status code. */
+const char* moe_status_string(int status);
+
+/* Sizes the caller must allocate for `shape`. Host only; no HIP call. */
+int moe_query_sizes(const moe_shape* shape, moe_sizes* out);
+
+/* Offsets of the plan arrays inside the workspace. Host only; no HIP call. */
+int moe_plan_offsets(const moe_shape* shape, moe_plan_view* out);
+
+/*
+ * moe_plan — Stage A of the tile-signal notes (§3, §4.2, §4.4, §4.5, §5.2):
+ * builds, on the device, the owner-aligned row layout of every local expert
+ * (rows grouped by owner; remote groups zero-padded to a multiple of tb_M,
+ * ascending owner rank with r skipped; the local group last, unpadded), the
+ * remote-first band schedule S (experts by remote band count, descending,
+ * ties to the lower id; remote bands first), the combine plan (destination,
+ * destination row, valid rows per band), the segments and the owner-side
+ * slot table of rank r's own tokens, and writes the layout X.
+ *   topk_ids  device int32 [N, k], N = sum(tokens): global expert ids of every
+ *             owner's tokens, owner-major (owner 0's T_0 tokens first).  Only
+ *             rows routed to rank r matter for X; owner r's rows give `pos`.
+ *   x_recv    device bf16 [R, d]: the received rows in arrival order, i.e.
+ *             every (owner, token, slot) with expert on rank r, lexicographic.
+ *   plan_ws   device, plan_bytes from moe_query_sizes; written.
+ *   x_layout  device bf16 [rows_cap, d]; rows [0, M) written (padding = +0).
+ * Owner o's receive buffer (see moe_expert_combine) is [T_o*k, d], ordered by
+ * (global expert, token).  Errors in the routing are reported through the
+ * error word; all later kernels of this plan then do nothing.
+ */
+int moe_plan(const moe_shape* shape, const int32_t* topk_ids, const uint16_t* x_recv,
+             void* plan_ws, uint16_t* x_layout, void* stream);
+
+/*
+ * moe_expert_combine — Stage B of the tile-signal notes (§5): the SwiGLU
+ * expert FFN of every local expert as grouped bf16 GEMMs over the layout, and
+ * the combine.  The gate/up GEMM writes h = silu(X W_gate^T) * (X W_up^T)
+ * (fp32 accumulation, h rounded once to bf16).  The down GEMM takes its tiles
+ * in schedule order (workgroup i takes tiles i, i+g, ...; §5.1), writes
+ * y = h W_down^T (bf16) and, in its epilogue, releases the tile and sets
+ * flags[tile] = epoch.  The consumer waits (acquire, bounded) until every
+ * tile of a segment is flagged and copies the segment's valid rows to
+ * recv[dst] + dst_off*d; padding rows are never copied.
+ *   x_layout   device bf16 [rows_cap, d] from moe_plan.
+ *   w_gate_up  device bf16 [E_l, 2f, d]: rows 0..f-1 gate, f..2f-1 up (K-contiguous).
+ *   w_down     device bf16 [E_l, d, f] (K-contiguous).
+ *   h, y       device bf16 [rows_cap, f] and [rows_cap, d]; scratch written here.
+ *   flags      device uint32 [flags_count]; zero them once at allocation, then
+ *              pass a new epoch (never 0, increasing) on every call: no reset.
+ *   recv       HOST array of W device pointers; recv[o] is bf16 [T_o*k, d].
+ *   opts       may be NULL (OVERLAP, defaults).
+ * OVERLAP uses two library-owned CU-masked streams at the default priority,
+ * ordered after and joined back into `stream` with events.
+ */
+int moe_expert_combine(const moe_shape* shape, const void* plan_ws, const uint16_t* x_layout,
+                       const uint16_t* w_gate_up, const uint16_t* w_down,
+                       uint16_t* h, uint16_t* y, uint32_t* flags, uint32_t epoch,
+                       uint16_t* const* recv, const moe_combine_opts* opts, void* stream);
+
+/*
+ * moe_scale — step 5 of the distributed MoE forward (tile-signal notes §2.2;
+ * §2.1: the output is the gate-weighted sum of the selected experts' outputs):
+ *   out[t] = bf16( sum_{j<k} topk_w[t][j] * recv_self[pos[t][j]] ), fp32 in j order.
+ *   recv_self  device bf16 [T_r*k, d]: rank r's own receive buffer.
+ *   topk_w     device float [T_r, k]: gate weights of rank r's tokens.
+ *   out        device bf16 [T_r, d].
+ */
+int moe_scale(const moe_shape* shape, const void* plan_ws, const uint16_t* recv_self,
+              const float* topk_w, uint16_t* out, void* stream);
+
+/* Synchronises `stream`, then returns the device error word of the plan
+ * (MOE_OK, MOE_ETIMEOUT or MOE_EROUTING), or MOE_EHIP. */
+int moe_device_status(const void* plan_ws, void* stream);
+
+/* Number of compute units of the current device (0 without a GPU). */
+int moe_device_cus(void);
+
+/* Destroys the cached CU-masked streams and events of the current device. */
+int moe_release_streams(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EXPERT_TILE_MOE_H */

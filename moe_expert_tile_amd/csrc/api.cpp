@@ -1,0 +1,422 @@
+// C ABI of libmoe.so (declared in include/moe.h): host-side validation,
+// workspace layout, CU-partitioned streams and launch orchestration.
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int valid_shape(const moe_shape* s) {
+  if (!s || !s->tokens) return MOE_EINVAL;
+  if (s->world < 1 || s->world > kMaxWorld) return MOE_EINVAL;
+  if (s->rank < 0 || s->rank >= s->world) return MOE_EINVAL;
+  if (s->experts_per_rank < 1 || (int64_t)s->experts_per_rank * s->world > 1024) return MOE_EINVAL;
+  const int E = s->experts_per_rank * s->world;
+  if (s->top_k < 1 || s->top_k > 32 || s->top_k > E) return MOE_EINVAL;
+  if (s->hidden < 256 || s->hidden % 256 != 0 || s->hidden > 65536) return MOE_EINVAL;
+  if (s->ffn < 128 || s->ffn % 128 != 0 || s->ffn > 65536) return MOE_EINVAL;
+  if (s->tb_m < 32 || s->tb_m > 256 || s->tb_m % 32 != 0) return MOE_EINVAL;
+  if (s->mgb < 1 || s->mgb > 64) return MOE_EINVAL;
+  int64_t pairs = 0;
+  for (int o = 0; o < s->world; ++o) {
+    if (s->tokens[o] < 0) return MOE_EINVAL;
+    pairs += (int64_t)s->tokens[o] * s->top_k;
+  }
+  if (pairs > (1ll << 30)) return MOE_EINVAL;
+  if (s->recv_rows < 0 || s->recv_rows > pairs) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, const int32_t* tokens, int64_t R,
+                 PlanLayout* L) {
+  memset(L, 0, sizeof(*L));
+  L->W = W; L->r = r; L->E_l = E_l; L->E = W * E_l; L->k = k; L->d = d; L->f = f;
+  L->tb_m = tb_m; L->mgb = mgb; L->R = (int)R;
+  const int64_t rows_cap = R + (int64_t)E_l * (W - 1) * (tb_m - 1);
+  if (rows_cap > (1ll << 30)) return false;
+  L->rows_cap = (int)rows_cap;
+  L->bands_cap = (int)(rows_cap / tb_m + (int64_t)E_l * W);
+  L->T_r = tokens[r];
+  int pair = 0, blk = 0, tok = 0;
+  for (int o = 0; o < W; ++o) {
+    L->pair_off[o] = pair;
+    L->blk_off[o] = blk;
+    L->tok_off[o] = tok;
+    const int p = tokens[o] * k;
+    pair += p;
+    blk += (p + kPairsPerBlock - 1) / kPairsPerBlock;
+    tok += tokens[o];
+  }
+  L->pair_off[W] = pair;
+  L->blk_off[W] = blk;
+  L->tok_off[W] = tok;
+  L->NB = blk;
+  L->NB_r = L->blk_off[r + 1] - L->blk_off[r];
+  int bm = 256;
+  while (tb_m % bm != 0) bm >>= 1;
+  L->dn_bm = bm;
+  L->dn_sub = tb_m / bm;
+  L->dn_ntn = d / kDnBN;
+  L->dn_tpb = L->dn_sub * L->dn_ntn;
+  L->gu_ntn = f / (kGuBN / 2);
+  L->gu_mt_cap = (int)(rows_cap / kGuBM + E_l + 1);
+
+  int64_t off = 0;
+  auto take = [&](int64_t n) {
+    const int64_t at = off;
+    off += round_up(n > 0 ? n : 1, 64);  // 256-byte aligned pieces
+    return at;
+  };
+  const int64_t EW = (int64_t)E_l * W, B = L->bands_cap;
+  L->o_hdr = take(H_WORDS);
+  L->o_c = take(EW);
+  L->o_low = take(W);
+  L->o_grp = take(EW);
+  L->o_me = take(E_l);
+  L->o_rowoff = take(E_l + 1);
+  L->o_rb = take(E_l);
+  L->o_order = take(E_l);
+  L->o_base = take(EW);
+  L->o_bexp = take(B); L->o_bdst = take(B); L->o_bsrc = take(B); L->o_bdoff = take(B); L->o_bval = take(B);
+  L->o_sfirst = take(B); L->o_snb = take(B); L->o_sdst = take(B); L->o_sdoff = take(B); L->o_ssrc = take(B);
+  L->o_srows = take(B); L->o_sunit = take(B + 1);
+  L->o_src = take(rows_cap);
+  L->o_pos = take((int64_t)L->T_r * k);
+  L->o_bh = take((int64_t)L->NB * (E_l + 2));
+  L->o_bp = take((int64_t)L->NB * (E_l + 1));
+  L->o_brecv = take(L->NB);
+  L->o_bhr = take((int64_t)L->NB_r * L->E);
+  L->o_bpr = take((int64_t)L->NB_r * L->E);
+  L->o_baser = take(L->E);
+  L->o_gumt_row = take(L->gu_mt_cap);
+  L->o_gumt_exp = take(L->gu_mt_cap);
+  L->o_gscr = take(3 * EW + 1);
+  L->total_words = off;
+  return true;
+}
+
+// --- per-device cache: CU-masked streams and events of the overlapped combine ---
+namespace {
+
+struct DeviceState {
+  bool init = false;
+  int cus = 0;
+  int consumer_cus = -1;
+  hipStream_t prod = nullptr, cons = nullptr;
+  hipEvent_t fork = nullptr, join_p = nullptr, join_c = nullptr;
+};
+constexpr int kMaxDevices = 16;
+DeviceState g_dev[kMaxDevices];
+std::mutex g_mu;
+
+int current_device(int* dev) {
+  if (hipGetDevice(dev) != hipSuccess) return MOE_EUNSUPPORTED;
+  if (*dev < 0 || *dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int device_cus(int dev) {
+  DeviceState& st = g_dev[dev];
+  if (!st.init) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    st.cus = n;
+    st.init = true;
+  }
+  return st.cus;
+}
+
+// CU mask with `n` bits set out of `total`.  The bit index of a CU interleaves
+// the XCDs (bit i belongs to XCD i mod 8), so the lowest n bits give n/8 CUs
+// on every XCD.
+void fill_mask(uint32_t* mask, int words, int lo_bit, int hi_bit) {
+  for (int i = 0; i < words; ++i) mask[i] = 0;
+  for (int b = lo_bit; b < hi_bit; ++b) mask[b / 32] |= (1u << (b % 32));
+}
+
+int ensure_streams(int dev, int consumer_cus, DeviceState** out) {
+  DeviceState& st = g_dev[dev];
+  const int cus = device_cus(dev);
+  if (cus <= 0) return MOE_EUNSUPPORTED;
+  if (st.prod && st.consumer_cus == consumer_cus) {
+    *out = &st;
+    return MOE_OK;
+  }
+  if (st.prod) { (void)hipStreamDestroy(st.prod); st.prod = nullptr; }
+  if (st.cons) { (void)hipStreamDestroy(st.cons); st.cons = nullptr; }
+  const int words = (cus + 31) / 32;
+  uint32_t mask[64];
+  fill_mask(mask, words, 0, consumer_cus);
+  if (hipExtStreamCreateWithCUMask(&st.cons, words, mask) != hipSuccess) return MOE_EHIP;
+  fill_mask(mask, words, consumer_cus, cus);
+  if (hipExtStreamCreateWithCUMask(&st.prod, words, mask) != hipSuccess) return MOE_EHIP;
+  if (!st.fork) {
+    if (hipEventCreateWithFlags(&st.fork, hipEventDisableTiming) != hipSuccess) return MOE_EHIP;
+    if (hipEventCreateWithFlags(&st.join_p, hipEventDisableTiming) != hipSuccess) return MOE_EHIP;
+    if (hipEventCreateWithFlags(&st.join_c, hipEventDisableTiming) != hipSuccess) return MOE_EHIP;
+  }
+  st.consumer_cus = consumer_cus;
+  *out = &st;
+  return MOE_OK;
+}
+
+int check_gfx950(int dev) {
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) return MOE_EUNSUPPORTED;
+  if (strncmp(p.gcnArchName, "gfx950", 6) != 0) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int prepare(int* dev) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int rc = current_device(dev);
+  if (rc) return rc;
+  DeviceState& st = g_dev[*dev];
+  if (!st.init) {
+    rc = check_gfx950(*dev);
+    if (rc) return rc;
+    if (device_cus(*dev) <= 0) return MOE_EUNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+void record(void* ev, hipStream_t s) {
+  if (ev) (void)hipEventRecord((hipEvent_t)ev, s);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_ECAPACITY: return "capacity exceeded";
+    case MOE_EHIP: return "HIP runtime error";
+    case MOE_ETIMEOUT: return "consumer wait timed out";
+    case MOE_EROUTING: return "routing inconsistent (expert id out of range or received-row count mismatch)";
+    case MOE_EUNSUPPORTED: return "no gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+int moe_query_sizes(const moe_shape* s, moe_sizes* out) {
+  int rc = valid_shape(s);
+  if (rc) return rc;
+  if (!out) return MOE_EINVAL;
+  PlanLayout L;
+  if (!make_layout(s->world, s->rank, s->experts_per_rank, s->top_k, s->hidden, s->ffn, s->tb_m, s->mgb, s->tokens,
+                   s->recv_rows, &L))
+    return MOE_ECAPACITY;
+  out->plan_bytes = (size_t)L.total_words * 4;
+  out->rows_cap = L.rows_cap;
+  out->bands_cap = L.bands_cap;
+  out->flags_count = (int64_t)L.bands_cap * L.dn_tpb;
+  out->recv_rows_self = (int64_t)L.T_r * L.k;
+  return MOE_OK;
+}
+
+int moe_plan_offsets(const moe_shape* s, moe_plan_view* v) {
+  int rc = valid_shape(s);
+  if (rc) return rc;
+  if (!v) return MOE_EINVAL;
+  PlanLayout L;
+  if (!make_layout(s->world, s->rank, s->experts_per_rank, s->top_k, s->hidden, s->ffn, s->tb_m, s->mgb, s->tokens,
+                   s->recv_rows, &L))
+    return MOE_ECAPACITY;
+  v->hdr = L.o_hdr * 4; v->c = L.o_c * 4; v->grp_off = L.o_grp * 4; v->m_e = L.o_me * 4;
+  v->row_off = L.o_rowoff * 4; v->rb = L.o_rb * 4; v->order = L.o_order * 4; v->base = L.o_base * 4;
+  v->band_expert = L.o_bexp * 4; v->band_dst = L.o_bdst * 4; v->band_src_row = L.o_bsrc * 4;
+  v->band_dst_off = L.o_bdoff * 4; v->band_valid = L.o_bval * 4;
+  v->seg_first = L.o_sfirst * 4; v->seg_nbands = L.o_snb * 4; v->seg_dst = L.o_sdst * 4;
+  v->seg_dst_off = L.o_sdoff * 4; v->seg_src_row = L.o_ssrc * 4; v->seg_rows = L.o_srows * 4;
+  v->seg_unit = L.o_sunit * 4; v->src_index = L.o_src * 4; v->pos = L.o_pos * 4;
+  return MOE_OK;
+}
+
+int moe_plan(const moe_shape* s, const int32_t* topk_ids, const uint16_t* x_recv, void* plan_ws,
+             uint16_t* x_layout, void* stream) {
+  int rc = valid_shape(s);
+  if (rc) return rc;
+  int64_t pairs = 0;
+  for (int o = 0; o < s->world; ++o) pairs += (int64_t)s->tokens[o] * s->top_k;
+  if (!plan_ws || !aligned(plan_ws, 256)) return MOE_EINVAL;
+  if (pairs > 0 && (!topk_ids || !aligned(topk_ids, 4))) return MOE_EINVAL;
+  if (s->recv_rows > 0 && (!x_recv || !aligned(x_recv, 16))) return MOE_EINVAL;
+  if (!x_layout || !aligned(x_layout, 16)) return MOE_EINVAL;
+  PlanLayout L;
+  if (!make_layout(s->world, s->rank, s->experts_per_rank, s->top_k, s->hidden, s->ffn, s->tb_m, s->mgb, s->tokens,
+                   s->recv_rows, &L))
+    return MOE_ECAPACITY;
+  int dev;
+  rc = prepare(&dev);
+  if (rc) return rc;
+  return hip_rc(launch_plan(L, topk_ids, x_recv, (int32_t*)plan_ws, x_layout, (hipStream_t)stream));
+}
+
+int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* x_layout, const uint16_t* w_gate_up,
+                       const uint16_t* w_down, uint16_t* h, uint16_t* y, uint32_t* flags, uint32_t epoch,
+                       uint16_t* const* recv, const moe_combine_opts* opts, void* stream) {
+  int rc = valid_shape(s);
+  if (rc) return rc;
+  moe_combine_opts o;
+  memset(&o, 0, sizeof(o));
+  if (opts) o = *opts;
+  if (o.mode < MOE_MODE_OVERLAP || o.mode > MOE_MODE_COPY_ONLY) return MOE_EINVAL;
+  if (o.consumer_cus == 0) o.consumer_cus = 32;
+  if (o.consumer_cus < 8 || o.consumer_cus > 128 || o.consumer_cus % 8 != 0) return MOE_EINVAL;
+  if (o.consumer_blocks < 0 || o.consumer_blocks > 65536) return MOE_EINVAL;
+  if (o.spin_timeout_ns < 0) return MOE_EINVAL;
+  if (epoch == 0) return MOE_EINVAL;
+  if (!plan_ws || !aligned(plan_ws, 256)) return MOE_EINVAL;
+  const bool compute = (o.mode != MOE_MODE_COPY_ONLY);
+  if (compute) {
+    if (!x_layout || !aligned(x_layout, 16) || !w_gate_up || !aligned(w_gate_up, 16) || !w_down ||
+        !aligned(w_down, 16) || !h || !aligned(h, 16))
+      return MOE_EINVAL;
+  }
+  if (!y || !aligned(y, 16) || !flags || !aligned(flags, 4) || !recv) return MOE_EINVAL;
+  RecvPtrs rp;
+  memset(&rp, 0, sizeof(rp));
+  for (int i = 0; i < s->world; ++i) {
+    if (s->tokens[i] > 0 && (!recv[i] || !aligned(recv[i], 16))) return MOE_EINVAL;
+    rp.p[i] = recv[i];
+  }
+  PlanLayout L;
+  if (!make_layout(s->world, s->rank, s->experts_per_rank, s->top_k, s->hidden, s->ffn, s->tb_m, s->mgb, s->tokens,
+                   s->recv_rows, &L))
+    return MOE_ECAPACITY;
+  int dev;
+  rc = prepare(&dev);
+  if (rc) return rc;
+  const int cus = g_dev[dev].cus;
+  const int64_t timeout = (o.spin_timeout_ns ? o.spin_timeout_ns : 2000000000ll) / 10;  // 100 MHz ticks
+  const hipStream_t st = (hipStream_t)stream;
+  const int32_t* ws = (const int32_t*)plan_ws;
+  int32_t* ws_rw = (int32_t*)plan_ws;
+  int full_grid = cus - cus % 8;
+  if (full_grid < 8) full_grid = 8;
+
+  if (o.mode == MOE_MODE_COPY_ONLY) {
+    record(o.events[4], st);
+    rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, timeout, o.consumer_blocks ? o.consumer_blocks : 1024,
+                                st));
+    record(o.events[5], st);
+    return rc;
+  }
+  record(o.events[0], st);
+  rc = hip_rc(launch_gateup(L, ws, x_layout, w_gate_up, h, full_grid, st));
+  record(o.events[1], st);
+  if (rc) return rc;
+  if (o.mode == MOE_MODE_SERIAL) {
+    record(o.events[2], st);
+    rc = hip_rc(launch_down(L, ws, h, w_down, y, flags, epoch, full_grid, st));
+    record(o.events[3], st);
+    if (rc) return rc;
+    record(o.events[4], st);
+    rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, timeout, o.consumer_blocks ? o.consumer_blocks : 1024,
+                                st));
+    record(o.events[5], st);
+    return rc;
+  }
+  // OVERLAP: down GEMM on the producer CU set, consumer on the reserved set
+  if (o.consumer_cus >= cus) return MOE_EINVAL;
+  DeviceState* ds = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    rc = ensure_streams(dev, o.consumer_cus, &ds);
+  }
+  if (rc) return rc;
+  if (hipEventRecord(ds->fork, st) != hipSuccess) return MOE_EHIP;
+  if (hipStreamWaitEvent(ds->prod, ds->fork, 0) != hipSuccess) return MOE_EHIP;
+  if (hipStreamWaitEvent(ds->cons, ds->fork, 0) != hipSuccess) return MOE_EHIP;
+  int pgrid = cus - o.consumer_cus;
+  pgrid -= pgrid % 8;
+  // the producer is enqueued first, so a consumer sharing its hardware queue
+  // would simply run after it
+  record(o.events[2], ds->prod);
+  rc = hip_rc(launch_down(L, ws, h, w_down, y, flags, epoch, pgrid, ds->prod));
+  record(o.events[3], ds->prod);
+  if (rc) return rc;
+  record(o.events[4], ds->cons);
+  rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, timeout,
+                              o.consumer_blocks ? o.consumer_blocks : 2 * o.consumer_cus, ds->cons));
+  record(o.events[5], ds->cons);
+  if (rc) return rc;
+  if (hipEventRecord(ds->join_p, ds->prod) != hipSuccess) return MOE_EHIP;
+  if (hipEventRecord(ds->join_c, ds->cons) != hipSuccess) return MOE_EHIP;
+  if (hipStreamWaitEvent(st, ds->join_p, 0) != hipSuccess) return MOE_EHIP;
+  if (hipStreamWaitEvent(st, ds->join_c, 0) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
+}
+
+int moe_scale(const moe_shape* s, const void* plan_ws, const uint16_t* recv_self, const float* topk_w, uint16_t* out,
+              void* stream) {
+  int rc = valid_shape(s);
+  if (rc) return rc;
+  if (!plan_ws || !aligned(plan_ws, 256)) return MOE_EINVAL;
+  const int T = s->tokens[s->rank];
+  if (T > 0 && (!recv_self || !aligned(recv_self, 16) || !topk_w || !aligned(topk_w, 4) || !out ||
+                !aligned(out, 16)))
+    return MOE_EINVAL;
+  PlanLayout L;
+  if (!make_layout(s->world, s->rank, s->experts_per_rank, s->top_k, s->hidden, s->ffn, s->tb_m, s->mgb, s->tokens,
+                   s->recv_rows, &L))
+    return MOE_ECAPACITY;
+  int dev;
+  rc = prepare(&dev);
+  if (rc) return rc;
+  return hip_rc(launch_scale(L, (const int32_t*)plan_ws, recv_self, topk_w, out, (hipStream_t)stream));
+}
+
+int moe_device_status(const void* plan_ws, void* stream) {
+  if (!plan_ws || !aligned(plan_ws, 256)) return MOE_EINVAL;
+  const hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_EHIP;
+  int32_t word = 0;
+  if (hipMemcpy(&word, plan_ws, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return MOE_EHIP;
+  return word;
+}
+
+int moe_device_cus(void) {
+  int dev;
+  if (prepare(&dev) != MOE_OK) return 0;
+  return g_dev[dev].cus;
+}
+
+int moe_release_streams(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int dev;
+  if (current_device(&dev) != MOE_OK) return MOE_EUNSUPPORTED;
+  DeviceState& st = g_dev[dev];
+  if (st.prod) (void)hipStreamDestroy(st.prod);
+  if (st.cons) (void)hipStreamDestroy(st.cons);
+  if (st.fork) (void)hipEventDestroy(st.fork);
+  if (st.join_p) (void)hipEventDestroy(st.join_p);
+  if (st.join_c) (void)hipEventDestroy(st.join_c);
+  st.prod = st.cons = nullptr;
+  st.fork = st.join_p = st.join_c = nullptr;
+  st.consumer_cus = -1;
+  return MOE_OK;
+}
+
+}  // extern "C"

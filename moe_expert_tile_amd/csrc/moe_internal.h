@@ -1,0 +1,73 @@
+// Internal definitions shared by the HIP kernels and the host orchestration
+// of libmoe.so.  Nothing here is part of the public ABI (include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxWorld = 64;
+constexpr int kPairsPerBlock = 2048;   // (token, slot) pairs per planner workgroup
+constexpr int kPlanThreads = 256;
+constexpr int kBuildThreads = 1024;    // the single-workgroup plan builder
+constexpr int kCopyChunk = 32768;      // bytes per consumer copy unit
+constexpr int kGuBM = 256;             // gate/up GEMM tile rows
+constexpr int kGuBN = 256;             // gate/up GEMM tile cols (128 gate + 128 up)
+constexpr int kDnBN = 256;             // down GEMM tile cols
+
+// header words of the plan workspace (mirrors the public description)
+enum Hdr {
+  H_ERROR = 0, H_M = 1, H_BANDS = 2, H_REMOTE = 3, H_SEGS = 4, H_RSEGS = 5,
+  H_GU_TILES = 6, H_DN_TILES = 7, H_UNITS = 8, H_RCOUNT = 9, H_GU_MT = 10,
+  H_WORDS = 64
+};
+
+// Everything a kernel needs to find the plan arrays: sizes and int32 element
+// offsets from the workspace base.  Built on the host, passed by value.
+struct PlanLayout {
+  int W, r, E_l, E, k, d, f, tb_m, mgb;
+  int R, rows_cap, bands_cap, T_r, NB, NB_r, gu_mt_cap;
+  int dn_bm, dn_sub, dn_ntn, dn_tpb;   // down GEMM: tile rows, tiles per band row, n tiles, tiles per band
+  int gu_ntn;                          // gate/up GEMM n tiles (f / 128)
+  int64_t o_hdr, o_c, o_low, o_grp, o_me, o_rowoff, o_rb, o_order, o_base;
+  int64_t o_bexp, o_bdst, o_bsrc, o_bdoff, o_bval;
+  int64_t o_sfirst, o_snb, o_sdst, o_sdoff, o_ssrc, o_srows, o_sunit;
+  int64_t o_src, o_pos;
+  int64_t o_bh, o_bp, o_brecv, o_bhr, o_bpr, o_baser;
+  int64_t o_gumt_row, o_gumt_exp, o_gscr;
+  int64_t total_words;
+  int pair_off[kMaxWorld + 1];   // first (token, slot) pair of each owner
+  int blk_off[kMaxWorld + 1];    // first planner block of each owner
+  int tok_off[kMaxWorld + 1];    // first token of each owner
+};
+
+struct RecvPtrs {
+  uint16_t* p[kMaxWorld];
+};
+
+// host-side helpers (api.cpp)
+bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb,
+                 const int32_t* tokens, int64_t R, PlanLayout* L);
+
+// launchers (defined next to their kernels); all asynchronous on `s`
+hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t* x_recv,
+                       int32_t* ws, uint16_t* x_layout, hipStream_t s);
+hipError_t launch_gateup(const PlanLayout& L, const int32_t* ws, const uint16_t* x,
+                         const uint16_t* wgu, uint16_t* h, int grid, hipStream_t s);
+hipError_t launch_down(const PlanLayout& L, const int32_t* ws, const uint16_t* h,
+                       const uint16_t* wd, uint16_t* y, uint32_t* flags, uint32_t epoch,
+                       int grid, hipStream_t s);
+hipError_t launch_consumer(const PlanLayout& L, int32_t* ws, const uint16_t* y,
+                           const uint32_t* flags, uint32_t epoch, const RecvPtrs& recv,
+                           int64_t timeout_ticks, int grid, hipStream_t s);
+hipError_t launch_scale(const PlanLayout& L, const int32_t* ws, const uint16_t* recv_self,
+                        const float* topk_w, uint16_t* out, hipStream_t s);
+
+// device helpers ------------------------------------------------------------
+#if defined(__HIPCC__)
+__device__ __forceinline__ int32_t* ws_at(int32_t* ws, int64_t off) { return ws + off; }
+__device__ __forceinline__ const int32_t* ws_at(const int32_t* ws, int64_t off) { return ws + off; }
+#endif
+
+}  // namespace moe

@@ -1,0 +1,520 @@
+// Planner: Stage A of the tile-signal notes ("MoE 计算-通信细粒度重叠：用 Tile 级信号把
+// All-to-All 藏在 GEMM 背后", §3 and §4.2-§4.5, segments §5.2), on the device.
+//
+//   K1 plan_count   one workgroup per 2048 (token, slot) pairs of one owner:
+//                   LDS histograms of the local experts, of "below this rank's
+//                   experts" (for receive offsets) and, for the rank's own
+//                   tokens, of all experts (for the owner-side slot table).
+//   K2 plan_build   one workgroup: scans over the histograms -> group counts,
+//                   padded group offsets, X_e sizes, rule (ii) expert order,
+//                   band list S (remote bands first), combine plan, segments,
+//                   gate/up tile table, padding entries of src_index.
+//   K3 plan_place   one workgroup per pair block again: stable rank of every
+//                   pair inside its (expert, owner) group with wave ballots +
+//                   LDS carries -> src_index of every real layout row, and the
+//                   owner-side slot of each of the rank's own pairs.
+//   K4 plan_gather  one wavefront per layout row: X[row] = x_recv[src] or 0,
+//                   16-byte coalesced loads and stores.
+//
+// Stability: pairs are visited in (owner, token, slot) order — blocks in
+// order, rounds of 256 pairs in order, wavefronts in order, lanes in order —
+// so every rank computed here is the rank in arrival order.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Exclusive scan of one int per thread over the whole workgroup.
+__device__ int block_excl_scan(int v, int* sh, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nw = (blockDim.x + 63) >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < nw; ++i) { int t = sh[i]; sh[i] = run; run += t; }
+    sh[32] = run;
+  }
+  __syncthreads();
+  int res = sh[w] + x - v;
+  *total = sh[32];
+  __syncthreads();
+  return res;
+}
+
+// Exclusive scan over n items: val(i) gives item i, out(i, prefix) receives
+// its exclusive prefix.  Items are split into contiguous per-thread chunks.
+template <class F, class G>
+__device__ int scan_items(int n, F val, G out, int* sh) {
+  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
+  int local = 0;
+  for (int i = lo; i < hi; ++i) local += val(i);
+  int total;
+  int run = block_excl_scan(local, sh, &total);
+  for (int i = lo; i < hi; ++i) { int v = val(i); out(i, run); run += v; }
+  __syncthreads();
+  return total;
+}
+
+__device__ __forceinline__ int owner_of_block(const PlanLayout& L, int b) {
+  int o = 0;
+  while (o < L.W - 1 && b >= L.blk_off[o + 1]) ++o;
+  return o;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(PlanLayout L, const int32_t* __restrict__ topk,
+                                                                 int32_t* __restrict__ ws) {
+  extern __shared__ int sh[];
+  const int b = blockIdx.x;
+  const int o = owner_of_block(L, b);
+  const int p0 = L.pair_off[o] + (b - L.blk_off[o]) * kPairsPerBlock;
+  const int p1 = min(p0 + kPairsPerBlock, L.pair_off[o + 1]);
+  const bool own = (o == L.r);
+  const int nb = L.E_l + 2 + (own ? L.E : 0);
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) sh[i] = 0;
+  __syncthreads();
+  const int lo = L.r * L.E_l;
+  for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+    const int g = topk[p];
+    if (g < 0 || g >= L.E) {
+      atomicAdd(&sh[L.E_l + 1], 1);
+      continue;
+    }
+    const int e = g - lo;
+    if (e >= 0 && e < L.E_l) atomicAdd(&sh[e], 1);
+    else if (g < lo) atomicAdd(&sh[L.E_l], 1);
+    if (own) atomicAdd(&sh[L.E_l + 2 + g], 1);
+  }
+  __syncthreads();
+  int32_t* bh = ws + L.o_bh + (int64_t)b * (L.E_l + 2);
+  for (int i = threadIdx.x; i < L.E_l + 2; i += blockDim.x) bh[i] = sh[i];
+  if (own) {
+    int32_t* bhr = ws + L.o_bhr + (int64_t)(b - L.blk_off[L.r]) * L.E;
+    for (int g = threadIdx.x; g < L.E; g += blockDim.x) bhr[g] = sh[L.E_l + 2 + g];
+  }
+}
+
+__global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L, int32_t* __restrict__ ws) {
+  __shared__ int sh[64];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int W = L.W, r = L.r, E_l = L.E_l, E = L.E, tb = L.tb_m;
+  const int HB = E_l + 2;
+  int32_t* hdr = ws + L.o_hdr;
+  int32_t* c = ws + L.o_c;
+  int32_t* low = ws + L.o_low;
+  int32_t* grp = ws + L.o_grp;
+  int32_t* me = ws + L.o_me;
+  int32_t* rowoff = ws + L.o_rowoff;
+  int32_t* rb = ws + L.o_rb;
+  int32_t* order = ws + L.o_order;
+  int32_t* base = ws + L.o_base;
+  const int32_t* bh = ws + L.o_bh;
+  int32_t* bp = ws + L.o_bp;
+  int32_t* brecv = ws + L.o_brecv;
+  const int32_t* bhr = ws + L.o_bhr;
+  int32_t* bpr = ws + L.o_bpr;
+  int32_t* baser = ws + L.o_baser;
+
+  // (a) routing errors
+  int bad_local = 0;
+  for (int b = tid; b < L.NB; b += nt) bad_local += bh[(int64_t)b * HB + E_l + 1];
+  int bad_total;
+  (void)block_excl_scan(bad_local, sh, &bad_total);
+
+  // (b) group counts c[e][o], low[o], per-block prefixes within each owner
+  for (int it = tid; it < W * (E_l + 1); it += nt) {
+    const int o = it / (E_l + 1), x = it % (E_l + 1);
+    int run = 0;
+    for (int b = L.blk_off[o]; b < L.blk_off[o + 1]; ++b) {
+      bp[(int64_t)b * (E_l + 1) + x] = run;
+      run += bh[(int64_t)b * HB + x];
+    }
+    if (x < E_l) c[x * W + o] = run; else low[o] = run;
+  }
+  // (c) received-row base of every block
+  int rcount = scan_items(
+      L.NB,
+      [&](int b) {
+        int s = 0;
+        for (int e = 0; e < E_l; ++e) s += bh[(int64_t)b * HB + e];
+        return s;
+      },
+      [&](int b, int pre) { brecv[b] = pre; }, sh);
+  // (d) the rank's own tokens: per-expert counts and per-block prefixes
+  for (int g = tid; g < E; g += nt) {
+    int run = 0;
+    for (int b = 0; b < L.NB_r; ++b) {
+      bpr[(int64_t)b * E + g] = run;
+      run += bhr[(int64_t)b * E + g];
+    }
+    baser[g] = run;  // count for now, turned into a prefix below
+  }
+  __syncthreads();
+  (void)scan_items(
+      E, [&](int g) { return baser[g]; }, [&](int g, int pre) { baser[g] = pre; }, sh);
+  // scan_items reads item g (val) before it calls out(g), so the counts can be
+  // replaced by their prefixes in place
+
+  if (bad_total > 0 || rcount != L.R) {
+    if (tid == 0) {
+      hdr[H_ERROR] = 5;  // MOE_EROUTING
+      for (int i = 1; i < H_WORDS; ++i) hdr[i] = 0;
+      hdr[H_RCOUNT] = rcount;
+    }
+    return;
+  }
+
+  // (e) layout: padded group offsets inside X_e, remote owners ascending then r
+  for (int e = tid; e < E_l; e += nt) {
+    int run = 0;
+    for (int q = 0; q < W; ++q) {
+      const int o = (q < W - 1) ? (q < r ? q : q + 1) : r;
+      grp[e * W + o] = run;
+      const int n = c[e * W + o];
+      run += (o == r) ? n : ((n + tb - 1) / tb) * tb;
+    }
+    me[e] = run;
+  }
+  // receive-buffer bases: owner o's pairs below global expert r*E_l + e
+  for (int o = tid; o < W; o += nt) {
+    int run = low[o];
+    for (int e = 0; e < E_l; ++e) { base[o * E_l + e] = run; run += c[e * W + o]; }
+  }
+  __syncthreads();
+  const int M = scan_items(
+      E_l, [&](int e) { return me[e]; }, [&](int e, int pre) { rowoff[e] = pre; }, sh);
+  if (tid == 0) rowoff[E_l] = M;
+  // remote bands per expert and rule (ii) order: more remote bands first, ties to lower id
+  for (int e = tid; e < E_l; e += nt) {
+    int n = 0;
+    for (int o = 0; o < W; ++o)
+      if (o != r) n += (c[e * W + o] + tb - 1) / tb;
+    rb[e] = n;
+  }
+  __syncthreads();
+  for (int e = tid; e < E_l; e += nt) {
+    int rank = 0;
+    const int mine = rb[e];
+    for (int x = 0; x < E_l; ++x) {
+      const int v = rb[x];
+      rank += (v > mine) || (v == mine && x < e);
+    }
+    order[rank] = e;
+  }
+  __syncthreads();
+
+  // (f) groups in schedule order: remote groups of experts in rule (ii) order
+  //     (owners ascending, r skipped), then the local group of every expert.
+  const int NGR = E_l * (W - 1);
+  const int NG = E_l * W;
+  auto group_eo = [&](int gi, int& e, int& o) {
+    if (gi < NGR) {
+      e = order[gi / (W - 1)];
+      const int q = gi % (W - 1);
+      o = q < r ? q : q + 1;
+    } else {
+      e = gi - NGR;
+      o = r;
+    }
+  };
+  auto group_nb = [&](int gi) {
+    int e, o;
+    group_eo(gi, e, o);
+    return (c[e * W + o] + tb - 1) / tb;
+  };
+  // per-group scratch: band start, segment base, unit base
+  int32_t* gstart = ws + L.o_gscr;
+  int32_t* gseg = gstart + NG;
+  int32_t* gunit = gseg + NG;
+  const int B = scan_items(NG, group_nb, [&](int gi, int pre) { gstart[gi] = pre; }, sh);
+  int nrem_local = 0;
+  for (int gi = tid; gi < NGR; gi += nt) nrem_local += group_nb(gi);
+  int n_remote;
+  (void)block_excl_scan(nrem_local, sh, &n_remote);
+  if (B > L.bands_cap) {
+    if (tid == 0) { hdr[H_ERROR] = 2; for (int i = 1; i < H_WORDS; ++i) hdr[i] = 0; }
+    return;
+  }
+
+  // (g) bands in S order, one thread per group
+  int32_t* bexp = ws + L.o_bexp;
+  int32_t* bdst = ws + L.o_bdst;
+  int32_t* bsrc = ws + L.o_bsrc;
+  int32_t* bdoff = ws + L.o_bdoff;
+  int32_t* bval = ws + L.o_bval;
+  for (int gi = tid; gi < NG; gi += nt) {
+    int e, o;
+    group_eo(gi, e, o);
+    const int n = c[e * W + o];
+    const int gs = gstart[gi];
+    const int src0 = rowoff[e] + grp[e * W + o];
+    const int d0 = base[o * E_l + e];
+    for (int b = 0; b * tb < n; ++b) {
+      const int s = gs + b;
+      bexp[s] = e;
+      bdst[s] = o;
+      bsrc[s] = src0 + b * tb;
+      bdoff[s] = d0 + b * tb;
+      bval[s] = min(tb, n - b * tb);
+    }
+  }
+
+  // segments (§5.2): the first and the last remote band alone; otherwise runs
+  // of <= mgb bands that restart at every group boundary.  Segments never cross
+  // a group, so each group's segments are found by its own thread.
+  const int mgb = L.mgb;
+  auto seg_start = [&](int s, int gs, bool remote) {
+    if (remote) {
+      if (s == 0 || s == n_remote - 1) return true;
+      const int run0 = gs > 1 ? gs : 1;
+      return ((s - run0) % mgb) == 0;
+    }
+    return ((s - gs) % mgb) == 0;
+  };
+  const int64_t row_bytes = (int64_t)L.d * 2;
+  auto units_of = [&](int rows) { return (int)((rows * row_bytes + kCopyChunk - 1) / kCopyChunk); };
+  // walks the segments of group gi; fn(first_band, n_bands, rows) per segment
+  auto for_segments = [&](int gi, auto fn) {
+    int e, o;
+    group_eo(gi, e, o);
+    const int cnt = c[e * W + o];
+    const int gs = gstart[gi], n = (cnt + tb - 1) / tb;
+    int first = gs, rows = 0;
+    for (int s = gs; s < gs + n; ++s) {
+      if (s > gs && seg_start(s, gs, gi < NGR)) {
+        fn(first, s - first, rows);
+        first = s;
+        rows = 0;
+      }
+      rows += min(tb, cnt - (s - gs) * tb);
+    }
+    if (n > 0) fn(first, gs + n - first, rows);
+  };
+  auto group_segs = [&](int gi) {
+    int cnt = 0;
+    for_segments(gi, [&](int, int, int) { ++cnt; });
+    return cnt;
+  };
+  auto group_units = [&](int gi) {
+    int u = 0;
+    for_segments(gi, [&](int, int, int rows) { u += units_of(rows); });
+    return u;
+  };
+  const int NS = scan_items(NG, group_segs, [&](int gi, int pre) { gseg[gi] = pre; }, sh);
+  const int U = scan_items(NG, group_units, [&](int gi, int pre) { gunit[gi] = pre; }, sh);
+  int nrs_local = 0;
+  for (int gi = tid; gi < NGR; gi += nt) nrs_local += group_segs(gi);
+  int n_rsegs;
+  (void)block_excl_scan(nrs_local, sh, &n_rsegs);
+  int32_t* sfirst = ws + L.o_sfirst;
+  int32_t* snb = ws + L.o_snb;
+  int32_t* sdst = ws + L.o_sdst;
+  int32_t* sdoff = ws + L.o_sdoff;
+  int32_t* ssrc = ws + L.o_ssrc;
+  int32_t* srows = ws + L.o_srows;
+  int32_t* sunit = ws + L.o_sunit;
+  for (int gi = tid; gi < NG; gi += nt) {
+    int e, o;
+    group_eo(gi, e, o);
+    const int gs = gstart[gi];
+    int sidx = gseg[gi];
+    int u = gunit[gi];
+    for_segments(gi, [&](int first, int nb, int rows) {
+      sfirst[sidx] = first;
+      snb[sidx] = nb;
+      sdst[sidx] = o;
+      sdoff[sidx] = base[o * E_l + e] + (first - gs) * tb;
+      ssrc[sidx] = rowoff[e] + grp[e * W + o] + (first - gs) * tb;
+      srows[sidx] = rows;
+      sunit[sidx] = u;
+      u += units_of(rows);
+      ++sidx;
+    });
+  }
+  if (tid == 0) sunit[NS] = U;
+
+  // (h) padding entries of src_index: the tail of every remote group
+  int32_t* src = ws + L.o_src;
+  for (int gi = tid; gi < NGR; gi += nt) {
+    int e, o;
+    group_eo(gi, e, o);
+    const int n = c[e * W + o];
+    const int row0 = rowoff[e] + grp[e * W + o];
+    const int padded = ((n + tb - 1) / tb) * tb;
+    for (int q = n; q < padded; ++q) src[row0 + q] = -1;
+  }
+
+  // (i) gate/up m-tiles: every X_e cut into kGuBM-row tiles, experts in order
+  int32_t* mt_row = ws + L.o_gumt_row;
+  int32_t* mt_exp = ws + L.o_gumt_exp;
+  const int NMT = scan_items(
+      E_l, [&](int q) { return (me[order[q]] + kGuBM - 1) / kGuBM; },
+      [&](int q, int pre) {
+        const int e = order[q];
+        const int n = (me[e] + kGuBM - 1) / kGuBM;
+        for (int i = 0; i < n; ++i) {
+          mt_row[pre + i] = rowoff[e] + i * kGuBM;
+          mt_exp[pre + i] = e;
+        }
+      },
+      sh);
+
+  if (tid == 0) {
+    hdr[H_ERROR] = 0;
+    hdr[H_M] = M;
+    hdr[H_BANDS] = B;
+    hdr[H_REMOTE] = n_remote;
+    hdr[H_SEGS] = NS;
+    hdr[H_RSEGS] = n_rsegs;
+    hdr[H_GU_TILES] = NMT * L.gu_ntn;
+    hdr[H_DN_TILES] = B * L.dn_tpb;
+    hdr[H_UNITS] = U;
+    hdr[H_RCOUNT] = rcount;
+    hdr[H_GU_MT] = NMT;
+  }
+}
+
+// in-wave stable rank of `v` among lanes holding the same value (v >= 0);
+// the lowest lane of each value writes the wave's count into cnt[v]
+__device__ __forceinline__ int wave_match_rank(int v, int* cnt) {
+  const int lane = threadIdx.x & 63;
+  uint64_t todo = __ballot(v >= 0);
+  int rank = 0;
+  while (todo) {
+    const int leader = __ffsll((long long)todo) - 1;
+    const int lv = __shfl(v, leader, 64);
+    const uint64_t m = __ballot(v == lv);
+    if (v == lv) rank = __popcll(m & lanes_below(lane));
+    if (lane == leader) cnt[lv] = __popcll(m);
+    todo &= ~m;
+  }
+  return rank;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_place_kernel(PlanLayout L, const int32_t* __restrict__ topk,
+                                                                 int32_t* __restrict__ ws) {
+  extern __shared__ int sh[];
+  const int32_t* hdr = ws + L.o_hdr;
+  if (hdr[H_ERROR] != 0) return;
+  const int b = blockIdx.x;
+  const int o = owner_of_block(L, b);
+  const int p0 = L.pair_off[o] + (b - L.blk_off[o]) * kPairsPerBlock;
+  const int p1 = min(p0 + kPairsPerBlock, L.pair_off[o + 1]);
+  const bool own = (o == L.r);
+  const int E_l = L.E_l, E = L.E, W = L.W;
+  const int NX = E_l + 1;              // local experts + "any local"
+  const int nw = kPlanThreads / 64;
+  int* run = sh;                       // [NX]
+  int* wc = run + NX;                  // [nw][NX]
+  int* run_g = wc + nw * NX;           // [E] (own only)
+  int* wc_g = run_g + E;               // [nw][E]
+  const int tid = threadIdx.x, w = tid >> 6;
+  for (int i = tid; i < NX * (nw + 1); i += blockDim.x) sh[i] = 0;
+  if (own)
+    for (int i = tid; i < E * (nw + 1); i += blockDim.x) run_g[i] = 0;
+  __syncthreads();
+  const int32_t* rowoff = ws + L.o_rowoff;
+  const int32_t* grp = ws + L.o_grp;
+  const int32_t* bp = ws + L.o_bp + (int64_t)b * (E_l + 1);
+  const int recv_base = ws[L.o_brecv + b];
+  int32_t* src = ws + L.o_src;
+  const int32_t* bpr = ws + L.o_bpr + (int64_t)(b - L.blk_off[L.r]) * E;
+  const int32_t* baser = ws + L.o_baser;
+  int32_t* pos = ws + L.o_pos;
+  const int lo = L.r * E_l;
+  for (int p_base = p0; p_base < p1; p_base += blockDim.x) {
+    const int p = p_base + tid;
+    const int g = (p < p1) ? topk[p] : -1;
+    const int e = (g >= lo && g < lo + E_l) ? g - lo : -1;
+    const int re = wave_match_rank(e, wc + w * NX);
+    const int rl = wave_match_rank(e >= 0 ? E_l : -1, wc + w * NX);
+    int rg = 0;
+    if (own) rg = wave_match_rank((g >= 0 && g < E) ? g : -1, wc_g + w * E);
+    __syncthreads();
+    if (e >= 0) {
+      int rank_e = run[e] + re, rank_l = run[E_l] + rl;
+      for (int x = 0; x < w; ++x) { rank_e += wc[x * NX + e]; rank_l += wc[x * NX + E_l]; }
+      const int dest = rowoff[e] + grp[e * W + o] + bp[e] + rank_e;
+      const int i = recv_base + rank_l;
+      if (dest < L.rows_cap && i < L.R) src[dest] = i;
+    }
+    if (own && g >= 0 && g < E) {
+      int rank_g = run_g[g] + rg;
+      for (int x = 0; x < w; ++x) rank_g += wc_g[x * E + g];
+      pos[p - L.pair_off[L.r]] = baser[g] + bpr[g] + rank_g;
+    }
+    __syncthreads();
+    for (int x = tid; x < NX; x += blockDim.x) {
+      int s = 0;
+      for (int y = 0; y < nw; ++y) { s += wc[y * NX + x]; wc[y * NX + x] = 0; }
+      run[x] += s;
+    }
+    if (own)
+      for (int x = tid; x < E; x += blockDim.x) {
+        int s = 0;
+        for (int y = 0; y < nw; ++y) { s += wc_g[y * E + x]; wc_g[y * E + x] = 0; }
+        run_g[x] += s;
+      }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void plan_gather_kernel(PlanLayout L, const int32_t* __restrict__ ws,
+                                                         const uint4* __restrict__ x_recv,
+                                                         uint4* __restrict__ x_layout) {
+  const int32_t* hdr = ws + L.o_hdr;
+  if (hdr[H_ERROR] != 0) return;
+  const int M = hdr[H_M];
+  const int32_t* src = ws + L.o_src;
+  const int lane = threadIdx.x & 63;
+  const int wpb = blockDim.x >> 6;
+  const int64_t vec = L.d / 8;  // 16-byte vectors per row
+  for (int row = blockIdx.x * wpb + (threadIdx.x >> 6); row < M; row += gridDim.x * wpb) {
+    const int s = src[row];
+    uint4* dst = x_layout + (int64_t)row * vec;
+    if (s >= 0) {
+      const uint4* sp = x_recv + (int64_t)s * vec;
+      for (int64_t v = lane; v < vec; v += 64) dst[v] = sp[v];
+    } else {
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      for (int64_t v = lane; v < vec; v += 64) dst[v] = z;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t* x_recv, int32_t* ws,
+                       uint16_t* x_layout, hipStream_t s) {
+  if (L.NB > 0) {
+    const size_t sh_count = (size_t)(L.E_l + 2 + L.E) * sizeof(int);
+    hipLaunchKernelGGL(plan_count_kernel, dim3(L.NB), dim3(kPlanThreads), sh_count, s, L, topk, ws);
+  }
+  hipLaunchKernelGGL(plan_build_kernel, dim3(1), dim3(kBuildThreads), 0, s, L, ws);
+  if (L.NB > 0) {
+    const int nw = kPlanThreads / 64;
+    const size_t sh_place = (size_t)((L.E_l + 1) * (nw + 1) + L.E * (nw + 1)) * sizeof(int);
+    hipLaunchKernelGGL(plan_place_kernel, dim3(L.NB), dim3(kPlanThreads), sh_place, s, L, topk, ws);
+  }
+  const int rows_per_block = 4;
+  int grid = (L.rows_cap + rows_per_block - 1) / rows_per_block;
+  if (grid > 4096) grid = 4096;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(plan_gather_kernel, dim3(grid), dim3(256), 0, s, L, (const int32_t*)ws,
+                     (const uint4*)x_recv, (uint4*)x_layout);
+  return hipGetLastError();
+}
+
+}  // namespace moe

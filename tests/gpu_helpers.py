@@ -1,0 +1,147 @@
+"""Shared pieces of the GPU parity tests: seeded workloads (synth), the oracle's
+expectations, the HIP path through the binding, and the comparison rules.
+
+Tolerance for bf16 outputs (the workload's stated bar, max-abs 2e-2 and
+relative 1e-2, read elementwise as |gpu - ref| <= 2e-2 + 1e-2 |ref|).  For the
+tiny workload, whose outputs are ~1e-5 because activations and weights are
+N(0, 0.02), the absolute term is also scaled by the reference's RMS so that the
+check is not vacuous: |gpu - ref| <= 2e-2 rms(ref) + 1e-2 |ref|.
+"""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+import torch
+
+import synth
+from oracle import bf16 as OB
+from oracle import combine as OC
+from oracle import ffn as OF
+from oracle import plan as OP
+
+ATOL, RTOL = 2e-2, 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def tol_ratio(gpu_bits, ref_bits, scale_aware=False) -> float:
+    g = OB.from_bits(gpu_bits)
+    r = OB.from_bits(ref_bits)
+    if g.size == 0:
+        return 0.0
+    atol = ATOL * (np.sqrt(np.mean(r * r)) if scale_aware else 1.0)
+    allowed = atol + RTOL * np.abs(r)
+    bad = ~np.isfinite(g)
+    ratio = np.abs(g - r) / allowed
+    ratio[bad] = np.inf
+    return float(ratio.max())
+
+
+@functools.lru_cache(maxsize=None)
+def case(name: str, mgb: int = 1):
+    cfg = synth.get_config(name, mgb=mgb)
+    ids, w = synth.routing(cfg)
+    x_owner = synth.activations(cfg)
+    x_recv, tok = synth.dispatch(cfg, ids, x_owner)
+    plan = OP.build_plan(ids, cfg.tokens, cfg.rank, cfg.E_l, cfg.tb_m, mgb)
+    return dict(cfg=cfg, ids=ids, w=w, x_owner=x_owner, x_recv=x_recv, tok=tok, plan=plan)
+
+
+@functools.lru_cache(maxsize=None)
+def weights(name: str):
+    cfg = synth.get_config(name)
+    return synth.local_weights(cfg)
+
+
+def shape_of(cfg, R, rank=None):
+    import moe_expert_tile_amd as m
+    r = cfg.rank if rank is None else rank
+    return m.Shape(cfg.W, r, cfg.E_l, cfg.k, cfg.d, cfg.f, cfg.tb_m, cfg.tokens, R, mgb=cfg.mgb)
+
+
+def owner_slice(cfg, o):
+    off = OP.owner_offsets(cfg.tokens)
+    return slice(int(off[o]), int(off[o + 1]))
+
+
+def plan_arrays(share, pl_gpu_hdr):
+    """Plan metadata read back from the workspace."""
+    s = share.shape.c
+    E_l, W = s.experts_per_rank, s.world
+    B = pl_gpu_hdr["bands"]
+    NS = pl_gpu_hdr["segments"]
+    M = pl_gpu_hdr["M"]
+    T_r = share.shape.tokens[s.rank]
+    a = {}
+    a["c"] = share.array("c", E_l * W).reshape(E_l, W)
+    a["grp_off"] = share.array("grp_off", E_l * W).reshape(E_l, W)
+    a["m_e"] = share.array("m_e", E_l)
+    a["row_off"] = share.array("row_off", E_l + 1)
+    a["rb"] = share.array("rb", E_l)
+    a["order"] = share.array("order", E_l)
+    a["base"] = share.array("base", W * E_l).reshape(W, E_l)
+    for k in ["band_expert", "band_dst", "band_src_row", "band_dst_off", "band_valid"]:
+        a[k] = share.array(k, B)
+    for k in ["seg_first", "seg_nbands", "seg_dst", "seg_dst_off", "seg_src_row", "seg_rows"]:
+        a[k] = share.array(k, NS)
+    a["src_index"] = share.array("src_index", M)
+    a["pos"] = share.array("pos", T_r * s.top_k).reshape(T_r, s.top_k)
+    return a
+
+
+def expected_plan(pl):
+    """The oracle plan in the same naming as plan_arrays."""
+    b, sg = pl.bands, pl.segs
+    return {
+        "c": pl.c, "grp_off": pl.grp_off, "m_e": pl.m_e, "row_off": pl.row_off, "rb": pl.rb,
+        "order": pl.expert_order, "base": pl.base,
+        "band_expert": b["expert"], "band_dst": b["dst"], "band_src_row": b["src_row"],
+        "band_dst_off": b["dst_off"], "band_valid": b["valid"],
+        "seg_first": sg["first_band"], "seg_nbands": sg["n_bands"], "seg_dst": sg["dst"],
+        "seg_dst_off": sg["dst_off"], "seg_src_row": sg["src_row"], "seg_rows": sg["rows"],
+        "src_index": pl.src_index, "pos": pl.pos,
+    }
+
+
+def sample_rows(pl, n_random=192, seed=0):
+    """Layout rows for sampled FFN checks: first and last row of every X_e,
+    the first row of every band, the last valid row of every band, one
+    padding row per padded band, and random rows."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for e in range(pl.E_l):
+        if pl.m_e[e] > 0:
+            rows.add(int(pl.row_off[e]))
+            rows.add(int(pl.row_off[e + 1] - 1))
+    b = pl.bands
+    for s in range(pl.n_bands):
+        rows.add(int(b["src_row"][s]))
+        rows.add(int(b["src_row"][s] + b["valid"][s] - 1))
+        if b["remote"][s] and b["valid"][s] < pl.tb_m:
+            rows.add(int(b["src_row"][s] + b["valid"][s]))
+    if pl.M:
+        rows.update(int(x) for x in rng.integers(0, pl.M, n_random))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def oracle_ffn_rows(name, pl, x_layout_bits, rows):
+    wgu, wd = weights(name)
+    return OF.layout_rows(pl, x_layout_bits, wgu, wd, rows)
+
+
+def layout_x(pl, x_recv):
+    return OC.layout_x(pl, x_recv)

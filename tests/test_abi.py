@@ -1,0 +1,104 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/moe.h declares, sizes follow the padding bound of the tile-signal
+notes (§4.3: at most (W-1)(tb_M-1) padding rows per local expert), and the
+host-side validation rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "moe_expert_tile_amd", "libmoe.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmoe.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    import moe_expert_tile_amd as m
+    assert sorted(m.EXPORTED) == names
+
+
+def _shape(**kw):
+    import moe_expert_tile_amd as m
+    base = dict(world=4, rank=0, experts_per_rank=2, top_k=2, hidden=512, ffn=1024, tb_m=64,
+                tokens=[256] * 4, recv_rows=500, mgb=1)
+    base.update(kw)
+    return m.Shape(**base)
+
+
+def test_sizes_follow_the_padding_bound():
+    import moe_expert_tile_amd as m
+    for W, E_l, tb, R in [(4, 2, 64, 500), (8, 32, 256, 46000), (16, 8, 32, 511), (1, 3, 128, 77)]:
+        s = _shape(world=W, rank=W - 1, experts_per_rank=E_l, tb_m=tb, tokens=[64] * W,
+                   recv_rows=min(R, 64 * W * 2), top_k=2)
+        z = m.moe_query_sizes(s)
+        R = s.recv_rows
+        assert z["rows_cap"] == R + E_l * (W - 1) * (tb - 1)
+        assert z["bands_cap"] == z["rows_cap"] // tb + E_l * W
+        assert z["recv_rows_self"] == 64 * 2
+        assert z["plan_bytes"] % 256 == 0
+        off = m.moe_plan_offsets(s)
+        vals = sorted(off.values())
+        assert all(v % 256 == 0 for v in vals)
+        assert len(set(vals)) == len(vals)
+        assert max(vals) < z["plan_bytes"]
+
+
+@pytest.mark.parametrize("bad", [
+    dict(world=0), dict(world=65), dict(rank=4), dict(rank=-1), dict(experts_per_rank=0),
+    dict(experts_per_rank=300), dict(top_k=0), dict(top_k=9), dict(hidden=500), dict(hidden=128),
+    dict(ffn=1000), dict(tb_m=48), dict(tb_m=16), dict(tb_m=512), dict(mgb=0),
+    dict(tokens=[256, -1, 256, 256]), dict(recv_rows=-1), dict(recv_rows=4 * 256 * 2 + 1),
+])
+def test_bad_shapes_are_rejected(bad):
+    import moe_expert_tile_amd as m
+    with pytest.raises(m.MoEError) as ei:
+        m.moe_query_sizes(_shape(**bad))
+    assert ei.value.status == m.MOE_EINVAL
+
+
+def test_bad_pointers_are_rejected_before_any_hip_call():
+    import moe_expert_tile_amd as m
+    s = _shape()
+    good = 1 << 20  # never dereferenced: validation fails first
+    with pytest.raises(m.MoEError) as ei:
+        m.moe_plan(s, good, good, 0, good, stream=0)
+    assert ei.value.status == m.MOE_EINVAL
+    with pytest.raises(m.MoEError) as ei:
+        m.moe_plan(s, good, good + 8, good, good, stream=0)        # misaligned x_recv
+    assert ei.value.status == m.MOE_EINVAL
+    with pytest.raises(m.MoEError) as ei:
+        m.moe_expert_combine(s, good, good, good, good, good, good, good, 0, [good] * 4, stream=0)
+    assert ei.value.status == m.MOE_EINVAL                        # epoch 0
+    with pytest.raises(m.MoEError) as ei:
+        m.moe_expert_combine(s, good, good, good, good, good, good, good, 1, [good] * 4,
+                             consumer_cus=12, stream=0)
+    assert ei.value.status == m.MOE_EINVAL                        # not a multiple of 8
+    with pytest.raises(m.MoEError) as ei:
+        m.moe_expert_combine(s, good, good, good, good, good, good, good, 1, [good, 0, good, good],
+                             stream=0)
+    assert ei.value.status == m.MOE_EINVAL                        # null receive buffer
+    with pytest.raises(m.MoEError) as ei:
+        m.moe_scale(s, good, good, good, good + 2, stream=0)
+    assert ei.value.status == m.MOE_EINVAL
+    assert m.moe_device_status(0, stream=0) == m.MOE_EINVAL
+
+
+def test_status_strings():
+    import moe_expert_tile_amd as m
+    for code in range(7):
+        assert m.status_string(code)
+    assert m.status_string(99) == "unknown status"
