@@ -1,0 +1,245 @@
+"""Benchmark: one expert-parallel rank's share of an MoE layer on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+moe_plan (owner-aligned layout, remote-first schedule, combine plan) ->
+moe_expert_combine (gate/up GEMM + SwiGLU, down GEMM with tile flags in
+parallel with the consumer copy on reserved CUs) -> moe_scale.  Inputs are
+resident in HBM before the timed region.  The default workload is the
+Mixtral-8x7B-like layer (W=4 ranks, 8 experts, 4096 tokens per owner,
+d=4096, f=14336, top-2, tb_M=128), rank 0's share.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode overlap|serial]
+                    [--consumer-cus C] [--no-cpu-baseline]
+
+Prints one JSON line.  value = tokens/s = (tokens per owner) / (time per
+step): the per-GPU rate if every rank took as long as rank 0.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+METRIC = "MoE-layer tokens/s on 1 MI355X; grouped-GEMM TFLOP/s & combine GB/s vs peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--mode", default="overlap", choices=["overlap", "serial"])
+    ap.add_argument("--consumer-cus", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def dev_bf16(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def algorithmic(cfg, R, M, n_seg_rows):
+    """Work per call (the rank-0 share) in the units the rooflines use."""
+    d, f, k, T_r = cfg.d, cfg.f, cfg.k, cfg.tokens[cfg.rank]
+    N = cfg.N
+    return {
+        "gateup_flop": 4.0 * d * f * M,          # executed rows, padding included
+        "down_flop": 2.0 * d * f * M,
+        "useful_flop": 6.0 * d * f * R,
+        "plan_bytes": 4.0 * N * k + 2.0 * d * R + 2.0 * d * M + 4.0 * M + 4.0 * T_r * k,
+        "combine_bytes": 4.0 * d * n_seg_rows,   # valid rows read + written
+        "scale_bytes": 2.0 * d * k * T_r + 2.0 * d * T_r + 8.0 * k * T_r,
+    }
+
+
+def cpu_baseline(cfg, ids, w, x_recv, wgu, wd, budget_s):
+    """The oracle as it stands on the host, on a bounded sample: the full plan,
+    the FFN on a sample of layout rows (extrapolated to all M rows), the
+    combine and the scale of the rank's tokens."""
+    from oracle import combine as OC, ffn as OF, plan as OP, scale as OS
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    pl = OP.build_plan(ids, cfg.tokens, cfg.rank, cfg.E_l, cfg.tb_m, cfg.mgb)
+    X = OC.layout_x(pl, x_recv)
+    t_plan = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    n = 64
+    t_ffn_rows, rows_done = 0.0, 0
+    while t_ffn_rows < budget_s * 0.6 and rows_done < pl.M:
+        rows = rng.integers(0, pl.M, n)
+        t1 = time.perf_counter()
+        OF.layout_rows(pl, X, wgu, wd, rows)
+        t_ffn_rows += time.perf_counter() - t1
+        rows_done += n
+        n = min(2 * n, 1024)
+    t_ffn = t_ffn_rows / max(rows_done, 1) * pl.M
+    Y = np.zeros((pl.M, cfg.d), np.uint16)
+    recv = [np.zeros((t * cfg.k, cfg.d), np.uint16) for t in cfg.tokens]
+    t2 = time.perf_counter()
+    recv = OC.apply(pl, Y, recv)
+    t_comb = time.perf_counter() - t2
+    t3 = time.perf_counter()
+    OS.scale(recv[cfg.rank], w[: cfg.tokens[cfg.rank]], pl.pos)
+    t_scale = time.perf_counter() - t3
+    total = t_plan + t_ffn + t_comb + t_scale
+    return {
+        "value": cfg.tokens[cfg.rank] / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"full plan+layout ({t_plan:.2f}s), FFN on {rows_done} of {pl.M} layout rows "
+                  f"({t_ffn_rows:.2f}s, extrapolated to {t_ffn:.1f}s), full combine ({t_comb:.2f}s) "
+                  f"and scale ({t_scale:.2f}s); float64 NumPy",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU only (the W ranks are emulated as HBM partitions on it); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_expert_tile_amd as m
+    import synth
+
+    cfg = synth.get_config(args.workload)
+    ids, w = synth.routing(cfg)
+    x_owner = synth.activations(cfg)
+    x_recv, _ = synth.dispatch(cfg, ids, x_owner)
+    wgu, wd = synth.local_weights(cfg)
+    R = x_recv.shape[0]
+    T_r = cfg.tokens[cfg.rank]
+
+    share = m.RankShare(m.Shape(cfg.W, cfg.rank, cfg.E_l, cfg.k, cfg.d, cfg.f, cfg.tb_m, cfg.tokens, R,
+                                mgb=cfg.mgb))
+    ids_d = torch.from_numpy(ids).cuda()
+    xr_d = dev_bf16(x_recv, torch)
+    wgu_d, wd_d = dev_bf16(wgu, torch), dev_bf16(wd, torch)
+    w_r = torch.from_numpy(np.ascontiguousarray(w[:T_r])).cuda()
+    for o in range(cfg.W):
+        share.recv[o].copy_(dev_bf16(synth.foreign_rows(cfg, o), torch))
+    mode = m.MODE_OVERLAP if args.mode == "overlap" else m.MODE_SERIAL
+    stream = torch.cuda.current_stream()
+
+    n_ev = args.steps
+    ev_plan = [m.timing_events(2) for _ in range(n_ev)]
+    ev_comb = [m.timing_events(6) for _ in range(n_ev)]
+    ev_scale = [m.timing_events(2) for _ in range(n_ev)]
+
+    def step(i=None):
+        if i is not None:
+            ev_plan[i][0].record(stream)
+        share.plan(ids_d, xr_d)
+        if i is not None:
+            ev_plan[i][1].record(stream)
+        share.combine(wgu_d, wd_d, mode=mode, consumer_cus=args.consumer_cus,
+                      events=ev_comb[i] if i is not None else None)
+        if i is not None:
+            ev_scale[i][0].record(stream)
+        share.scale(w_r)
+        if i is not None:
+            ev_scale[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = share.status()
+    if st != m.MOE_OK:
+        raise SystemExit(f"device status after warmup: {m.status_string(st)}")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = share.status()
+    if st != m.MOE_OK:
+        raise SystemExit(f"device status after timed steps: {m.status_string(st)}")
+    ms = elapsed / args.steps * 1e3
+
+    def avg(pairs):
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e-3
+
+    t_plan = avg([(e[0], e[1]) for e in ev_plan])
+    t_gu = avg([(e[0], e[1]) for e in ev_comb])
+    t_dn = avg([(e[2], e[3]) for e in ev_comb])
+    t_cons = avg([(e[4], e[5]) for e in ev_comb])
+    t_ec = avg([(e[0], ev_scale[i][0]) for i, e in enumerate(ev_comb)])
+    t_scale = avg([(e[0], e[1]) for e in ev_scale])
+    hdr = share.header()
+    M = hdr["M"]
+    seg_rows = int(share.array("seg_rows", hdr["segments"]).sum()) if hdr["segments"] else 0
+    work = algorithmic(cfg, R, M, seg_rows)
+
+    # standalone consumer (flags already set by the last call; all CUs)
+    ev_copy = [m.timing_events(6) for _ in range(5)]
+    for e in ev_copy:
+        share.combine(None, None, mode=m.MODE_COPY_ONLY, events=e, epoch=share.epoch)
+    torch.cuda.synchronize()
+    t_copy = avg([(e[4], e[5]) for e in ev_copy])
+
+    gu_tflops = work["gateup_flop"] / t_gu
+    result = {
+        "metric": METRIC,
+        "value": round(T_r / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: rank {cfg.rank} share of W={cfg.W} ranks, E={cfg.E} experts "
+                        f"({cfg.E_l} local), {cfg.tokens[0]} tokens per owner, d={cfg.d}, f={cfg.f} SwiGLU, "
+                        f"top-{cfg.k}, tb_M={cfg.tb_m}, mgb={cfg.mgb}",
+            "mode": args.mode, "consumer_cus": args.consumer_cus, "R": R, "M": M,
+            "padding_pct": round(100.0 * (M - R) / max(M, 1), 2),
+        },
+        "roofline": {
+            "kernel": "gate/up grouped GEMM + SwiGLU (grouped_gemm_kernel, gate/up instance)",
+            "bound": "mfma", "achieved": round(gu_tflops / 1e12, 2), "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16, 4), "traffic": None,
+        },
+        "stages_us": {
+            "plan": round(t_plan * 1e6, 2), "gateup_gemm": round(t_gu * 1e6, 2),
+            "down_gemm": round(t_dn * 1e6, 2), "consumer_overlapped": round(t_cons * 1e6, 2),
+            "expert_combine": round(t_ec * 1e6, 2), "scale": round(t_scale * 1e6, 2),
+            "consumer_standalone": round(t_copy * 1e6, 2),
+        },
+        "rates": {
+            "gateup_TFLOPs": round(gu_tflops / 1e12, 2),
+            "down_TFLOPs": round(work["down_flop"] / t_dn / 1e12, 2),
+            "plan_GBs": round(work["plan_bytes"] / t_plan / 1e9, 1),
+            "combine_standalone_GBs": round(work["combine_bytes"] / t_copy / 1e9, 1),
+            "scale_GBs": round(work["scale_bytes"] / t_scale / 1e9, 1),
+            "plan_frac_hbm": round(work["plan_bytes"] / t_plan / PEAK_HBM, 4),
+            "combine_frac_hbm": round(work["combine_bytes"] / t_copy / PEAK_HBM, 4),
+            "scale_frac_hbm": round(work["scale_bytes"] / t_scale / PEAK_HBM, 4),
+            "down_frac_mfma": round(work["down_flop"] / t_dn / PEAK_BF16, 4),
+            "routed_rows_per_s": round(R / (ms * 1e-3), 1),
+        },
+        "work": {k: v for k, v in work.items()},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, ids, w, x_recv, wgu, wd, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -114,7 +114,9 @@ def test_edge_case_rank_share(case_name):
     pl = OP.build_plan(ids, cfg.tokens, r, cfg.E_l, cfg.tb_m, cfg.mgb)
     say(f"[edge] {case_name} R={pl.R} M={pl.M} bands={pl.n_bands}")
     sh = m.RankShare(_shape(cfg, r, pl.R))
-    sentinel = [np.full((max(1, t * cfg.k), cfg.d), 0x7F7F, np.uint16) for t in cfg.tokens]
+    # other ranks' rows (finite, distinct): any stray write would change them
+    sentinel = [synth.foreign_rows(cfg, o) if cfg.tokens[o] else np.zeros((1, cfg.d), np.uint16)
+                for o in range(cfg.W)]
     for o in range(cfg.W):
         sh.recv[o].copy_(dev_bf16(sentinel[o]))
     ids_d = torch.from_numpy(ids).cuda() if ids.size else torch.zeros(1, dtype=torch.int32, device="cuda")

@@ -140,9 +140,12 @@ def test_scale_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_unit", "qwen3", "dsv3_skew"])
-def test_scale_alone_within_one_ulp(name):
-    """Scale on fixed receive rows (no GEMM in between): fp32 on the GPU vs
-    float64 in the oracle differ by at most one bf16 ulp."""
+def test_scale_alone_within_rounding_bound(name):
+    """Scale on fixed receive rows (no GEMM in between).  The GPU sums k fp32
+    products in order; the oracle sums in float64 and rounds once.  Their
+    difference is bounded by one bf16 ulp of the result plus the fp32
+    accumulation error, k * 2^-23 * sum_j |w_j x_j| (standard bound for
+    recursive summation with fused multiply-add)."""
     import moe_expert_tile_amd as m
     c, share, _, _ = planned(name, m.MODE_OVERLAP)
     cfg, pl = c["cfg"], c["plan"]
@@ -152,6 +155,12 @@ def test_scale_alone_within_one_ulp(name):
     w_r = c["w"][owner_slice(cfg, r)]
     share.scale(torch.from_numpy(w_r).cuda())
     assert share.status() == m.MOE_OK
-    out = host_bits(share.out[: cfg.tokens[r]])
-    ref = OS.scale(recv_r, w_r, pl.pos)
-    assert int(OB.ulp_distance(out, ref).max()) <= 1
+    out = OB.from_bits(host_bits(share.out[: cfg.tokens[r]]))
+    ref_bits = OS.scale(recv_r, w_r, pl.pos)
+    ref = OB.from_bits(ref_bits)
+    absum = np.einsum("tk,tkd->td", np.abs(w_r.astype(np.float64)), np.abs(OB.from_bits(recv_r[pl.pos])))
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.maximum(np.abs(ref), np.abs(out)), 1e-38))[1] - 8)
+    bound = ulp + cfg.k * 2.0 ** -23 * absum
+    excess = float((np.abs(out - ref) / bound).max())
+    say(f"[scale-bound] {name} worst {excess:.3f}, max ulps {int(OB.ulp_distance(host_bits(share.out[: cfg.tokens[r]]), ref_bits).max())}")
+    assert excess <= 1.0
