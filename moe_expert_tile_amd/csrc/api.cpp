@@ -6,7 +6,7 @@
 #include <mutex>
 #include <string.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -24,6 +24,8 @@ int valid_shape(const moe_shape* s) {
   if (s->top_k < 1 || s->top_k > 32 || s->top_k > E) return MOE_EINVAL;
   if (s->hidden < 256 || s->hidden % 256 != 0 || s->hidden > 65536) return MOE_EINVAL;
   if (s->ffn < 128 || s->ffn % 128 != 0 || s->ffn > 65536) return MOE_EINVAL;
+  // the GEMMs address one expert's weights with 32-bit byte offsets
+  if ((int64_t)s->ffn * s->hidden >= (1ll << 30)) return MOE_EINVAL;
   if (s->tb_m < 32 || s->tb_m > 256 || s->tb_m % 32 != 0) return MOE_EINVAL;
   if (s->mgb < 1 || s->mgb > 64) return MOE_EINVAL;
   int64_t pairs = 0;
