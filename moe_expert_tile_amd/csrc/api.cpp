@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string.h>
 
@@ -75,6 +76,7 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->dn_tpb = L->dn_sub * L->dn_ntn;
   L->gu_ntn = f / (kGuBN / 2);
   L->gu_mt_cap = (int)(rows_cap / kGuBM + E_l + 1);
+  L->build_stage = 0;  // decided at launch, against the device's LDS limit
 
   int64_t off = 0;
   auto take = [&](int64_t n) {
@@ -105,7 +107,6 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->o_baser = take(L->E);
   L->o_gumt_row = take(L->gu_mt_cap);
   L->o_gumt_exp = take(L->gu_mt_cap);
-  L->o_gscr = take(3 * EW + 1);
   L->total_words = off;
   return true;
 }
@@ -116,6 +117,7 @@ namespace {
 struct DeviceState {
   bool init = false;
   int cus = 0;
+  int lds_per_block = 0;
   int consumer_cus = -1;
   hipStream_t prod = nullptr, cons = nullptr;
   hipEvent_t fork = nullptr, join_p = nullptr, join_c = nullptr;
@@ -133,9 +135,11 @@ int current_device(int* dev) {
 int device_cus(int dev) {
   DeviceState& st = g_dev[dev];
   if (!st.init) {
-    int n = 0;
+    int n = 0, lds = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
     st.cus = n;
+    st.lds_per_block = lds;
     st.init = true;
   }
   return st.cus;
@@ -272,6 +276,11 @@ int moe_plan(const moe_shape* s, const int32_t* topk_ids, const uint16_t* x_recv
   int dev;
   rc = prepare(&dev);
   if (rc) return rc;
+  // the plan builder copies the per-block histograms into LDS only when the
+  // whole request fits well inside the device's per-workgroup LDS
+  const int64_t stage_bytes =
+      ((int64_t)build_lds_words(L.W, L.E_l, L.E) + (int64_t)L.NB * (L.E_l + 2) + (int64_t)L.NB_r * L.E) * 4;
+  L.build_stage = stage_bytes <= std::min<int64_t>(g_dev[dev].lds_per_block, kBuildLdsBytes);
   return hip_rc(launch_plan(L, topk_ids, x_recv, (int32_t*)plan_ws, x_layout, (hipStream_t)stream));
 }
 

@@ -83,15 +83,30 @@ __global__ __launch_bounds__(256) void consumer_kernel(PlanLayout L, int32_t* __
     const int64_t hi = min(lo + (int64_t)kCopyChunk, bytes);
     const uint64_t* src = (const uint64_t*)(y + (int64_t)ssrc[seg] * d);
     uint4* dst = (uint4*)(recv.p[sdst[seg]] + (int64_t)sdoff[seg] * d);
-    for (int64_t off = lo + tid * 16; off < hi; off += 256 * 16) {
-      const uint64_t a = agent_load64(src + off / 8);
-      const uint64_t b = agent_load64(src + off / 8 + 1);
-      uint4 v;
-      v.x = (uint32_t)a;
-      v.y = (uint32_t)(a >> 32);
-      v.z = (uint32_t)b;
-      v.w = (uint32_t)(b >> 32);
-      dst[off / 16] = v;
+    // 4 vectors of 16 bytes per thread per pass, all loads issued before the stores
+    constexpr int V = 4;
+    for (int64_t off = lo + tid * 16; off < hi; off += 256 * 16 * V) {
+      uint64_t a[V], b[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int64_t o = off + (int64_t)i * 256 * 16;
+        if (o < hi) {
+          a[i] = agent_load64(src + o / 8);
+          b[i] = agent_load64(src + o / 8 + 1);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int64_t o = off + (int64_t)i * 256 * 16;
+        if (o < hi) {
+          uint4 v;
+          v.x = (uint32_t)a[i];
+          v.y = (uint32_t)(a[i] >> 32);
+          v.z = (uint32_t)b[i];
+          v.w = (uint32_t)(b[i] >> 32);
+          dst[o / 16] = v;
+        }
+      }
     }
   }
 }

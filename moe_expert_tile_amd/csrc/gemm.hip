@@ -122,7 +122,8 @@ __device__ __forceinline__ void stage_barrier(int stages_in_flight) {
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x8, kSchedVmem = 0x10, kSchedDsRead = 0x100;
 
-// Tile t of a (n_mt x n_nt) grid in grouped order -> (mt, nt).
+// Tile t of a (n_mt x n_nt) grid in grouped order -> (mt, nt): groups of
+// kGroupM row tiles sweep all column tiles.
 __device__ __forceinline__ void decode_tile(int t, int n_mt, int n_nt, int& mt, int& nt) {
   const int per_group = kGroupM * n_nt;
   const int g = t / per_group;

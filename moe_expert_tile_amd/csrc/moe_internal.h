@@ -8,7 +8,7 @@
 namespace moe {
 
 constexpr int kMaxWorld = 64;
-constexpr int kPairsPerBlock = 2048;   // (token, slot) pairs per planner workgroup
+constexpr int kPairsPerBlock = 512;    // (token, slot) pairs per planner workgroup
 constexpr int kPlanThreads = 256;
 constexpr int kBuildThreads = 1024;    // the single-workgroup plan builder
 constexpr int kCopyChunk = 32768;      // bytes per consumer copy unit
@@ -30,12 +30,13 @@ struct PlanLayout {
   int R, rows_cap, bands_cap, T_r, NB, NB_r, gu_mt_cap;
   int dn_bm, dn_sub, dn_ntn, dn_tpb;   // down GEMM: tile rows, tiles per band row, n tiles, tiles per band
   int gu_ntn;                          // gate/up GEMM n tiles (f / 128)
+  int build_stage;                     // plan_build copies the block histograms into LDS
   int64_t o_hdr, o_c, o_low, o_grp, o_me, o_rowoff, o_rb, o_order, o_base;
   int64_t o_bexp, o_bdst, o_bsrc, o_bdoff, o_bval;
   int64_t o_sfirst, o_snb, o_sdst, o_sdoff, o_ssrc, o_srows, o_sunit;
   int64_t o_src, o_pos;
   int64_t o_bh, o_bp, o_brecv, o_bhr, o_bpr, o_baser;
-  int64_t o_gumt_row, o_gumt_exp, o_gscr;
+  int64_t o_gumt_row, o_gumt_exp;
   int64_t total_words;
   int pair_off[kMaxWorld + 1];   // first (token, slot) pair of each owner
   int blk_off[kMaxWorld + 1];    // first planner block of each owner
@@ -45,6 +46,14 @@ struct PlanLayout {
 struct RecvPtrs {
   uint16_t* p[kMaxWorld];
 };
+
+// LDS words of plan_build_kernel: the expert x owner tables and the per-group
+// scratch stay on chip; only the results are written out.
+inline int build_lds_words(int W, int E_l, int E) {
+  const int EW = E_l * W;
+  return 6 * EW + W + 3 * E_l + 1 + E + 64;
+}
+constexpr int kBuildLdsBytes = 32 * 1024;   // cap on plan_build's dynamic LDS
 
 // host-side helpers (api.cpp)
 bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb,

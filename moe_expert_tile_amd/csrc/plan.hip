@@ -107,25 +107,41 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(PlanLayout L, 
 }
 
 __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L, int32_t* __restrict__ ws) {
-  __shared__ int sh[64];
+  extern __shared__ int smem[];
   const int tid = threadIdx.x, nt = blockDim.x;
   const int W = L.W, r = L.r, E_l = L.E_l, E = L.E, tb = L.tb_m;
   const int HB = E_l + 2;
+  const int EW = E_l * W;
   int32_t* hdr = ws + L.o_hdr;
-  int32_t* c = ws + L.o_c;
-  int32_t* low = ws + L.o_low;
-  int32_t* grp = ws + L.o_grp;
-  int32_t* me = ws + L.o_me;
-  int32_t* rowoff = ws + L.o_rowoff;
-  int32_t* rb = ws + L.o_rb;
-  int32_t* order = ws + L.o_order;
-  int32_t* base = ws + L.o_base;
+  int* c = smem;                 // [E_l][W]
+  int* grp = c + EW;             // [E_l][W]
+  int* base = grp + EW;          // [W][E_l]
+  int* gstart = base + EW;       // [E_l*W] per-group band start
+  int* gseg = gstart + EW;       // [E_l*W] per-group segment base
+  int* gunit = gseg + EW;        // [E_l*W] per-group copy-unit base
+  int* low = gunit + EW;         // [W]
+  int* me = low + W;             // [E_l]
+  int* rowoff = me + E_l;        // [E_l + 1]
+  int* rb = rowoff + E_l + 1;    // [E_l]
+  int* order = rb + E_l;         // [E_l]
+  int* baser = order + E_l;      // [E]
+  int* sh = baser + E;           // [64] scan scratch
   const int32_t* bh = ws + L.o_bh;
   int32_t* bp = ws + L.o_bp;
   int32_t* brecv = ws + L.o_brecv;
   const int32_t* bhr = ws + L.o_bhr;
   int32_t* bpr = ws + L.o_bpr;
-  int32_t* baser = ws + L.o_baser;
+  if (L.build_stage) {
+    // the per-block histograms are read many times below: one coalesced
+    // parallel copy into LDS, after the tables (the host sized the LDS for it)
+    int* s_bh = sh + 64;
+    int* s_bhr = s_bh + L.NB * HB;
+    for (int i = tid; i < L.NB * HB; i += nt) s_bh[i] = bh[i];
+    for (int i = tid; i < L.NB_r * E; i += nt) s_bhr[i] = bhr[i];
+    __syncthreads();
+    bh = s_bh;
+    bhr = s_bhr;
+  }
 
   // (a) routing errors
   int bad_local = 0;
@@ -234,10 +250,6 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     group_eo(gi, e, o);
     return (c[e * W + o] + tb - 1) / tb;
   };
-  // per-group scratch: band start, segment base, unit base
-  int32_t* gstart = ws + L.o_gscr;
-  int32_t* gseg = gstart + NG;
-  int32_t* gunit = gseg + NG;
   const int B = scan_items(NG, group_nb, [&](int gi, int pre) { gstart[gi] = pre; }, sh);
   int nrem_local = 0;
   for (int gi = tid; gi < NGR; gi += nt) nrem_local += group_nb(gi);
@@ -371,6 +383,20 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
       },
       sh);
 
+  // results used by later kernels and by inspection
+  for (int i = tid; i < EW; i += nt) {
+    ws[L.o_c + i] = c[i];
+    ws[L.o_grp + i] = grp[i];
+    ws[L.o_base + i] = base[i];
+  }
+  for (int i = tid; i < W; i += nt) ws[L.o_low + i] = low[i];
+  for (int i = tid; i < E_l; i += nt) {
+    ws[L.o_me + i] = me[i];
+    ws[L.o_rb + i] = rb[i];
+    ws[L.o_order + i] = order[i];
+  }
+  for (int i = tid; i <= E_l; i += nt) ws[L.o_rowoff + i] = rowoff[i];
+  for (int i = tid; i < E; i += nt) ws[L.o_baser + i] = baser[i];
   if (tid == 0) {
     hdr[H_ERROR] = 0;
     hdr[H_M] = M;
@@ -502,7 +528,8 @@ hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t*
     const size_t sh_count = (size_t)(L.E_l + 2 + L.E) * sizeof(int);
     hipLaunchKernelGGL(plan_count_kernel, dim3(L.NB), dim3(kPlanThreads), sh_count, s, L, topk, ws);
   }
-  hipLaunchKernelGGL(plan_build_kernel, dim3(1), dim3(kBuildThreads), 0, s, L, ws);
+  const int words = build_lds_words(L.W, L.E_l, L.E) + (L.build_stage ? L.NB * (L.E_l + 2) + L.NB_r * L.E : 0);
+  hipLaunchKernelGGL(plan_build_kernel, dim3(1), dim3(kBuildThreads), (size_t)words * sizeof(int), s, L, ws);
   if (L.NB > 0) {
     const int nw = kPlanThreads / 64;
     const size_t sh_place = (size_t)((L.E_l + 1) * (nw + 1) + L.E * (nw + 1)) * sizeof(int);

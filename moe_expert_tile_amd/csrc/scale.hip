@@ -2,8 +2,10 @@
 // ("MoE 计算-通信细粒度重叠：用 Tile 级信号把 All-to-All 藏在 GEMM 背后", §2.2; §2.1: the
 // layer output is the gate-weighted sum of the k selected experts' outputs).
 //   out[t] = bf16( sum_{j<k} w[t][j] * recv[pos[t][j]] ), fp32, j ascending.
-// One thread per 16-byte output vector: k coalesced 16-byte row loads, fp32
-// fused multiply-adds, one round-to-nearest-even conversion, one 16-byte store.
+// One wavefront per run of 256 16-byte output vectors of a token: each lane
+// keeps 4k row loads in flight (each a contiguous 1 KB access across the
+// wavefront), fp32 fused multiply-adds in slot order, one round-to-nearest-
+// even conversion per value, 16-byte stores.
 #include "moe_internal.h"
 
 namespace moe {
@@ -24,28 +26,51 @@ __global__ __launch_bounds__(256) void scale_kernel(PlanLayout L, const int32_t*
   const int32_t* pos = ws + L.o_pos;
   const int k = L.k;
   const int64_t vec = L.d / 8;
-  const int64_t total = (int64_t)L.T_r * vec;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / vec, v = i - t * vec;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // a wavefront takes a run of 64*VPT vectors of one token's row; lane l
+  // handles vectors l, l+64, l+128, l+192 of the run, so each of its VPT*k
+  // row loads is a contiguous 1 KB access across the wavefront
+  constexpr int VPT = 4, RUN = 64 * VPT;
+  const int64_t runs = (vec + RUN - 1) / RUN;
+  const int64_t total_waves = (int64_t)L.T_r * runs;
+  const int lane = threadIdx.x & 63;
+  const int64_t wpb = blockDim.x >> 6;
+  for (int64_t wv = (int64_t)blockIdx.x * wpb + (threadIdx.x >> 6); wv < total_waves; wv += (int64_t)gridDim.x * wpb) {
+    const int64_t t = wv / runs;
+    const int64_t v0 = (wv - t * runs) * RUN + lane;
+    float acc[VPT][8];
+#pragma unroll
+    for (int q = 0; q < VPT; ++q)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[q][c] = 0.f;
     for (int j = 0; j < k; ++j) {
       const float wj = w[t * k + j];
-      const uint4 x = recv[(int64_t)pos[t * k + j] * vec + v];
-      acc[0] = fmaf(wj, bf_lo(x.x), acc[0]);
-      acc[1] = fmaf(wj, bf_hi(x.x), acc[1]);
-      acc[2] = fmaf(wj, bf_lo(x.y), acc[2]);
-      acc[3] = fmaf(wj, bf_hi(x.y), acc[3]);
-      acc[4] = fmaf(wj, bf_lo(x.z), acc[4]);
-      acc[5] = fmaf(wj, bf_hi(x.z), acc[5]);
-      acc[6] = fmaf(wj, bf_lo(x.w), acc[6]);
-      acc[7] = fmaf(wj, bf_hi(x.w), acc[7]);
+      const uint4* row = recv + (int64_t)pos[t * k + j] * vec;
+      uint4 x[VPT];
+#pragma unroll
+      for (int q = 0; q < VPT; ++q) x[q] = (v0 + 64 * q < vec) ? row[v0 + 64 * q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < VPT; ++q) {
+        acc[q][0] = fmaf(wj, bf_lo(x[q].x), acc[q][0]);
+        acc[q][1] = fmaf(wj, bf_hi(x[q].x), acc[q][1]);
+        acc[q][2] = fmaf(wj, bf_lo(x[q].y), acc[q][2]);
+        acc[q][3] = fmaf(wj, bf_hi(x[q].y), acc[q][3]);
+        acc[q][4] = fmaf(wj, bf_lo(x[q].z), acc[q][4]);
+        acc[q][5] = fmaf(wj, bf_hi(x[q].z), acc[q][5]);
+        acc[q][6] = fmaf(wj, bf_lo(x[q].w), acc[q][6]);
+        acc[q][7] = fmaf(wj, bf_hi(x[q].w), acc[q][7]);
+      }
     }
-    uint4 o;
-    o.x = pack2(acc[0], acc[1]);
-    o.y = pack2(acc[2], acc[3]);
-    o.z = pack2(acc[4], acc[5]);
-    o.w = pack2(acc[6], acc[7]);
-    out[i] = o;
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+      if (v0 + 64 * q < vec) {
+        uint4 o;
+        o.x = pack2(acc[q][0], acc[q][1]);
+        o.y = pack2(acc[q][2], acc[q][3]);
+        o.z = pack2(acc[q][4], acc[q][5]);
+        o.w = pack2(acc[q][6], acc[q][7]);
+        out[t * vec + v0 + 64 * q] = o;
+      }
+    }
   }
 }
 
@@ -53,9 +78,10 @@ __global__ __launch_bounds__(256) void scale_kernel(PlanLayout L, const int32_t*
 
 hipError_t launch_scale(const PlanLayout& L, const int32_t* ws, const uint16_t* recv_self, const float* topk_w,
                         uint16_t* out, hipStream_t s) {
-  const int64_t total = (int64_t)L.T_r * (L.d / 8);
-  if (total == 0) return hipSuccess;
-  int64_t grid = (total + 255) / 256;
+  const int64_t runs = (L.d / 8 + 255) / 256;            // 256-vector runs per row, one wavefront each
+  const int64_t waves = (int64_t)L.T_r * runs;
+  if (waves == 0) return hipSuccess;
+  int64_t grid = (waves + 3) / 4;
   if (grid > 16384) grid = 16384;
   hipLaunchKernelGGL(scale_kernel, dim3((unsigned)grid), dim3(256), 0, s, L, ws, (const uint4*)recv_self, topk_w,
                      (uint4*)out);
