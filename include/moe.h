@@ -17,9 +17,9 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call is asynchronous on it; nothing synchronises with the host
  *     except moe_device_status.
- *   - The caller owns every buffer.  The library allocates no device memory.
- *     Its only state is a per-device cache of two CU-masked streams and a few
- *     events for the overlapped combine (moe_release_streams frees them).
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     creates no streams or events, and keeps only a per-device cache of the
+ *     compute-unit count and LDS limit.
  *   - Errors the device detects (an expert id out of range, a received-row
  *     count that disagrees with the routing, a consumer wait that timed out)
  *     are written to an error word inside the plan workspace and reported by
@@ -77,8 +77,12 @@ typedef struct moe_sizes {
  *   [0] error (moe_status of the last device-detected error, 0 if none)
  *   [1] M  total layout rows          [2] B  bands        [3] remote bands
  *   [4] segments                      [5] remote segments
- *   [6] gate/up tiles                 [7] down tiles      [8] consumer copy units
- *   [9] received rows counted from the routing */
+ *   [6] gate/up tiles                 [7] down tile flags used (B * tiles per band)
+ *   [8] consumer copy units           [9] received rows counted from the routing
+ *   [10] gate/up row tiles            [11] down row tiles
+ *   [12..13] uint64: 100 MHz wall clock when the last producer workgroup of
+ *            the down GEMM ended (raised by every call, never reset)
+ *   [14..15] uint64: the same for the last consumer workgroup */
 typedef struct moe_plan_view {
   size_t hdr;
   size_t c;          /* [E_l][W] rows of local expert e from owner o */
@@ -92,24 +96,30 @@ typedef struct moe_plan_view {
   size_t seg_first, seg_nbands, seg_dst, seg_dst_off, seg_src_row, seg_rows, seg_unit; /* [segments] (+1 for seg_unit) */
   size_t src_index;  /* [rows_cap] received row of each layout row, -1 for padding (first M valid) */
   size_t pos;        /* [T_r][k] row of the rank's own receive buffer holding slot (t, j) */
+  /* GEMM row tiles (implementation detail, for tests): gate/up tiles of 256
+   * rows of one X_e, experts in rule (ii) order; down tiles of up to
+   * 256 / tb_M row-contiguous bands of one expert, in schedule order S
+   * (present when tb_M divides 256; first band and band count per tile) */
+  size_t gu_tile_row, gu_tile_expert;                              /* [hdr[10]] */
+  size_t dn_tile_row, dn_tile_expert, dn_tile_band, dn_tile_nbands; /* [hdr[11]] */
 } moe_plan_view;
 
 /* moe_expert_combine modes */
 enum {
-  MOE_MODE_OVERLAP = 0,   /* down GEMM and consumer run concurrently on disjoint CU sets (§5.3) */
+  MOE_MODE_OVERLAP = 0,   /* down GEMM and consumer run concurrently on disjoint CUs, one launch (§5.3) */
   MOE_MODE_SERIAL = 1,    /* down GEMM to completion, then the consumer on all CUs (serial baseline) */
   MOE_MODE_COPY_ONLY = 2  /* only the consumer, on the caller's stream; flags must already equal `epoch` */
 };
 
 typedef struct moe_combine_opts {
   int32_t mode;             /* MOE_MODE_* */
-  int32_t consumer_cus;     /* OVERLAP: CUs reserved for the consumer, multiple of 8 in [8, 128]; 0 = 32 */
-  int32_t consumer_blocks;  /* workgroups of the consumer; 0 = 2 per reserved CU (OVERLAP) or 1024 */
+  int32_t consumer_cus;     /* OVERLAP: CUs given to the consumer, multiple of 8 in [8, 128]; 0 = 8 */
+  int32_t consumer_blocks;  /* workgroups of the consumer; 0 = consumer_cus (OVERLAP) or 1024 */
   int32_t reserved;
   int64_t spin_timeout_ns;  /* bound on the consumer's wait for one segment's flags; 0 = 2 s */
-  void* events[6];          /* optional hipEvent_t, recorded: [0]/[1] around the gate/up GEMM (caller's
-                               stream), [2]/[3] around the down GEMM, [4]/[5] around the consumer (on the
-                               stream each kernel runs on); NULL entries are skipped */
+  void* events[6];          /* optional hipEvent_t, recorded on `stream`: [0]/[1] around the gate/up GEMM,
+                               [2]/[3] around the down GEMM, [4]/[5] around the consumer (in OVERLAP both
+                               pairs bracket the one launch that runs both); NULL entries are skipped */
 } moe_combine_opts;
 
 /* Text of a status code. */
@@ -152,8 +162,10 @@ int moe_plan(const moe_shape* shape, const int32_t* topk_ids, const uint16_t* x_
  * in schedule order (workgroup i takes tiles i, i+g, ...; §5.1), writes
  * y = h W_down^T (bf16) and, in its epilogue, releases the tile and sets
  * flags[tile] = epoch.  The consumer waits (acquire, bounded) until every
- * tile of a segment is flagged and copies the segment's valid rows to
- * recv[dst] + dst_off*d; padding rows are never copied.
+ * tile of a remote segment is flagged and copies the segment's valid rows to
+ * recv[dst] + dst_off*d; padding rows are never copied.  Rows of local bands
+ * (destination r) never leave the rank: the down GEMM's epilogue writes them
+ * into recv[r] itself, besides y.
  *   x_layout   device bf16 [rows_cap, d] from moe_plan.
  *   w_gate_up  device bf16 [E_l, 2f, d]: rows 0..f-1 gate, f..2f-1 up (K-contiguous).
  *   w_down     device bf16 [E_l, d, f] (K-contiguous).
@@ -162,8 +174,9 @@ int moe_plan(const moe_shape* shape, const int32_t* topk_ids, const uint16_t* x_
  *              pass a new epoch (never 0, increasing) on every call: no reset.
  *   recv       HOST array of W device pointers; recv[o] is bf16 [T_o*k, d].
  *   opts       may be NULL (OVERLAP, defaults).
- * OVERLAP uses two library-owned CU-masked streams at the default priority,
- * ordered after and joined back into `stream` with events.
+ * Every mode runs on `stream` alone.  OVERLAP launches the down GEMM with
+ * consumer_blocks extra workgroups past its producers; they take the last
+ * CUs to be filled and copy while the producers compute.
  */
 int moe_expert_combine(const moe_shape* shape, const void* plan_ws, const uint16_t* x_layout,
                        const uint16_t* w_gate_up, const uint16_t* w_down,
@@ -188,8 +201,6 @@ int moe_device_status(const void* plan_ws, void* stream);
 /* Number of compute units of the current device (0 without a GPU). */
 int moe_device_cus(void);
 
-/* Destroys the cached CU-masked streams and events of the current device. */
-int moe_release_streams(void);
 
 #ifdef __cplusplus
 }

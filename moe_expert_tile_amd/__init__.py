@@ -15,6 +15,7 @@ import ctypes
 import os
 from typing import Dict, List, Optional, Sequence
 
+import numpy as np
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -23,7 +24,8 @@ MOE_OK, MOE_EINVAL, MOE_ECAPACITY, MOE_EHIP, MOE_ETIMEOUT, MOE_EROUTING, MOE_EUN
 MODE_OVERLAP, MODE_SERIAL, MODE_COPY_ONLY = 0, 1, 2
 
 HDR_FIELDS = ["error", "M", "bands", "remote_bands", "segments", "remote_segments",
-              "gateup_tiles", "down_tiles", "copy_units", "received_rows"]
+              "gateup_tiles", "down_tiles", "copy_units", "received_rows", "gateup_row_tiles",
+              "down_row_tiles"]
 
 
 class moe_shape(ctypes.Structure):
@@ -43,7 +45,8 @@ class moe_sizes(ctypes.Structure):
 _VIEW_FIELDS = ["hdr", "c", "grp_off", "m_e", "row_off", "rb", "order", "base",
                 "band_expert", "band_dst", "band_src_row", "band_dst_off", "band_valid",
                 "seg_first", "seg_nbands", "seg_dst", "seg_dst_off", "seg_src_row", "seg_rows",
-                "seg_unit", "src_index", "pos"]
+                "seg_unit", "src_index", "pos",
+                "gu_tile_row", "gu_tile_expert", "dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands"]
 
 
 class moe_plan_view(ctypes.Structure):
@@ -78,7 +81,6 @@ def _load():
         "moe_scale": (I, [P(moe_shape), V, V, V, V, V]),
         "moe_device_status": (I, [V, V]),
         "moe_device_cus": (I, []),
-        "moe_release_streams": (I, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -89,8 +91,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ["moe_status_string", "moe_query_sizes", "moe_plan_offsets", "moe_plan",
-            "moe_expert_combine", "moe_scale", "moe_device_status", "moe_device_cus",
-            "moe_release_streams"]
+            "moe_expert_combine", "moe_scale", "moe_device_status", "moe_device_cus"]
 
 
 def library_path() -> str:
@@ -187,10 +188,6 @@ def moe_device_cus() -> int:
     return int(_lib.moe_device_cus())
 
 
-def moe_release_streams() -> int:
-    return int(_lib.moe_release_streams())
-
-
 def timing_events(n: int = 6) -> List[torch.cuda.Event]:
     """torch events with timing, already created (recorded once) so that their
     raw handles can be recorded by the library."""
@@ -243,6 +240,13 @@ class RankShare:
     def header(self) -> Dict[str, int]:
         h = self.plan_ws[self.offsets["hdr"] // 4: self.offsets["hdr"] // 4 + 16].cpu().tolist()
         return {k: h[i] for i, k in enumerate(HDR_FIELDS)}
+
+    def end_stamps(self):
+        """(last producer end, last consumer end) of the down-GEMM launch, in
+        ticks of the GPU's 100 MHz wall clock (header words 12-15)."""
+        o = self.offsets["hdr"] // 4
+        w = self.plan_ws[o + 12: o + 16].cpu().numpy().astype(np.uint32).astype(np.uint64)
+        return int(w[0] | (w[1] << np.uint64(32))), int(w[2] | (w[3] << np.uint64(32)))
 
     def array(self, name: str, count: int):
         o = self.offsets[name] // 4

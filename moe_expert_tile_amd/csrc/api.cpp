@@ -1,7 +1,6 @@
 // C ABI of libmoe.so (declared in include/moe.h): host-side validation,
 // workspace layout, CU-partitioned streams and launch orchestration.
 #include <hip/hip_runtime.h>
-#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <mutex>
@@ -68,10 +67,16 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->tok_off[W] = tok;
   L->NB = blk;
   L->NB_r = L->blk_off[r + 1] - L->blk_off[r];
+  // down GEMM m-tiles: when tb_M divides 256, 256-row tiles of up to
+  // 256 / tb_M row-contiguous bands (a table the planner builds); otherwise
+  // every band is cut into tb_M / bm sub-tiles of the largest power of two
+  // bm dividing tb_M
   int bm = 256;
   while (tb_m % bm != 0) bm >>= 1;
+  L->dn_merge = (256 % tb_m == 0) ? 256 / tb_m : 0;
+  if (L->dn_merge > 0) bm = 256;
   L->dn_bm = bm;
-  L->dn_sub = tb_m / bm;
+  L->dn_sub = L->dn_merge > 0 ? 1 : tb_m / bm;
   L->dn_ntn = d / kDnBN;
   L->dn_tpb = L->dn_sub * L->dn_ntn;
   L->gu_ntn = f / (kGuBN / 2);
@@ -107,20 +112,18 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->o_baser = take(L->E);
   L->o_gumt_row = take(L->gu_mt_cap);
   L->o_gumt_exp = take(L->gu_mt_cap);
+  L->o_dnt_row = take(B); L->o_dnt_exp = take(B); L->o_dnt_band = take(B); L->o_dnt_nb = take(B);
   L->total_words = off;
   return true;
 }
 
-// --- per-device cache: CU-masked streams and events of the overlapped combine ---
+// --- per-device cache: compute units and LDS limit ---
 namespace {
 
 struct DeviceState {
   bool init = false;
   int cus = 0;
   int lds_per_block = 0;
-  int consumer_cus = -1;
-  hipStream_t prod = nullptr, cons = nullptr;
-  hipEvent_t fork = nullptr, join_p = nullptr, join_c = nullptr;
 };
 constexpr int kMaxDevices = 16;
 DeviceState g_dev[kMaxDevices];
@@ -143,40 +146,6 @@ int device_cus(int dev) {
     st.init = true;
   }
   return st.cus;
-}
-
-// CU mask with `n` bits set out of `total`.  The bit index of a CU interleaves
-// the XCDs (bit i belongs to XCD i mod 8), so the lowest n bits give n/8 CUs
-// on every XCD.
-void fill_mask(uint32_t* mask, int words, int lo_bit, int hi_bit) {
-  for (int i = 0; i < words; ++i) mask[i] = 0;
-  for (int b = lo_bit; b < hi_bit; ++b) mask[b / 32] |= (1u << (b % 32));
-}
-
-int ensure_streams(int dev, int consumer_cus, DeviceState** out) {
-  DeviceState& st = g_dev[dev];
-  const int cus = device_cus(dev);
-  if (cus <= 0) return MOE_EUNSUPPORTED;
-  if (st.prod && st.consumer_cus == consumer_cus) {
-    *out = &st;
-    return MOE_OK;
-  }
-  if (st.prod) { (void)hipStreamDestroy(st.prod); st.prod = nullptr; }
-  if (st.cons) { (void)hipStreamDestroy(st.cons); st.cons = nullptr; }
-  const int words = (cus + 31) / 32;
-  uint32_t mask[64];
-  fill_mask(mask, words, 0, consumer_cus);
-  if (hipExtStreamCreateWithCUMask(&st.cons, words, mask) != hipSuccess) return MOE_EHIP;
-  fill_mask(mask, words, consumer_cus, cus);
-  if (hipExtStreamCreateWithCUMask(&st.prod, words, mask) != hipSuccess) return MOE_EHIP;
-  if (!st.fork) {
-    if (hipEventCreateWithFlags(&st.fork, hipEventDisableTiming) != hipSuccess) return MOE_EHIP;
-    if (hipEventCreateWithFlags(&st.join_p, hipEventDisableTiming) != hipSuccess) return MOE_EHIP;
-    if (hipEventCreateWithFlags(&st.join_c, hipEventDisableTiming) != hipSuccess) return MOE_EHIP;
-  }
-  st.consumer_cus = consumer_cus;
-  *out = &st;
-  return MOE_OK;
 }
 
 int check_gfx950(int dev) {
@@ -256,6 +225,9 @@ int moe_plan_offsets(const moe_shape* s, moe_plan_view* v) {
   v->seg_first = L.o_sfirst * 4; v->seg_nbands = L.o_snb * 4; v->seg_dst = L.o_sdst * 4;
   v->seg_dst_off = L.o_sdoff * 4; v->seg_src_row = L.o_ssrc * 4; v->seg_rows = L.o_srows * 4;
   v->seg_unit = L.o_sunit * 4; v->src_index = L.o_src * 4; v->pos = L.o_pos * 4;
+  v->gu_tile_row = L.o_gumt_row * 4; v->gu_tile_expert = L.o_gumt_exp * 4;
+  v->dn_tile_row = L.o_dnt_row * 4; v->dn_tile_expert = L.o_dnt_exp * 4;
+  v->dn_tile_band = L.o_dnt_band * 4; v->dn_tile_nbands = L.o_dnt_nb * 4;
   return MOE_OK;
 }
 
@@ -293,7 +265,7 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
   if (o.mode < MOE_MODE_OVERLAP || o.mode > MOE_MODE_COPY_ONLY) return MOE_EINVAL;
-  if (o.consumer_cus == 0) o.consumer_cus = 32;
+  if (o.consumer_cus == 0) o.consumer_cus = 8;
   if (o.consumer_cus < 8 || o.consumer_cus > 128 || o.consumer_cus % 8 != 0) return MOE_EINVAL;
   if (o.consumer_blocks < 0 || o.consumer_blocks > 65536) return MOE_EINVAL;
   if (o.spin_timeout_ns < 0) return MOE_EINVAL;
@@ -340,7 +312,7 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   if (rc) return rc;
   if (o.mode == MOE_MODE_SERIAL) {
     record(o.events[2], st);
-    rc = hip_rc(launch_down(L, ws, h, w_down, y, flags, epoch, full_grid, st));
+    rc = hip_rc(launch_down(L, ws_rw, h, w_down, y, flags, epoch, rp, timeout, full_grid, full_grid, st));
     record(o.events[3], st);
     if (rc) return rc;
     record(o.events[4], st);
@@ -349,35 +321,19 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
     record(o.events[5], st);
     return rc;
   }
-  // OVERLAP: down GEMM on the producer CU set, consumer on the reserved set
+  // OVERLAP (§5.3): one launch on the caller's stream; the first n_prod
+  // workgroups run the down GEMM, the last consumer_cus (one per CU, as the
+  // GEMM's LDS footprint leaves room for one workgroup per CU) consume
   if (o.consumer_cus >= cus) return MOE_EINVAL;
-  DeviceState* ds = nullptr;
-  {
-    std::lock_guard<std::mutex> lk(g_mu);
-    rc = ensure_streams(dev, o.consumer_cus, &ds);
-  }
-  if (rc) return rc;
-  if (hipEventRecord(ds->fork, st) != hipSuccess) return MOE_EHIP;
-  if (hipStreamWaitEvent(ds->prod, ds->fork, 0) != hipSuccess) return MOE_EHIP;
-  if (hipStreamWaitEvent(ds->cons, ds->fork, 0) != hipSuccess) return MOE_EHIP;
-  int pgrid = cus - o.consumer_cus;
-  pgrid -= pgrid % 8;
-  // the producer is enqueued first, so a consumer sharing its hardware queue
-  // would simply run after it
-  record(o.events[2], ds->prod);
-  rc = hip_rc(launch_down(L, ws, h, w_down, y, flags, epoch, pgrid, ds->prod));
-  record(o.events[3], ds->prod);
-  if (rc) return rc;
-  record(o.events[4], ds->cons);
-  rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, timeout,
-                              o.consumer_blocks ? o.consumer_blocks : 2 * o.consumer_cus, ds->cons));
-  record(o.events[5], ds->cons);
-  if (rc) return rc;
-  if (hipEventRecord(ds->join_p, ds->prod) != hipSuccess) return MOE_EHIP;
-  if (hipEventRecord(ds->join_c, ds->cons) != hipSuccess) return MOE_EHIP;
-  if (hipStreamWaitEvent(st, ds->join_p, 0) != hipSuccess) return MOE_EHIP;
-  if (hipStreamWaitEvent(st, ds->join_c, 0) != hipSuccess) return MOE_EHIP;
-  return MOE_OK;
+  int n_prod = cus - o.consumer_cus;
+  n_prod -= n_prod % 8;
+  const int n_cons = o.consumer_blocks ? o.consumer_blocks : o.consumer_cus;
+  record(o.events[2], st);
+  record(o.events[4], st);
+  rc = hip_rc(launch_down(L, ws_rw, h, w_down, y, flags, epoch, rp, timeout, n_prod, n_prod + n_cons, st));
+  record(o.events[3], st);
+  record(o.events[5], st);
+  return rc;
 }
 
 int moe_scale(const moe_shape* s, const void* plan_ws, const uint16_t* recv_self, const float* topk_w, uint16_t* out,
@@ -412,22 +368,6 @@ int moe_device_cus(void) {
   int dev;
   if (prepare(&dev) != MOE_OK) return 0;
   return g_dev[dev].cus;
-}
-
-int moe_release_streams(void) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  int dev;
-  if (current_device(&dev) != MOE_OK) return MOE_EUNSUPPORTED;
-  DeviceState& st = g_dev[dev];
-  if (st.prod) (void)hipStreamDestroy(st.prod);
-  if (st.cons) (void)hipStreamDestroy(st.cons);
-  if (st.fork) (void)hipEventDestroy(st.fork);
-  if (st.join_p) (void)hipEventDestroy(st.join_p);
-  if (st.join_c) (void)hipEventDestroy(st.join_c);
-  st.prod = st.cons = nullptr;
-  st.fork = st.join_p = st.join_c = nullptr;
-  st.consumer_cus = -1;
-  return MOE_OK;
 }
 
 }  // extern "C"

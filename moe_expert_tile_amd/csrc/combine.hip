@@ -1,122 +1,29 @@
-// Consumer: the second all-to-all of the tile-signal notes ("MoE 计算-通信细粒度重叠：
-// 用 Tile 级信号把 All-to-All 藏在 GEMM 背后"), §3 Stage B, §5.2 and §5.3.  A
-// persistent kernel, on its own CU set in the overlapped mode, waits for the
-// tile flags of each segment in schedule order and then copies the segment's
-// valid rows — contiguous in the layout and contiguous at the destination —
-// into the owner's receive buffer.  The W owners are W buffers in HBM; the
-// pages' one-sided remote put becomes a device-memory copy.
-//
-// Memory ordering: the producer stores a tile, releases at agent scope and
-// sets flags[tile] = epoch with an agent-scope store.  Here wave 0 polls the
-// flags with agent-scope loads; every later read of the tile also uses
-// agent-scope loads (they bypass the non-coherent caches of this XCD), so no
-// cache-wide invalidation is issued and the producer's L2 contents on the
-// same XCD survive.
-//
-// Work split: each segment is cut into units of kCopyChunk bytes; unit u goes
-// to workgroup u mod G, units in schedule order.  A workgroup waits for a
-// segment once, on its first unit of that segment.  The wait is bounded: after
-// `timeout` ticks of the 100 MHz constant clock it records MOE_ETIMEOUT in the
-// plan's error word and every workgroup leaves.
-#include "moe_internal.h"
+// Standalone consumer kernel (tile-signal notes, "MoE 计算-通信细粒度重叠：用 Tile 级信号
+// 把 All-to-All 藏在 GEMM 背后", §5.2 and §5.3): the consumer body of consume.h on
+// its own grid, after the down GEMM (serial mode) or with the flags already
+// set (copy-only mode).  The overlapped mode runs the same body inside the
+// down-GEMM launch instead.
+#include "consume.h"
 
 namespace moe {
 namespace {
 
-__device__ __forceinline__ uint64_t agent_load64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+constexpr int kConsumerThreads = 256;
 
-__global__ __launch_bounds__(256) void consumer_kernel(PlanLayout L, int32_t* __restrict__ ws,
-                                                      const uint16_t* __restrict__ y,
-                                                      const uint32_t* __restrict__ flags, uint32_t epoch,
-                                                      RecvPtrs recv, int64_t timeout) {
+__global__ __launch_bounds__(kConsumerThreads) void consumer_kernel(PlanLayout L, int32_t* __restrict__ ws,
+                                                                   const uint16_t* __restrict__ y,
+                                                                   const uint32_t* __restrict__ flags, uint32_t epoch,
+                                                                   RecvPtrs recv, int64_t timeout) {
   __shared__ int s_go;
-  int32_t* hdr = ws + L.o_hdr;
-  if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
-  const int U = hdr[H_UNITS];
-  const int32_t* sfirst = ws + L.o_sfirst;
-  const int32_t* snb = ws + L.o_snb;
-  const int32_t* sdst = ws + L.o_sdst;
-  const int32_t* sdoff = ws + L.o_sdoff;
-  const int32_t* ssrc = ws + L.o_ssrc;
-  const int32_t* srows = ws + L.o_srows;
-  const int32_t* sunit = ws + L.o_sunit;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int64_t d = L.d;
-  const int tpb = L.dn_tpb;
-  int seg = 0, ready = -1;
-  for (int u = blockIdx.x; u < U; u += gridDim.x) {
-    while (sunit[seg + 1] <= u) ++seg;
-    if (seg != ready) {
-      if (tid < 64) {
-        const int f0 = sfirst[seg] * tpb, f1 = (sfirst[seg] + snb[seg]) * tpb;
-        const uint64_t t0 = wall_clock64();
-        int go = 1;
-        for (;;) {
-          bool ok = true;
-          for (int i = f0 + lane; i < f1; i += 64)
-            ok &= (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch);
-          if (__ballot(!ok) == 0) break;
-          if ((int64_t)(wall_clock64() - t0) > timeout) {
-            if (lane == 0)
-              __hip_atomic_store(hdr + H_ERROR, 4 /* MOE_ETIMEOUT */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            go = 0;
-            break;
-          }
-          if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-            go = 0;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-        if (lane == 0) s_go = go;
-      }
-      __syncthreads();
-      const int go = s_go;
-      __syncthreads();
-      if (!go) return;
-      ready = seg;
-    }
-    const int64_t bytes = (int64_t)srows[seg] * d * 2;
-    const int64_t lo = (int64_t)(u - sunit[seg]) * kCopyChunk;
-    const int64_t hi = min(lo + (int64_t)kCopyChunk, bytes);
-    const uint64_t* src = (const uint64_t*)(y + (int64_t)ssrc[seg] * d);
-    uint4* dst = (uint4*)(recv.p[sdst[seg]] + (int64_t)sdoff[seg] * d);
-    // 4 vectors of 16 bytes per thread per pass, all loads issued before the stores
-    constexpr int V = 4;
-    for (int64_t off = lo + tid * 16; off < hi; off += 256 * 16 * V) {
-      uint64_t a[V], b[V];
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const int64_t o = off + (int64_t)i * 256 * 16;
-        if (o < hi) {
-          a[i] = agent_load64(src + o / 8);
-          b[i] = agent_load64(src + o / 8 + 1);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const int64_t o = off + (int64_t)i * 256 * 16;
-        if (o < hi) {
-          uint4 v;
-          v.x = (uint32_t)a[i];
-          v.y = (uint32_t)(a[i] >> 32);
-          v.z = (uint32_t)b[i];
-          v.w = (uint32_t)(b[i] >> 32);
-          dst[o / 16] = v;
-        }
-      }
-    }
-  }
+  consume_segments<kConsumerThreads>(L, ws, y, flags, epoch, recv, timeout, blockIdx.x, gridDim.x, &s_go);
 }
 
 }  // namespace
 
 hipError_t launch_consumer(const PlanLayout& L, int32_t* ws, const uint16_t* y, const uint32_t* flags,
-                           uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks, int grid,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(consumer_kernel, dim3(grid), dim3(256), 0, s, L, ws, y, flags, epoch, recv, timeout_ticks);
+                           uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(consumer_kernel, dim3(grid), dim3(kConsumerThreads), 0, s, L, ws, y, flags, epoch, recv,
+                     timeout_ticks);
   return hipGetLastError();
 }
 

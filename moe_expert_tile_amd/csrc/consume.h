@@ -1,0 +1,124 @@
+// Consumer body: the second all-to-all of the tile-signal notes ("MoE 计算-通信
+// 细粒度重叠：用 Tile 级信号把 All-to-All 藏在 GEMM 背后"), §3 Stage B, §5.2 and §5.3.
+// Shared by the standalone consumer kernel and by the consumer workgroups of
+// the overlapped down-GEMM launch.
+//
+// The remote segments are walked in schedule order: each waits until every
+// tile flag of its bands equals this call's epoch, then its valid rows --
+// contiguous in the layout and contiguous at the destination -- are copied
+// into the owner's receive buffer.  The W owners are W buffers in HBM; the
+// pages' one-sided remote put becomes a device-memory copy.  Local segments
+// are not copied here: their rows never leave the rank, and the down GEMM's
+// epilogue writes them straight into the rank's own receive buffer.
+//
+// Memory ordering: the producer stores a tile, releases at agent scope and
+// sets flags[tile] = epoch with an agent-scope store.  Here wave 0 polls the
+// flags with agent-scope loads; every later read of the tile also uses
+// agent-scope loads (they bypass the non-coherent caches of this XCD), so no
+// cache-wide invalidation is issued and the producer's L2 contents on the
+// same XCD survive.
+//
+// Work split: each segment is cut into units of kCopyChunk bytes; unit u goes
+// to consumer workgroup u mod n_cons, units in schedule order.  A workgroup
+// waits for a segment once, on its first unit of that segment.  The wait is
+// bounded: after `timeout` ticks of the 100 MHz constant clock it records
+// MOE_ETIMEOUT in the plan's error word and every consumer workgroup leaves.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+__device__ __forceinline__ uint64_t agent_load64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One consumer workgroup of NT threads; `cid` in [0, n_cons).  `s_go` is one
+// int of the caller's LDS (the caller's only LDS object, so that the
+// compiler's LDS-DMA wait tracking in the GEMM stays exact).
+template <int NT>
+__device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_t* __restrict__ y,
+                                 const uint32_t* __restrict__ flags, uint32_t epoch, const RecvPtrs& recv,
+                                 int64_t timeout, int cid, int n_cons, int* s_go) {
+  int32_t* hdr = ws + L.o_hdr;
+  if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
+  const int32_t* sfirst = ws + L.o_sfirst;
+  const int32_t* snb = ws + L.o_snb;
+  const int32_t* sdst = ws + L.o_sdst;
+  const int32_t* sdoff = ws + L.o_sdoff;
+  const int32_t* ssrc = ws + L.o_ssrc;
+  const int32_t* srows = ws + L.o_srows;
+  const int32_t* sunit = ws + L.o_sunit;
+  // remote segments come first in schedule order; their units end where the
+  // first local segment's begin
+  const int U = sunit[hdr[H_RSEGS]];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t d = L.d;
+  const int tpb = L.dn_tpb;
+  int seg = 0, ready = -1;
+  for (int u = cid; u < U; u += n_cons) {
+    while (sunit[seg + 1] <= u) ++seg;
+    if (seg != ready) {
+      if (tid < 64) {
+        const int f0 = sfirst[seg] * tpb, f1 = (sfirst[seg] + snb[seg]) * tpb;
+        const uint64_t t0 = wall_clock64();
+        int go = 1;
+        for (;;) {
+          bool ok = true;
+          for (int i = f0 + lane; i < f1; i += 64)
+            ok &= (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch);
+          if (__ballot(!ok) == 0) break;
+          if ((int64_t)(wall_clock64() - t0) > timeout) {
+            if (lane == 0)
+              __hip_atomic_store(hdr + H_ERROR, 4 /* MOE_ETIMEOUT */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            go = 0;
+            break;
+          }
+          if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+            go = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane == 0) *s_go = go;
+      }
+      __syncthreads();
+      const int go = *s_go;
+      __syncthreads();
+      if (!go) return;
+      ready = seg;
+    }
+    const int64_t bytes = (int64_t)srows[seg] * d * 2;
+    const int64_t lo = (int64_t)(u - sunit[seg]) * kCopyChunk;
+    const int64_t hi = min(lo + (int64_t)kCopyChunk, bytes);
+    const uint64_t* src = (const uint64_t*)(y + (int64_t)ssrc[seg] * d);
+    uint4* dst = (uint4*)(recv.p[sdst[seg]] + (int64_t)sdoff[seg] * d);
+    // V vectors of 16 bytes per thread per pass, all loads issued before the stores
+    constexpr int V = 4;
+    for (int64_t off = lo + tid * 16; off < hi; off += (int64_t)NT * 16 * V) {
+      uint64_t a[V], b[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int64_t o = off + (int64_t)i * NT * 16;
+        if (o < hi) {
+          a[i] = agent_load64(src + o / 8);
+          b[i] = agent_load64(src + o / 8 + 1);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int64_t o = off + (int64_t)i * NT * 16;
+        if (o < hi) {
+          uint4 v;
+          v.x = (uint32_t)a[i];
+          v.y = (uint32_t)(a[i] >> 32);
+          v.z = (uint32_t)b[i];
+          v.w = (uint32_t)(b[i] >> 32);
+          dst[o / 16] = v;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace moe

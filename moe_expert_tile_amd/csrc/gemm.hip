@@ -14,7 +14,7 @@
 //     with 4 consecutive output columns per accumulator quad: 8-byte bf16
 //     stores, and the SwiGLU gate/up pair of a column sits in one lane.
 //   * K steps of 64: both operands are K-contiguous in HBM, copied straight
-//     into LDS with 16-byte global_load_lds (no staging registers), two LDS
+//     into LDS with 16-byte buffer loads (no staging registers), two LDS
 //     stages, 16-byte chunks XOR-swizzled by (row mod 8) so that the
 //     ds_read_b128 operand fetches are bank-conflict free.
 //   * Persistent grid (a multiple of 8 workgroups).  Workgroup w runs on XCD
@@ -22,7 +22,9 @@
 //     tiles, so each XCD works on a contiguous run of the tile order, and the
 //     tile order groups GM row tiles per column sweep so the run shares
 //     operand rows in that XCD's L2.
-#include "moe_internal.h"
+#include <type_traits>
+
+#include "consume.h"
 
 namespace moe {
 namespace {
@@ -42,16 +44,22 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #define MOE_GU_WAVES_N 2
 #endif
 #ifndef MOE_DN_WAVES_M
-#define MOE_DN_WAVES_M 4
+#define MOE_DN_WAVES_M 2
 #endif
 #ifndef MOE_DN_WAVES_N
-#define MOE_DN_WAVES_N 2
+#define MOE_DN_WAVES_N 4
 #endif
-#ifndef MOE_BK
-#define MOE_BK 64
+#ifndef MOE_GU_BK
+#define MOE_GU_BK 64
 #endif
-#ifndef MOE_STAGES
-#define MOE_STAGES 2
+#ifndef MOE_GU_STAGES
+#define MOE_GU_STAGES 2
+#endif
+#ifndef MOE_DN_BK
+#define MOE_DN_BK 64
+#endif
+#ifndef MOE_DN_STAGES
+#define MOE_DN_STAGES 2
 #endif
 constexpr int kGroupM = MOE_GROUP_M;   // row tiles per column sweep
 
@@ -85,13 +93,13 @@ struct Cfg {
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "every wavefront loads both operands");
   static_assert(BM % (RPB * NW) == 0 && BN % (RPB * NW) == 0, "whole wave loads");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+  static_assert(STAGES >= 2 && STAGES <= 6, "ring depth");
   static_assert(LPW * (STAGES - 2) <= 63, "vmcnt range");
   __device__ static int swz(int row, int c) { return c ^ ((row / R256) % CPR); }
 };
 
 struct GemmArgs {
-  const int32_t* ws;
+  int32_t* ws;
   const uint16_t* a;      // activations [rows, K]
   const uint16_t* w;      // weights [E_l, N_total, K]
   uint16_t* out;          // [rows, out_cols]
@@ -101,7 +109,14 @@ struct GemmArgs {
   int out_cols;           // columns of `out`
   int w_rows;             // rows of one expert's weight matrix
   int half;               // SWIGLU: f (offset of the up rows); else 0
+  int n_prod;             // producer workgroups (the rest of the grid consumes)
+  int64_t timeout;        // consumer wait bound, 100 MHz ticks
 };
+
+__device__ __forceinline__ void stamp_max(int32_t* hdr, int word) {
+  __hip_atomic_fetch_max((uint64_t*)(hdr + word), (uint64_t)wall_clock64(), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -109,14 +124,22 @@ __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" :
 // `stages_in_flight` later stages of its own global->LDS loads are
 // outstanding (so the current stage has landed) and its LDS reads are done,
 // then all wavefronts meet.  __syncthreads() would also wait for every
-// outstanding load (vmcnt(0)) and so drain the prefetch ring.
+// outstanding load (vmcnt(0)) and so drain the prefetch ring.  Written with
+// the waitcnt builtin (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8) rather than inline assembly, so the compiler's own
+// counter tracking sees the wait and keeps its later LDS waits partial.
+__host__ __device__ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4); }
+
 template <int LPW>
 __device__ __forceinline__ void stage_barrier(int stages_in_flight) {
   switch (stages_in_flight) {
-    case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPW) : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LPW) : "memory"); break;
+    case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LPW)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LPW)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * LPW)); break;
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4 * LPW)); break;
   }
+  __builtin_amdgcn_s_barrier();
 }
 
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
@@ -143,36 +166,58 @@ __device__ __forceinline__ float silu_f(float g) {
   return g / (1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
 }
 
+// Buffer resource word 3 for untyped (raw) buffer access on gfx9-family
+// chips: data format 32, every other field zero.
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kBufWord3);
+}
+
 template <class C>
-__device__ __forceinline__ void issue_stage(lds_void_t* lds_stage, const char* a_base, const uint32_t (&a_off)[C::A_LOADS],
-                                            const char* b_base, const uint32_t (&b_off)[C::B_LOADS], int k0,
-                                            int wave) {
+__device__ __forceinline__ void issue_stage(lds_void_t* lds_stage, __amdgpu_buffer_rsrc_t ra,
+                                            const uint32_t (&a_off)[C::A_LOADS], __amdgpu_buffer_rsrc_t rb,
+                                            const uint32_t (&b_off)[C::B_LOADS], int k0, int wave) {
   // wave `wave` fills LDS rows [RPB q, RPB (q+1)) for q = wave, wave + NW, ...;
-  // the lane byte offsets (from wave-uniform bases) carry the swizzled chunk
+  // the lane byte offsets (from wave-uniform bases) carry the swizzled chunk,
+  // the K offset goes in the scalar offset.  MUBUF loads with the LDS bit
+  // count only in vmcnt, so the LDS-read waits around them stay partial.
   char* base = (char*)lds_stage;
-  const char* a = a_base + 2 * k0;
-  const char* b = b_base + 2 * k0;
+  const int koff = 2 * k0;
 #pragma unroll
   for (int i = 0; i < C::A_LOADS; ++i) {
     const int q = wave + i * C::NW;
-    __builtin_amdgcn_global_load_lds((const void*)(a + a_off[i]), (lds_void_t*)(base + q * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(base + q * 1024), 16, (int)a_off[i], koff, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < C::B_LOADS; ++i) {
     const int q = wave + i * C::NW;
-    __builtin_amdgcn_global_load_lds((const void*)(b + b_off[i]), (lds_void_t*)(base + C::A_ELEMS * 2 + q * 1024),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(base + C::A_ELEMS * 2 + q * 1024), 16, (int)b_off[i],
+                                             koff, 0, 0);
   }
 }
 
 template <class C, bool SWIGLU, bool FLAGS>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
-void grouped_gemm_kernel(PlanLayout L, GemmArgs g) {
+void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::STAGES * C::STAGE_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int WAVES_N = C::BN / C::WN;
   const int wave_m = wave / WAVES_N, wave_n = wave % WAVES_N;
-  const int32_t* hdr = g.ws + L.o_hdr;
+  int32_t* hdr = g.ws + L.o_hdr;
+  if constexpr (FLAGS) {
+    // overlapped combine (§5.3): the workgroups past the producers are the
+    // consumer.  They are dispatched after every producer of their XCD and
+    // hold the GEMM's LDS footprint, so each has a CU of its own; producers
+    // never wait for them.
+    if ((int)blockIdx.x >= g.n_prod) {
+      consume_segments<C::NT>(L, g.ws, g.out, g.flags, g.epoch, recv, g.timeout, blockIdx.x - g.n_prod,
+                              gridDim.x - g.n_prod, (int*)lds);
+      if (tid == 0) stamp_max(hdr, H_T_CONS_END);
+      return;
+    }
+  }
   if (hdr[H_ERROR] != 0) return;
 
   int n_mt, n_nt;
@@ -180,11 +225,11 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g) {
     n_mt = hdr[H_GU_MT];
     n_nt = L.gu_ntn;
   } else {
-    n_mt = hdr[H_BANDS] * L.dn_sub;
+    n_mt = hdr[H_DN_MT];
     n_nt = L.dn_ntn;
   }
   const int total = n_mt * n_nt;
-  const int G = gridDim.x;
+  const int G = g.n_prod;   // a multiple of 8
   const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int KT = g.K / C::BK;
   const int32_t* rowoff = g.ws + L.o_rowoff;
@@ -213,24 +258,55 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g) {
   for (int t = slot; t < total; t += G) {
     int mt, nt;
     decode_tile(t, n_mt, n_nt, mt, nt);
-    int e, row0;
+    // row tile: its expert, first row and row limit; for the down GEMM also
+    // the first band and the number of bands whose flags it sets
+    int e, row0, lim, band0 = 0, nbt = 1;
     if constexpr (SWIGLU) {
       row0 = g.ws[L.o_gumt_row + mt];
       e = g.ws[L.o_gumt_exp + mt];
+      lim = rowoff[e + 1];
+    } else if (L.dn_merge > 0) {
+      // up to dn_merge row-contiguous bands of one expert
+      row0 = g.ws[L.o_dnt_row + mt];
+      e = g.ws[L.o_dnt_exp + mt];
+      band0 = g.ws[L.o_dnt_band + mt];
+      nbt = g.ws[L.o_dnt_nb + mt];
+      lim = min(rowoff[e + 1], row0 + nbt * L.tb_m);
     } else {
+      // sub-tile mt % dn_sub of band mt / dn_sub
       const int band = mt / L.dn_sub;
       e = g.ws[L.o_bexp + band];
       row0 = g.ws[L.o_bsrc + band] + (mt - band * L.dn_sub) * C::BM;
+      lim = rowoff[e + 1];
     }
-    const int row_end = rowoff[e + 1];
+    // per-tile values are wave-uniform; say so, so that the buffer
+    // descriptors built from them live in scalar registers
+    e = __builtin_amdgcn_readfirstlane(e);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    band0 = __builtin_amdgcn_readfirstlane(band0);
+    nbt = __builtin_amdgcn_readfirstlane(nbt);
+    const int row_end = __builtin_amdgcn_readfirstlane(lim);
+    // local bands (destination r) never leave the rank: the epilogue also
+    // writes their rows into r's own receive buffer at the combine plan's
+    // destination rows, so the consumer moves only remote segments
+    int ldst0 = -1;
+    if constexpr (FLAGS) {
+      const int bfirst = L.dn_merge > 0 ? band0 : mt / L.dn_sub;
+      if (g.ws[L.o_bdst + bfirst] == L.r)
+        ldst0 = g.ws[L.o_bdoff + bfirst] + (L.dn_merge > 0 ? 0 : (mt - bfirst * L.dn_sub) * C::BM);
+      ldst0 = __builtin_amdgcn_readfirstlane(ldst0);
+    }
     // a sub-tile of a partial (local tail) band can start past the expert's
     // last row: nothing to compute or store, only its flag to publish
     const bool empty = row0 >= row_end;
     // wave-uniform base row (clamped into the expert) + 32-bit lane byte
     // offsets, never negative (rows < 2^16 apart, K < 2^16)
     const int rbase = min(row0, row_end - 1);
-    const char* a_base = (const char*)(g.a + (int64_t)rbase * g.K);
-    const char* b_base = (const char*)(g.w + (int64_t)e * g.w_rows * g.K);
+    // buffer descriptors: A from the clamped base row to the expert's last
+    // row, B over the expert's weight matrix (loads never leave them)
+    const __amdgpu_buffer_rsrc_t a_rsrc =
+        make_rsrc(g.a + (int64_t)rbase * g.K, (int64_t)(row_end - rbase) * g.K * 2);
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(g.w + (int64_t)e * g.w_rows * g.K, (int64_t)g.w_rows * g.K * 2);
     uint32_t a_off[C::A_LOADS];
     uint32_t b_off[C::B_LOADS];
 #pragma unroll
@@ -268,43 +344,56 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g) {
 #pragma unroll
     for (int s = 0; s < C::STAGES - 1; ++s)
       if (s < KTt)
-        issue_stage<C>((lds_void_t*)(lds + s * C::STAGE_ELEMS), a_base, a_off, b_base, b_off, s * C::BK, wave);
+        issue_stage<C>((lds_void_t*)(lds + s * C::STAGE_ELEMS), a_rsrc, a_off, b_rsrc, b_off, s * C::BK, wave);
 
-    for (int kt = 0; kt < KTt; ++kt) {
-      // stage kt has landed once at most min(STAGES-2, KT-1-kt) later stages
-      // of this wave are still in flight; the barrier makes it true for all
-      // waves and also retires every read of the buffer refilled next
-      stage_barrier<C::LPW>(min(C::STAGES - 2, KT - 1 - kt));
+    // One K step.  Stage kt has landed once at most `in_flight` later stages
+    // of this wave are still in flight; the barrier makes it true for all
+    // waves and also retires every read of the buffer refilled next.
+    // Operand fragments run one 16-wide k-substep ahead of the MFMAs (two
+    // register sets), so at most 2 (FN + FM) LDS reads are outstanding and
+    // each substep waits only for its own fragments; the next stage's
+    // global->LDS loads go out after the first substep's reads.  The
+    // steady-state steps always refill (ISSUE) and the last STAGES-1 never
+    // do, so each step body is one branch-free scheduling region.
+    auto k_step = [&](int kt, auto issue_tag, int in_flight) {
+      constexpr bool ISSUE = decltype(issue_tag)::value;
+      stage_barrier<C::LPW>(in_flight);
       const uint16_t* sa = lds + (kt % C::STAGES) * C::STAGE_ELEMS;
       const uint16_t* sb = sa + C::A_ELEMS;
-      // all fragments of the stage first, the next stage's loads in between,
-      // then the MFMAs (the first ones wait only for the first fragments)
-      bf16x8 pw[C::KK][C::FN], px[C::KK][C::FM];
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
+      bf16x8 pw[2][C::FN], px[2][C::FM];
+      auto read_frags = [&](int kk, int slot) {
         const int phys = ((2 * kk + lhalf) ^ rsw) * 8;
 #pragma unroll
         for (int i = 0; i < C::FN; ++i)
-          pw[kk][i] = *(const bf16x8*)(sb + (prow[i] + lrow) * C::BK + phys);
+          pw[slot][i] = *(const bf16x8*)(sb + (prow[i] + lrow) * C::BK + phys);
 #pragma unroll
         for (int j = 0; j < C::FM; ++j)
-          px[kk][j] = *(const bf16x8*)(sa + (wave_m * C::WM + 32 * j + lrow) * C::BK + phys);
-        if (kk == 0 && kt + C::STAGES - 1 < KT)
-          issue_stage<C>((lds_void_t*)(lds + ((kt + C::STAGES - 1) % C::STAGES) * C::STAGE_ELEMS), a_base, a_off,
-                         b_base, b_off, (kt + C::STAGES - 1) * C::BK, wave);
-      }
+          px[slot][j] = *(const bf16x8*)(sa + (wave_m * C::WM + 32 * j + lrow) * C::BK + phys);
+      };
+      read_frags(0, 0);
+      if constexpr (ISSUE)
+        issue_stage<C>((lds_void_t*)(lds + ((kt + C::STAGES - 1) % C::STAGES) * C::STAGE_ELEMS), a_rsrc, a_off,
+                       b_rsrc, b_off, (kt + C::STAGES - 1) * C::BK, wave);
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk)
+      for (int kk = 0; kk < C::KK; ++kk) {
+        if (kk + 1 < C::KK) read_frags(kk + 1, (kk + 1) & 1);
 #pragma unroll
         for (int i = 0; i < C::FN; ++i)
 #pragma unroll
           for (int j = 0; j < C::FM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pw[kk][i], px[kk][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pw[kk & 1][i], px[kk & 1][j], acc[i][j], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::FN + C::FM, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedVmem, C::LPW, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, (C::KK - 1) * (C::FN + C::FM), 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, C::KK * C::FN * C::FM, 0);
-    }
+      if constexpr (ISSUE) __builtin_amdgcn_sched_group_barrier(kSchedVmem, C::LPW, 0);
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) {
+        if (kk + 1 < C::KK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::FN + C::FM, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, C::FN * C::FM, 0);
+      }
+    };
+    int kt = 0;
+    for (; kt + C::STAGES - 1 < KTt; ++kt) k_step(kt, std::integral_constant<bool, true>{}, C::STAGES - 2);
+    for (; kt < KTt; ++kt) k_step(kt, std::integral_constant<bool, false>{}, min(C::STAGES - 2, KTt - 1 - kt));
 
     // epilogue: lane holds rows m = .. + (lane & 31), columns n = .. + 8*(v/4) + 4*(lane/32) + v%4
     const int mrow0 = row0 + wave_m * C::WM + lrow;
@@ -342,6 +431,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g) {
         const int m = mrow0 + 32 * j;
         if (m < row_end) {
           uint16_t* orow = g.out + (int64_t)m * g.out_cols;
+          uint16_t* lrow = recv.p[L.r] + (int64_t)(ldst0 + (m - row0)) * g.out_cols;
 #pragma unroll
           for (int i = 0; i < C::FN; ++i)
 #pragma unroll
@@ -350,6 +440,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g) {
               pk.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
               pk.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
               *(uint2*)(orow + ncol0 + 32 * i + 8 * q) = pk;
+              if (ldst0 >= 0) *(uint2*)(lrow + ncol0 + 32 * i + 8 * q) = pk;
             }
         }
       }
@@ -360,17 +451,31 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g) {
         __syncthreads();
         if (tid == 0) {
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-          __hip_atomic_store(g.flags + (int64_t)mt * n_nt + nt, g.epoch, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+          if (L.dn_merge > 0) {
+            // one flag per covered band (a band has n_nt flags, one per column tile)
+            for (int b = 0; b < nbt; ++b)
+              __hip_atomic_store(g.flags + (int64_t)(band0 + b) * n_nt + nt, g.epoch, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            __hip_atomic_store(g.flags + (int64_t)mt * n_nt + nt, g.epoch, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
       }
     }
   }
+  if constexpr (FLAGS) {
+    if (tid == 0) stamp_max(hdr, H_T_PROD_END);
+  }
 }
 
-using GuCfg = Cfg<256, 256, MOE_GU_WAVES_M, MOE_GU_WAVES_N, MOE_BK, MOE_STAGES>;
-using Dn256 = Cfg<256, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_BK, MOE_STAGES>;
-using Dn128 = Cfg<128, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_BK, MOE_STAGES>;
+// ring depth: the requested number of stages, at most what fits in LDS
+constexpr int fit_stages(int bm, int bn, int bk, int stages) {
+  return stages * (bm + bn) * bk * 2 <= 160 * 1024 ? stages : (160 * 1024) / ((bm + bn) * bk * 2);
+}
+using GuCfg = Cfg<256, 256, MOE_GU_WAVES_M, MOE_GU_WAVES_N, MOE_GU_BK, fit_stages(256, 256, MOE_GU_BK, MOE_GU_STAGES)>;
+using Dn256 = Cfg<256, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_DN_BK, fit_stages(256, 256, MOE_DN_BK, MOE_DN_STAGES)>;
+using Dn128 = Cfg<128, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_DN_BK, fit_stages(128, 256, MOE_DN_BK, MOE_DN_STAGES)>;
 using Dn64 = Cfg<64, 256, 1, 4, 32, 4>;
 using Dn32 = Cfg<32, 256, 1, 4, 64, 3>;
 
@@ -378,19 +483,29 @@ using Dn32 = Cfg<32, 256, 1, 4, 64, 3>;
 
 hipError_t launch_gateup(const PlanLayout& L, const int32_t* ws, const uint16_t* x, const uint16_t* wgu,
                          uint16_t* h, int grid, hipStream_t s) {
-  GemmArgs a{ws, x, wgu, h, nullptr, 0u, L.d, L.f, 2 * L.f, L.f};
-  hipLaunchKernelGGL((grouped_gemm_kernel<GuCfg, true, false>), dim3(grid), dim3(GuCfg::NT), 0, s, L, a);
+  GemmArgs a{const_cast<int32_t*>(ws), x, wgu, h, nullptr, 0u, L.d, L.f, 2 * L.f, L.f, grid, 0};
+  RecvPtrs none{};
+  hipLaunchKernelGGL((grouped_gemm_kernel<GuCfg, true, false>), dim3(grid), dim3(GuCfg::NT), 0, s, L, a, none);
   return hipGetLastError();
 }
 
-hipError_t launch_down(const PlanLayout& L, const int32_t* ws, const uint16_t* h, const uint16_t* wd,
-                       uint16_t* y, uint32_t* flags, uint32_t epoch, int grid, hipStream_t s) {
-  GemmArgs a{ws, h, wd, y, flags, epoch, L.f, L.d, L.d, 0};
+hipError_t launch_down(const PlanLayout& L, int32_t* ws, const uint16_t* h, const uint16_t* wd, uint16_t* y,
+                       uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks, int n_prod,
+                       int grid, hipStream_t s) {
+  GemmArgs a{ws, h, wd, y, flags, epoch, L.f, L.d, L.d, 0, n_prod, timeout_ticks};
   switch (L.dn_bm) {
-    case 256: hipLaunchKernelGGL((grouped_gemm_kernel<Dn256, false, true>), dim3(grid), dim3(Dn256::NT), 0, s, L, a); break;
-    case 128: hipLaunchKernelGGL((grouped_gemm_kernel<Dn128, false, true>), dim3(grid), dim3(Dn128::NT), 0, s, L, a); break;
-    case 64: hipLaunchKernelGGL((grouped_gemm_kernel<Dn64, false, true>), dim3(grid), dim3(Dn64::NT), 0, s, L, a); break;
-    default: hipLaunchKernelGGL((grouped_gemm_kernel<Dn32, false, true>), dim3(grid), dim3(Dn32::NT), 0, s, L, a); break;
+    case 256:
+      hipLaunchKernelGGL((grouped_gemm_kernel<Dn256, false, true>), dim3(grid), dim3(Dn256::NT), 0, s, L, a, recv);
+      break;
+    case 128:
+      hipLaunchKernelGGL((grouped_gemm_kernel<Dn128, false, true>), dim3(grid), dim3(Dn128::NT), 0, s, L, a, recv);
+      break;
+    case 64:
+      hipLaunchKernelGGL((grouped_gemm_kernel<Dn64, false, true>), dim3(grid), dim3(Dn64::NT), 0, s, L, a, recv);
+      break;
+    default:
+      hipLaunchKernelGGL((grouped_gemm_kernel<Dn32, false, true>), dim3(grid), dim3(Dn32::NT), 0, s, L, a, recv);
+      break;
   }
   return hipGetLastError();
 }

@@ -19,7 +19,11 @@ constexpr int kDnBN = 256;             // down GEMM tile cols
 // header words of the plan workspace (mirrors the public description)
 enum Hdr {
   H_ERROR = 0, H_M = 1, H_BANDS = 2, H_REMOTE = 3, H_SEGS = 4, H_RSEGS = 5,
-  H_GU_TILES = 6, H_DN_TILES = 7, H_UNITS = 8, H_RCOUNT = 9, H_GU_MT = 10,
+  H_GU_TILES = 6, H_DN_TILES = 7, H_UNITS = 8, H_RCOUNT = 9, H_GU_MT = 10, H_DN_MT = 11,
+  // uint64 wall-clock stamps (100 MHz) raised by every producer / consumer
+  // workgroup of the down-GEMM launch as it ends (atomic max, so no reset is
+  // needed between calls): words 12-13 and 14-15
+  H_T_PROD_END = 12, H_T_CONS_END = 14,
   H_WORDS = 64
 };
 
@@ -29,6 +33,7 @@ struct PlanLayout {
   int W, r, E_l, E, k, d, f, tb_m, mgb;
   int R, rows_cap, bands_cap, T_r, NB, NB_r, gu_mt_cap;
   int dn_bm, dn_sub, dn_ntn, dn_tpb;   // down GEMM: tile rows, tiles per band row, n tiles, tiles per band
+  int dn_merge;                        // > 0: down m-tiles of up to dn_merge row-contiguous bands (table)
   int gu_ntn;                          // gate/up GEMM n tiles (f / 128)
   int build_stage;                     // plan_build copies the block histograms into LDS
   int64_t o_hdr, o_c, o_low, o_grp, o_me, o_rowoff, o_rb, o_order, o_base;
@@ -37,6 +42,7 @@ struct PlanLayout {
   int64_t o_src, o_pos;
   int64_t o_bh, o_bp, o_brecv, o_bhr, o_bpr, o_baser;
   int64_t o_gumt_row, o_gumt_exp;
+  int64_t o_dnt_row, o_dnt_exp, o_dnt_band, o_dnt_nb;
   int64_t total_words;
   int pair_off[kMaxWorld + 1];   // first (token, slot) pair of each owner
   int blk_off[kMaxWorld + 1];    // first planner block of each owner
@@ -64,8 +70,11 @@ hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t*
                        int32_t* ws, uint16_t* x_layout, hipStream_t s);
 hipError_t launch_gateup(const PlanLayout& L, const int32_t* ws, const uint16_t* x,
                          const uint16_t* wgu, uint16_t* h, int grid, hipStream_t s);
-hipError_t launch_down(const PlanLayout& L, const int32_t* ws, const uint16_t* h,
-                       const uint16_t* wd, uint16_t* y, uint32_t* flags, uint32_t epoch,
+// down GEMM: `n_prod` persistent producer workgroups; the grid's remaining
+// workgroups (if any) are consumers (consume.h).  Local bands are also
+// written to recv.p[L.r].
+hipError_t launch_down(const PlanLayout& L, int32_t* ws, const uint16_t* h, const uint16_t* wd, uint16_t* y,
+                       uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks, int n_prod,
                        int grid, hipStream_t s);
 hipError_t launch_consumer(const PlanLayout& L, int32_t* ws, const uint16_t* y,
                            const uint32_t* flags, uint32_t epoch, const RecvPtrs& recv,

@@ -383,6 +383,50 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
       },
       sh);
 
+  // (j) down m-tiles, when tb_M divides 256: the runs of row-contiguous
+  //     bands in S order -- the remote bands of each expert (its remote
+  //     groups follow one another at the start of X_e), then the local bands
+  //     of each expert -- cut into tiles of at most dn_merge bands
+  int NDT = B * L.dn_sub;
+  if (L.dn_merge > 0) {
+    const int P = L.dn_merge;
+    int32_t* dt_row = ws + L.o_dnt_row;
+    int32_t* dt_exp = ws + L.o_dnt_exp;
+    int32_t* dt_band = ws + L.o_dnt_band;
+    int32_t* dt_nb = ws + L.o_dnt_nb;
+    auto run_of = [&](int q, int& e, int& first, int& nb, int& row0) {
+      if (q < E_l) {
+        e = order[q];
+        first = gstart[q * (W - 1)];   // with W == 1 there are no remote bands
+        nb = rb[e];
+        row0 = rowoff[e];
+      } else {
+        e = q - E_l;
+        first = gstart[NGR + e];
+        nb = (c[e * W + r] + tb - 1) / tb;
+        row0 = rowoff[e] + grp[e * W + r];
+      }
+    };
+    NDT = scan_items(
+        2 * E_l,
+        [&](int q) {
+          int e, first, nb, row0;
+          run_of(q, e, first, nb, row0);
+          return (nb + P - 1) / P;
+        },
+        [&](int q, int pre) {
+          int e, first, nb, row0;
+          run_of(q, e, first, nb, row0);
+          for (int j = 0; j * P < nb; ++j) {
+            dt_row[pre + j] = row0 + j * P * tb;
+            dt_exp[pre + j] = e;
+            dt_band[pre + j] = first + j * P;
+            dt_nb[pre + j] = min(P, nb - j * P);
+          }
+        },
+        sh);
+  }
+
   // results used by later kernels and by inspection
   for (int i = tid; i < EW; i += nt) {
     ws[L.o_c + i] = c[i];
@@ -409,6 +453,7 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     hdr[H_UNITS] = U;
     hdr[H_RCOUNT] = rcount;
     hdr[H_GU_MT] = NMT;
+    hdr[H_DN_MT] = NDT;
   }
 }
 

@@ -24,7 +24,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(LIB)
     names = declared_functions()
-    assert len(names) >= 9
+    assert len(names) >= 8
     for n in names:
         assert hasattr(lib, n), n
     import moe_expert_tile_amd as m

@@ -67,3 +67,52 @@ def test_replanning_reuses_the_workspace():
     exp = expected_plan(c1["plan"])
     for k, v in exp.items():
         assert np.array_equal(np.asarray(got[k]).astype(np.int64), np.asarray(v).astype(np.int64)), k
+
+
+def expected_tiles(pl):
+    """GEMM row tiles implied by the oracle plan: gate/up tiles cut every X_e
+    (experts in rule (ii) order) into 256-row pieces; down tiles cut each
+    maximal run of bands in S order with one expert and one side (remote or
+    local) into pieces of at most 256 / tb_M bands."""
+    gu_row, gu_exp = [], []
+    for e in pl.expert_order:
+        for i in range(-(-int(pl.m_e[e]) // 256)):
+            gu_row.append(int(pl.row_off[e]) + 256 * i)
+            gu_exp.append(int(e))
+    P = 256 // pl.tb_m
+    b = pl.bands
+    dn = []
+    s0 = 0
+    while s0 < pl.n_bands:
+        s1 = s0
+        while (s1 + 1 < pl.n_bands and b["expert"][s1 + 1] == b["expert"][s0]
+               and b["remote"][s1 + 1] == b["remote"][s0]):
+            s1 += 1
+        for f0 in range(s0, s1 + 1, P):
+            dn.append((int(b["src_row"][f0]), int(b["expert"][f0]), f0, min(P, s1 + 1 - f0)))
+        s0 = s1 + 1
+    return gu_row, gu_exp, dn
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_gemm_tile_tables(name):
+    """The planner's GEMM row-tile tables equal the ones the oracle plan
+    implies, and every down tile's bands are consecutive rows of one expert."""
+    c, share = run_plan(name, 1)
+    pl = c["plan"]
+    assert 256 % pl.tb_m == 0
+    hdr = share.header()
+    gu_row, gu_exp, dn = expected_tiles(pl)
+    assert hdr["gateup_row_tiles"] == len(gu_row)
+    assert hdr["down_row_tiles"] == len(dn)
+    assert share.array("gu_tile_row", len(gu_row)).tolist() == gu_row
+    assert share.array("gu_tile_expert", len(gu_row)).tolist() == gu_exp
+    got = list(zip(*(share.array(k, len(dn)).tolist() for k in
+                     ["dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands"])))
+    assert got == dn
+    covered = [f0 + q for _, _, f0, nb in dn for q in range(nb)]
+    assert covered == list(range(pl.n_bands))
+    for row0, e, f0, nb in dn:
+        for q in range(nb):
+            assert int(pl.bands["src_row"][f0 + q]) == row0 + q * pl.tb_m
+            assert int(pl.bands["expert"][f0 + q]) == e
