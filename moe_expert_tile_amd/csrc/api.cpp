@@ -113,6 +113,12 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->o_gumt_row = take(L->gu_mt_cap);
   L->o_gumt_exp = take(L->gu_mt_cap);
   L->o_dnt_row = take(B); L->o_dnt_exp = take(B); L->o_dnt_band = take(B); L->o_dnt_nb = take(B);
+  // stream-K: only when a GEMM can have more tiles than the smallest grid
+  const int64_t gu_tiles_max = (int64_t)L->gu_mt_cap * L->gu_ntn;
+  const int64_t dn_tiles_max = B * L->dn_sub * L->dn_ntn;
+  L->sk_slots = (std::max(gu_tiles_max, dn_tiles_max) > 8) ? 2 * kMaxProducers : 0;
+  L->o_skc = take(2 * kMaxProducers * 2);
+  L->o_skp = take((int64_t)L->sk_slots * 256 * 256);
   L->total_words = off;
   return true;
 }
@@ -296,7 +302,8 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   const hipStream_t st = (hipStream_t)stream;
   const int32_t* ws = (const int32_t*)plan_ws;
   int32_t* ws_rw = (int32_t*)plan_ws;
-  int full_grid = cus - cus % 8;
+  int full_grid = std::min(cus, kMaxProducers);
+  full_grid -= full_grid % 8;
   if (full_grid < 8) full_grid = 8;
 
   if (o.mode == MOE_MODE_COPY_ONLY) {
@@ -307,7 +314,7 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
     return rc;
   }
   record(o.events[0], st);
-  rc = hip_rc(launch_gateup(L, ws, x_layout, w_gate_up, h, full_grid, st));
+  rc = hip_rc(launch_gateup(L, ws_rw, x_layout, w_gate_up, h, epoch, full_grid, st));
   record(o.events[1], st);
   if (rc) return rc;
   if (o.mode == MOE_MODE_SERIAL) {
@@ -325,7 +332,7 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   // workgroups run the down GEMM, the last consumer_cus (one per CU, as the
   // GEMM's LDS footprint leaves room for one workgroup per CU) consume
   if (o.consumer_cus >= cus) return MOE_EINVAL;
-  int n_prod = cus - o.consumer_cus;
+  int n_prod = std::min(cus - o.consumer_cus, kMaxProducers);
   n_prod -= n_prod % 8;
   const int n_cons = o.consumer_blocks ? o.consumer_blocks : o.consumer_cus;
   record(o.events[2], st);

@@ -229,10 +229,40 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     n_nt = L.dn_ntn;
   }
   const int total = n_mt * n_nt;
-  const int G = g.n_prod;   // a multiple of 8
+  const int G = g.n_prod;   // a multiple of 8, at most kMaxProducers
   const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int KT = g.K / C::BK;
   const int32_t* rowoff = g.ws + L.o_rowoff;
+
+  // Work split.  The first `full` tiles (whole rounds of G) are taken whole:
+  // tile slot, slot + G, ...  When the last round would be at most 3/4 full
+  // and tiles are long (KT >= kMinSkKT), its sk_tiles tiles are shared out
+  // along K instead ("stream-K"): their
+  // sk_tiles * KT K steps are cut into G_sk equal ranges, one per slot below
+  // G_sk, each at least kMinSkSteps long.  A range spans at most two tiles;
+  // each part (a piece) accumulates its K steps and stores its fp32 partial
+  // sums, and the piece that completes a tile's K steps sums all pieces in
+  // K order (so the result does not depend on which piece came last) and
+  // runs the tile's epilogue.
+  int full = total, sk_tiles = 0, G_sk = 0;
+  int64_t W_sk = 0;
+  if (L.sk_slots >= 2 * G && total > G && KT >= kMinSkKT) {
+    const int rem = total % G;
+    if (rem != 0 && 4 * rem <= 3 * G) {
+      full = total - rem;
+      sk_tiles = rem;
+      W_sk = (int64_t)sk_tiles * KT;
+      G_sk = (int)min((int64_t)G, W_sk / kMinSkSteps);
+    }
+  }
+  auto sk_lo = [&](int w) { return (int64_t)w * W_sk / G_sk; };
+  int64_t sk_cur = 0, sk_hi = 0;
+  if (slot < G_sk) {
+    sk_cur = sk_lo(slot);
+    sk_hi = sk_lo(slot + 1);
+  }
+  float* sk_part = (float*)(g.ws + L.o_skp);
+  uint64_t* sk_ctr = (uint64_t*)(g.ws + L.o_skc) + (SWIGLU ? 0 : kMaxProducers);
 
   // load-side lane constants: lane l fills row RPB q + l / CPR, physical chunk
   // l % CPR, so it must fetch the logical chunk swz(row, l % CPR)
@@ -255,7 +285,22 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     }
   }
 
-  for (int t = slot; t < total; t += G) {
+  int t_dp = slot, piece = 0;
+  for (;;) {
+    // next work item: a whole tile, or a piece [kb, ke) of a stream-K tile
+    int t, kb = 0, ke = KT, sk_j = -1;
+    if (t_dp < full) {
+      t = t_dp;
+      t_dp += G;
+    } else if (sk_cur < sk_hi) {
+      sk_j = (int)(sk_cur / KT);
+      kb = (int)(sk_cur - (int64_t)sk_j * KT);
+      ke = (int)min((int64_t)KT, kb + (sk_hi - sk_cur));
+      t = full + sk_j;
+      sk_cur += ke - kb;
+    } else {
+      break;
+    }
     int mt, nt;
     decode_tile(t, n_mt, n_nt, mt, nt);
     // row tile: its expert, first row and row limit; for the down GEMM also
@@ -336,15 +381,16 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    const int KTt = empty ? 0 : KT;   // K steps of this tile
-    // every wave is done with the previous tile's LDS stages before the
+    const int KTt = empty ? 0 : ke - kb;   // K steps of this work item
+    // every wave is done with the previous item's LDS stages before the
     // prologue below refills them
     __syncthreads();
     // prologue: the first STAGES-1 stages in flight
 #pragma unroll
     for (int s = 0; s < C::STAGES - 1; ++s)
       if (s < KTt)
-        issue_stage<C>((lds_void_t*)(lds + s * C::STAGE_ELEMS), a_rsrc, a_off, b_rsrc, b_off, s * C::BK, wave);
+        issue_stage<C>((lds_void_t*)(lds + s * C::STAGE_ELEMS), a_rsrc, a_off, b_rsrc, b_off, (kb + s) * C::BK,
+                       wave);
 
     // One K step.  Stage kt has landed once at most `in_flight` later stages
     // of this wave are still in flight; the barrier makes it true for all
@@ -373,7 +419,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       read_frags(0, 0);
       if constexpr (ISSUE)
         issue_stage<C>((lds_void_t*)(lds + ((kt + C::STAGES - 1) % C::STAGES) * C::STAGE_ELEMS), a_rsrc, a_off,
-                       b_rsrc, b_off, (kt + C::STAGES - 1) * C::BK, wave);
+                       b_rsrc, b_off, (kb + kt + C::STAGES - 1) * C::BK, wave);
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk) {
         if (kk + 1 < C::KK) read_frags(kk + 1, (kk + 1) & 1);
@@ -394,6 +440,94 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     int kt = 0;
     for (; kt + C::STAGES - 1 < KTt; ++kt) k_step(kt, std::integral_constant<bool, true>{}, C::STAGES - 2);
     for (; kt < KTt; ++kt) k_step(kt, std::integral_constant<bool, false>{}, min(C::STAGES - 2, KTt - 1 - kt));
+
+    if (sk_j >= 0) {
+      // stream-K piece: store the partial sums in register order (slot
+      // 2*slot + piece, [float4 c][thread]), publish them, count this piece's
+      // K steps on the tile's epoch-tagged counter; the piece that completes
+      // KT adds every other piece's partials and goes on to the epilogue.
+      float4* mine = (float4*)(sk_part + (int64_t)(2 * slot + piece) * C::BM * C::BN);
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            mine[((i * C::FM + j) * 4 + q) * C::NT + tid] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      wait_vm0();
+      __syncthreads();   // also: every wave is done with the LDS ring
+      int* s_last = (int*)lds;
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        uint64_t* ctr = sk_ctr + sk_j;
+        uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t cnt;
+        for (;;) {
+          cnt = ((uint32_t)(old >> 32) == g.epoch ? (uint32_t)old : 0u) + (uint32_t)(ke - kb);
+          const uint64_t nv = ((uint64_t)g.epoch << 32) | cnt;
+          if (__hip_atomic_compare_exchange_strong(ctr, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT))
+            break;
+        }
+        *s_last = (cnt == (uint32_t)KT);
+      }
+      __syncthreads();
+      const int last = *s_last;
+      ++piece;
+      if (!last) continue;
+      // the tile's K range [sk_j*KT, (sk_j+1)*KT) meets the ranges of slots
+      // w_a..w_b (ascending K); each holds it as its first (piece 0) or
+      // second piece.  Sum all of them in that order -- this slot's own
+      // partial re-read from memory like the others -- so the result does
+      // not depend on which piece came last.  Pieces outside, and for each
+      // piece half the tile's loads in flight at once: the loads bypass this
+      // XCD's caches and their latency, not their bytes, sets the cost.
+      const int64_t a0 = (int64_t)sk_j * KT, a1 = a0 + KT;
+      int wa = (int)(a0 * G_sk / W_sk);
+      while (wa > 0 && sk_lo(wa) > a0) --wa;
+      while (wa + 1 < G_sk && sk_lo(wa + 1) <= a0) ++wa;
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      constexpr int FH = (C::FN + 1) / 2;   // blocks of i per half
+      for (int w = wa; w < G_sk && sk_lo(w) < a1; ++w) {
+        const int pw_idx = (sk_lo(w) / KT == sk_j) ? 0 : 1;
+        const uint64_t* part = (const uint64_t*)(sk_part + (int64_t)(2 * w + pw_idx) * C::BM * C::BN);
+#pragma unroll
+        for (int h = 0; h < C::FN; h += FH) {
+          uint64_t ld[FH][C::FM][4][2];
+#pragma unroll
+          for (int i = 0; i < FH; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                if (h + i < C::FN) {
+                  const int64_t o = (int64_t)((((h + i) * C::FM + j) * 4 + q) * C::NT + tid) * 2;
+                  ld[i][j][q][0] = __hip_atomic_load(part + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  ld[i][j][q][1] = __hip_atomic_load(part + o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+              }
+#pragma unroll
+          for (int i = 0; i < FH; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                if (h + i < C::FN) {
+                  acc[h + i][j][4 * q] += __uint_as_float((uint32_t)ld[i][j][q][0]);
+                  acc[h + i][j][4 * q + 1] += __uint_as_float((uint32_t)(ld[i][j][q][0] >> 32));
+                  acc[h + i][j][4 * q + 2] += __uint_as_float((uint32_t)ld[i][j][q][1]);
+                  acc[h + i][j][4 * q + 3] += __uint_as_float((uint32_t)(ld[i][j][q][1] >> 32));
+                }
+              }
+        }
+      }
+    }
 
     // epilogue: lane holds rows m = .. + (lane & 31), columns n = .. + 8*(v/4) + 4*(lane/32) + v%4
     const int mrow0 = row0 + wave_m * C::WM + lrow;
@@ -469,6 +603,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   }
 }
 
+
 // ring depth: the requested number of stages, at most what fits in LDS
 constexpr int fit_stages(int bm, int bn, int bk, int stages) {
   return stages * (bm + bn) * bk * 2 <= 160 * 1024 ? stages : (160 * 1024) / ((bm + bn) * bk * 2);
@@ -481,9 +616,9 @@ using Dn32 = Cfg<32, 256, 1, 4, 64, 3>;
 
 }  // namespace
 
-hipError_t launch_gateup(const PlanLayout& L, const int32_t* ws, const uint16_t* x, const uint16_t* wgu,
-                         uint16_t* h, int grid, hipStream_t s) {
-  GemmArgs a{const_cast<int32_t*>(ws), x, wgu, h, nullptr, 0u, L.d, L.f, 2 * L.f, L.f, grid, 0};
+hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const uint16_t* x, const uint16_t* wgu, uint16_t* h,
+                         uint32_t epoch, int grid, hipStream_t s) {
+  GemmArgs a{ws, x, wgu, h, nullptr, epoch, L.d, L.f, 2 * L.f, L.f, grid, 0};
   RecvPtrs none{};
   hipLaunchKernelGGL((grouped_gemm_kernel<GuCfg, true, false>), dim3(grid), dim3(GuCfg::NT), 0, s, L, a, none);
   return hipGetLastError();

@@ -15,6 +15,11 @@ constexpr int kCopyChunk = 32768;      // bytes per consumer copy unit
 constexpr int kGuBM = 256;             // gate/up GEMM tile rows
 constexpr int kGuBN = 256;             // gate/up GEMM tile cols (128 gate + 128 up)
 constexpr int kDnBN = 256;             // down GEMM tile cols
+constexpr int kMaxProducers = 256;     // persistent GEMM workgroups at most (one per CU on MI355X)
+constexpr int kMinSkSteps = 16;        // shortest K range of a stream-K piece
+constexpr int kMinSkKT = 128;          // stream-K only for tiles of at least this many K steps: the
+                                       // partials' round trip costs ~60-100 us per launch, which
+                                       // only a long tail round repays
 
 // header words of the plan workspace (mirrors the public description)
 enum Hdr {
@@ -36,6 +41,7 @@ struct PlanLayout {
   int dn_merge;                        // > 0: down m-tiles of up to dn_merge row-contiguous bands (table)
   int gu_ntn;                          // gate/up GEMM n tiles (f / 128)
   int build_stage;                     // plan_build copies the block histograms into LDS
+  int sk_slots;                        // stream-K partial-sum slots (256x256 fp32 each) in the workspace
   int64_t o_hdr, o_c, o_low, o_grp, o_me, o_rowoff, o_rb, o_order, o_base;
   int64_t o_bexp, o_bdst, o_bsrc, o_bdoff, o_bval;
   int64_t o_sfirst, o_snb, o_sdst, o_sdoff, o_ssrc, o_srows, o_sunit;
@@ -43,6 +49,8 @@ struct PlanLayout {
   int64_t o_bh, o_bp, o_brecv, o_bhr, o_bpr, o_baser;
   int64_t o_gumt_row, o_gumt_exp;
   int64_t o_dnt_row, o_dnt_exp, o_dnt_band, o_dnt_nb;
+  int64_t o_skc;                       // uint64 [2][kMaxProducers] stream-K tile counters (gate/up, down)
+  int64_t o_skp;                       // float [sk_slots][256*256] stream-K partial sums
   int64_t total_words;
   int pair_off[kMaxWorld + 1];   // first (token, slot) pair of each owner
   int blk_off[kMaxWorld + 1];    // first planner block of each owner
@@ -68,8 +76,8 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb,
 // launchers (defined next to their kernels); all asynchronous on `s`
 hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t* x_recv,
                        int32_t* ws, uint16_t* x_layout, hipStream_t s);
-hipError_t launch_gateup(const PlanLayout& L, const int32_t* ws, const uint16_t* x,
-                         const uint16_t* wgu, uint16_t* h, int grid, hipStream_t s);
+hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const uint16_t* x, const uint16_t* wgu, uint16_t* h,
+                         uint32_t epoch, int grid, hipStream_t s);
 // down GEMM: `n_prod` persistent producer workgroups; the grid's remaining
 // workgroups (if any) are consumers (consume.h).  Local bands are also
 // written to recv.p[L.r].

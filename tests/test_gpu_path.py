@@ -7,9 +7,9 @@
   is exactly zero (§4.2 step 2).
 * Combine (§4.5, §5.2): with the receive buffers pre-filled with other ranks'
   rows, exactly the plan's rows change and each is a bit-exact copy of its
-  layout row; overlapped and serial modes give identical buffers; repeated
-  epochs without a flag reset, with y poisoned by NaN before each call, give
-  the same buffers again.
+  layout row; repeated overlapped epochs without a flag reset, with y
+  poisoned by NaN before each call, copy exactly their own y and give the
+  same y again; serial and overlapped y agree within the tolerance.
 * Scale (§2.2 step 5): sampled tokens of the rank's own output against the
   oracle, whose receive rows come from the oracle's own FFN.
 """
@@ -92,20 +92,40 @@ def test_combine_writes_exactly_the_plan(name):
         assert np.array_equal(got, exp), f"owner {o}"
 
 
-@pytest.mark.parametrize("name", ["tiny_unit", "qwen3", "decode_tb32", "dsv3_skew"])
-def test_overlap_equals_serial_over_epochs(name):
+@pytest.mark.parametrize("name", ["tiny_unit", "mixtral", "qwen3", "decode_tb32", "dsv3_skew"])
+def test_overlapped_combine_over_epochs(name):
+    """Overlapped calls, each with y poisoned by NaN and the receive buffers
+    refilled first: every call's buffers equal the plan applied to that call's
+    own y (a consumer that read a tile before its flag would copy NaN or stale
+    rows), y is identical across epochs (the stream-K fixup sums in a fixed
+    order), and y matches the serial mode's within the tolerance -- bit for bit
+    where neither mode splits tiles along K (the overlapped down GEMM has 16
+    fewer producers, so the two modes may split different tail tiles)."""
     import moe_expert_tile_amd as m
     c, share, wgu_d, wd_d = planned(name, m.MODE_SERIAL)
-    cfg = c["cfg"]
-    ref = [r.clone() for r in share.recv]
+    cfg, pl = c["cfg"], c["plan"]
+    y_serial = host_bits(share.y[:pl.M])
+    written = OC.written_rows(pl)
+    y_first = None
     for it in range(3):
         share.y.fill_(float("nan"))
         for o in range(cfg.W):
             share.recv[o].copy_(dev_bf16(synth.foreign_rows(cfg, o)))
         share.combine(wgu_d, wd_d, mode=m.MODE_OVERLAP)
         assert share.status() == m.MOE_OK
+        Y = host_bits(share.y[:pl.M])
         for o in range(cfg.W):
-            assert torch.equal(share.recv[o].view(torch.int16), ref[o].view(torch.int16)), (it, o)
+            exp = synth.foreign_rows(cfg, o)
+            dst, src = written[o]
+            exp[dst] = Y[src]
+            assert np.array_equal(host_bits(share.recv[o][: exp.shape[0]]), exp), (it, o)
+        if y_first is None:
+            y_first = Y
+        else:
+            assert np.array_equal(Y, y_first), it
+    assert tol_ratio(y_first, y_serial, name == "tiny") <= 1.0
+    if name in ("tiny_unit", "decode_tb32"):
+        assert np.array_equal(y_first, y_serial)
 
 
 @pytest.mark.parametrize("name", WORKLOADS)
