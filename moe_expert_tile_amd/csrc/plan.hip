@@ -150,12 +150,20 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   (void)block_excl_scan(bad_local, sh, &bad_total);
 
   // (b) group counts c[e][o], low[o], per-block prefixes within each owner
+  // (the histogram entries are loaded 8 at a time ahead of the dependent
+  // stores, which the compiler cannot move past loads from the same workspace)
   for (int it = tid; it < W * (E_l + 1); it += nt) {
     const int o = it / (E_l + 1), x = it % (E_l + 1);
     int run = 0;
-    for (int b = L.blk_off[o]; b < L.blk_off[o + 1]; ++b) {
-      bp[(int64_t)b * (E_l + 1) + x] = run;
-      run += bh[(int64_t)b * HB + x];
+    for (int b0 = L.blk_off[o]; b0 < L.blk_off[o + 1]; b0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = (b0 + u < L.blk_off[o + 1]) ? bh[(int64_t)(b0 + u) * HB + x] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b0 + u < L.blk_off[o + 1]) bp[(int64_t)(b0 + u) * (E_l + 1) + x] = run;
+        run += v[u];
+      }
     }
     if (x < E_l) c[x * W + o] = run; else low[o] = run;
   }
@@ -171,9 +179,15 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   // (d) the rank's own tokens: per-expert counts and per-block prefixes
   for (int g = tid; g < E; g += nt) {
     int run = 0;
-    for (int b = 0; b < L.NB_r; ++b) {
-      bpr[(int64_t)b * E + g] = run;
-      run += bhr[(int64_t)b * E + g];
+    for (int b0 = 0; b0 < L.NB_r; b0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = (b0 + u < L.NB_r) ? bhr[(int64_t)(b0 + u) * E + g] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b0 + u < L.NB_r) bpr[(int64_t)(b0 + u) * E + g] = run;
+        run += v[u];
+      }
     }
     baser[g] = run;  // count for now, turned into a prefix below
   }
@@ -260,76 +274,54 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     return;
   }
 
-  // (g) bands in S order, one thread per group
+  // (g) bands in S order, one thread per band.  Band s belongs to the last
+  //     group whose first band is <= s (that group is never empty).
   int32_t* bexp = ws + L.o_bexp;
   int32_t* bdst = ws + L.o_bdst;
   int32_t* bsrc = ws + L.o_bsrc;
   int32_t* bdoff = ws + L.o_bdoff;
   int32_t* bval = ws + L.o_bval;
-  for (int gi = tid; gi < NG; gi += nt) {
+  auto group_of = [&](int band) {
+    int lo = 0, hi = NG - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (gstart[mid] <= band) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  for (int b = tid; b < B; b += nt) {
+    const int gi = group_of(b);
     int e, o;
     group_eo(gi, e, o);
-    const int n = c[e * W + o];
-    const int gs = gstart[gi];
-    const int src0 = rowoff[e] + grp[e * W + o];
-    const int d0 = base[o * E_l + e];
-    for (int b = 0; b * tb < n; ++b) {
-      const int s = gs + b;
-      bexp[s] = e;
-      bdst[s] = o;
-      bsrc[s] = src0 + b * tb;
-      bdoff[s] = d0 + b * tb;
-      bval[s] = min(tb, n - b * tb);
-    }
+    const int q = b - gstart[gi];
+    bexp[b] = e;
+    bdst[b] = o;
+    bsrc[b] = rowoff[e] + grp[e * W + o] + q * tb;
+    bdoff[b] = base[o * E_l + e] + q * tb;
+    bval[b] = min(tb, c[e * W + o] - q * tb);
   }
+  __syncthreads();   // the band arrays are read back below
 
   // segments (§5.2): the first and the last remote band alone; otherwise runs
-  // of <= mgb bands that restart at every group boundary.  Segments never cross
-  // a group, so each group's segments are found by its own thread.
+  // of <= mgb bands that restart at every group boundary.  Every band decides
+  // whether it starts a segment; a scan numbers the starts; each segment then
+  // reads its fields off its first band (segments never cross a group, so the
+  // first band's destination offset and source row are the segment's) and
+  // sums its <= 64 bands' valid rows; a second scan places the copy units.
   const int mgb = L.mgb;
-  auto seg_start = [&](int s, int gs, bool remote) {
-    if (remote) {
-      if (s == 0 || s == n_remote - 1) return true;
+  auto starts_segment = [&](int b) {
+    const int gi = group_of(b);
+    const int gs = gstart[gi];
+    if (b == gs) return 1;
+    if (gi < NGR) {
+      if (b == n_remote - 1) return 1;
       const int run0 = gs > 1 ? gs : 1;
-      return ((s - run0) % mgb) == 0;
+      return ((b - run0) % mgb) == 0 ? 1 : 0;
     }
-    return ((s - gs) % mgb) == 0;
+    return ((b - gs) % mgb) == 0 ? 1 : 0;
   };
   const int64_t row_bytes = (int64_t)L.d * 2;
   auto units_of = [&](int rows) { return (int)((rows * row_bytes + kCopyChunk - 1) / kCopyChunk); };
-  // walks the segments of group gi; fn(first_band, n_bands, rows) per segment
-  auto for_segments = [&](int gi, auto fn) {
-    int e, o;
-    group_eo(gi, e, o);
-    const int cnt = c[e * W + o];
-    const int gs = gstart[gi], n = (cnt + tb - 1) / tb;
-    int first = gs, rows = 0;
-    for (int s = gs; s < gs + n; ++s) {
-      if (s > gs && seg_start(s, gs, gi < NGR)) {
-        fn(first, s - first, rows);
-        first = s;
-        rows = 0;
-      }
-      rows += min(tb, cnt - (s - gs) * tb);
-    }
-    if (n > 0) fn(first, gs + n - first, rows);
-  };
-  auto group_segs = [&](int gi) {
-    int cnt = 0;
-    for_segments(gi, [&](int, int, int) { ++cnt; });
-    return cnt;
-  };
-  auto group_units = [&](int gi) {
-    int u = 0;
-    for_segments(gi, [&](int, int, int rows) { u += units_of(rows); });
-    return u;
-  };
-  const int NS = scan_items(NG, group_segs, [&](int gi, int pre) { gseg[gi] = pre; }, sh);
-  const int U = scan_items(NG, group_units, [&](int gi, int pre) { gunit[gi] = pre; }, sh);
-  int nrs_local = 0;
-  for (int gi = tid; gi < NGR; gi += nt) nrs_local += group_segs(gi);
-  int n_rsegs;
-  (void)block_excl_scan(nrs_local, sh, &n_rsegs);
   int32_t* sfirst = ws + L.o_sfirst;
   int32_t* snb = ws + L.o_snb;
   int32_t* sdst = ws + L.o_sdst;
@@ -337,35 +329,46 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   int32_t* ssrc = ws + L.o_ssrc;
   int32_t* srows = ws + L.o_srows;
   int32_t* sunit = ws + L.o_sunit;
-  for (int gi = tid; gi < NG; gi += nt) {
-    int e, o;
-    group_eo(gi, e, o);
-    const int gs = gstart[gi];
-    int sidx = gseg[gi];
-    int u = gunit[gi];
-    for_segments(gi, [&](int first, int nb, int rows) {
-      sfirst[sidx] = first;
-      snb[sidx] = nb;
-      sdst[sidx] = o;
-      sdoff[sidx] = base[o * E_l + e] + (first - gs) * tb;
-      ssrc[sidx] = rowoff[e] + grp[e * W + o] + (first - gs) * tb;
-      srows[sidx] = rows;
-      sunit[sidx] = u;
-      u += units_of(rows);
-      ++sidx;
-    });
+  int* s_nrsegs = gseg;   // one LDS word (the per-group table is not needed)
+  if (tid == 0) *s_nrsegs = -1;
+  __syncthreads();
+  const int NS = scan_items(
+      B, starts_segment,
+      [&](int b, int pre) {
+        if (starts_segment(b)) sfirst[pre] = b;
+        if (b == n_remote) *s_nrsegs = pre;   // the first local band starts a segment
+      },
+      sh);
+  const int n_rsegs = (*s_nrsegs >= 0) ? *s_nrsegs : NS;
+  for (int i = tid; i < NS; i += nt) {
+    const int b0 = sfirst[i];
+    const int b1 = (i + 1 < NS) ? sfirst[i + 1] : B;
+    int rows = 0;
+    for (int b = b0; b < b1; ++b) rows += bval[b];
+    snb[i] = b1 - b0;
+    sdst[i] = bdst[b0];
+    sdoff[i] = bdoff[b0];
+    ssrc[i] = bsrc[b0];
+    srows[i] = rows;
   }
+  __syncthreads();   // srows is read back by the scan
+  const int U = scan_items(
+      NS, [&](int i) { return units_of(srows[i]); }, [&](int i, int pre) { sunit[i] = pre; }, sh);
   if (tid == 0) sunit[NS] = U;
 
   // (h) padding entries of src_index: the tail of every remote group
   int32_t* src = ws + L.o_src;
-  for (int gi = tid; gi < NGR; gi += nt) {
-    int e, o;
-    group_eo(gi, e, o);
-    const int n = c[e * W + o];
-    const int row0 = rowoff[e] + grp[e * W + o];
-    const int padded = ((n + tb - 1) / tb) * tb;
-    for (int q = n; q < padded; ++q) src[row0 + q] = -1;
+  // one wavefront per group, its lanes over the group's (< tb) pad rows
+  {
+    const int wv = tid >> 6, nwv = nt >> 6, ln = tid & 63;
+    for (int gi = wv; gi < NGR; gi += nwv) {
+      int e, o;
+      group_eo(gi, e, o);
+      const int n = c[e * W + o];
+      const int padded = ((n + tb - 1) / tb) * tb;
+      const int row0 = rowoff[e] + grp[e * W + o];
+      for (int q = n + ln; q < padded; q += 64) src[row0 + q] = -1;
+    }
   }
 
   // (i) gate/up m-tiles: every X_e cut into kGuBM-row tiles, experts in order
