@@ -52,25 +52,32 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #ifndef MOE_GU_BK
 #define MOE_GU_BK 64
 #endif
-#ifndef MOE_GU_STAGES
-#define MOE_GU_STAGES 2
+#ifndef MOE_GU_SA
+#define MOE_GU_SA 2
+#endif
+#ifndef MOE_GU_SB
+#define MOE_GU_SB 2
 #endif
 #ifndef MOE_DN_BK
 #define MOE_DN_BK 64
 #endif
-#ifndef MOE_DN_STAGES
-#define MOE_DN_STAGES 2
+#ifndef MOE_DN_SA
+#define MOE_DN_SA 2
+#endif
+#ifndef MOE_DN_SB
+#define MOE_DN_SB 2
 #endif
 constexpr int kGroupM = MOE_GROUP_M;   // row tiles per column sweep
 
-// BM x BN output tile, WAVES_M x WAVES_N wavefronts, K step BK, STAGES-deep
-// global -> LDS ring.  An LDS row holds BK bf16 (BK/8 chunks of 16 bytes);
-// chunks are XOR-swizzled so that any 16 lanes reading 16 consecutive rows at
-// the same logical chunk touch 16 distinct 16-byte bank groups of gfx950's
-// 64-bank LDS (one ds_read_b128 phase).
-template <int BM_, int BN_, int WAVES_M, int WAVES_N, int BK_, int STAGES_>
+// BM x BN output tile, WAVES_M x WAVES_N wavefronts, K step BK; the A and B
+// operands have their own global -> LDS rings, SA and SB stages deep (2 or
+// 3).  An LDS row holds BK bf16 (BK/8 chunks of 16 bytes); chunks are
+// XOR-swizzled so that any 16 lanes reading 16 consecutive rows at the same
+// logical chunk touch 16 distinct 16-byte bank groups of gfx950's 64-bank LDS
+// (one ds_read_b128 phase).
+template <int BM_, int BN_, int WAVES_M, int WAVES_N, int BK_, int SA_, int SB_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, SA = SA_, SB = SB_;
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int NT = NW * 64;
   static constexpr int WM = BM / WAVES_M;
@@ -83,18 +90,23 @@ struct Cfg {
   static constexpr int R256 = 256 / (BK * 2);   // rows per 256-byte bank line
   static constexpr int A_ELEMS = BM * BK;
   static constexpr int B_ELEMS = BN * BK;
-  static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
-  static constexpr int LDS_BYTES = STAGES * STAGE_ELEMS * 2;
+  static constexpr int LDS_ELEMS = SA * A_ELEMS + SB * B_ELEMS;
+  static constexpr int LDS_BYTES = LDS_ELEMS * 2;
   static constexpr int A_LOADS = BM / RPB / NW;  // 1 KB wave loads per stage and wave
   static constexpr int B_LOADS = BN / RPB / NW;
   static constexpr int LPW = A_LOADS + B_LOADS;
+  static constexpr int S_DEEP = SA > SB ? SA : SB;
+  static constexpr int S_SHALLOW = SA < SB ? SA : SB;
+  // loads of this wave still in flight at a K step's barrier (while a later
+  // stage exists): the newest stage of every 3-deep ring
+  static constexpr int DEEP_LOADS = (SA == 3 ? A_LOADS : 0) + (SB == 3 ? B_LOADS : 0);
   static_assert(NW == 4 || NW == 8, "four or eight wavefronts per workgroup");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "every wavefront loads both operands");
   static_assert(BM % (RPB * NW) == 0 && BN % (RPB * NW) == 0, "whole wave loads");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-  static_assert(STAGES >= 2 && STAGES <= 6, "ring depth");
-  static_assert(LPW * (STAGES - 2) <= 63, "vmcnt range");
+  static_assert(SA >= 2 && SA <= 3 && SB >= 2 && SB <= 3, "ring depths 2 or 3");
+  static_assert(DEEP_LOADS <= 63, "vmcnt range");
   __device__ static int swz(int row, int c) { return c ^ ((row / R256) % CPR); }
 };
 
@@ -120,25 +132,22 @@ __device__ __forceinline__ void stamp_max(int32_t* hdr, int word) {
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Workgroup barrier for the K loop: this wavefront waits until at most
-// `stages_in_flight` later stages of its own global->LDS loads are
-// outstanding (so the current stage has landed) and its LDS reads are done,
-// then all wavefronts meet.  __syncthreads() would also wait for every
-// outstanding load (vmcnt(0)) and so drain the prefetch ring.  Written with
+// K-step barriers wait for this wave's own outstanding global->LDS loads with
 // the waitcnt builtin (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
-// 6:4, lgkmcnt in 11:8) rather than inline assembly, so the compiler's own
-// counter tracking sees the wait and keeps its later LDS waits partial.
+// 6:4, lgkmcnt in 11:8): __syncthreads() would wait for every outstanding
+// load (vmcnt(0)) and so drain the prefetch rings, and inline assembly would
+// hide the wait from the compiler's own counter tracking.
 __host__ __device__ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4); }
 
-template <int LPW>
-__device__ __forceinline__ void stage_barrier(int stages_in_flight) {
-  switch (stages_in_flight) {
-    case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(LPW)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LPW)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * LPW)); break;
-    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4 * LPW)); break;
-  }
+// Workgroup barrier of a K step: this wavefront waits until at most `n` of
+// its global->LDS loads are outstanding (n is 0 or one of the compile-time
+// load counts) and its LDS reads are done, then all wavefronts meet.
+template <class C>
+__device__ __forceinline__ void stage_barrier(int n) {
+  if (n == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  else if (n == C::A_LOADS) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(C::A_LOADS));
+  else if (n == C::B_LOADS) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(C::B_LOADS));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(C::LPW));
   __builtin_amdgcn_s_barrier();
 }
 
@@ -175,33 +184,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kBufWord3);
 }
 
-template <class C>
-__device__ __forceinline__ void issue_stage(lds_void_t* lds_stage, __amdgpu_buffer_rsrc_t ra,
-                                            const uint32_t (&a_off)[C::A_LOADS], __amdgpu_buffer_rsrc_t rb,
-                                            const uint32_t (&b_off)[C::B_LOADS], int k0, int wave) {
-  // wave `wave` fills LDS rows [RPB q, RPB (q+1)) for q = wave, wave + NW, ...;
-  // the lane byte offsets (from wave-uniform bases) carry the swizzled chunk,
-  // the K offset goes in the scalar offset.  MUBUF loads with the LDS bit
-  // count only in vmcnt, so the LDS-read waits around them stay partial.
-  char* base = (char*)lds_stage;
+// One operand's share of a stage: wave `wave` fills LDS rows [RPB q, RPB (q+1))
+// for q = wave, wave + NW, ...; the lane byte offsets (from wave-uniform
+// bases) carry the swizzled chunk, the K offset goes in the scalar offset.
+// MUBUF loads with the LDS bit count only in vmcnt, so the LDS-read waits
+// around them stay partial.
+template <int NLOADS, int NW>
+__device__ __forceinline__ void issue_operand(lds_void_t* dst, __amdgpu_buffer_rsrc_t rsrc,
+                                              const uint32_t (&off)[NLOADS], int k0, int wave) {
+  char* base = (char*)dst;
   const int koff = 2 * k0;
 #pragma unroll
-  for (int i = 0; i < C::A_LOADS; ++i) {
-    const int q = wave + i * C::NW;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(base + q * 1024), 16, (int)a_off[i], koff, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < C::B_LOADS; ++i) {
-    const int q = wave + i * C::NW;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(base + C::A_ELEMS * 2 + q * 1024), 16, (int)b_off[i],
-                                             koff, 0, 0);
+  for (int i = 0; i < NLOADS; ++i) {
+    const int q = wave + i * NW;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(base + q * 1024), 16, (int)off[i], koff, 0, 0);
   }
 }
 
 template <class C, bool SWIGLU, bool FLAGS>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
 void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::STAGES * C::STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int WAVES_N = C::BN / C::WN;
   const int wave_m = wave / WAVES_N, wave_n = wave % WAVES_N;
@@ -385,29 +388,43 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     // every wave is done with the previous item's LDS stages before the
     // prologue below refills them
     __syncthreads();
-    // prologue: the first STAGES-1 stages in flight
-#pragma unroll
-    for (int s = 0; s < C::STAGES - 1; ++s)
-      if (s < KTt)
-        issue_stage<C>((lds_void_t*)(lds + s * C::STAGE_ELEMS), a_rsrc, a_off, b_rsrc, b_off, (kb + s) * C::BK,
-                       wave);
+    // Stage k of A lives in A buffer k % SA, of B in B buffer k % SB.  Each
+    // K step issues the shallow ring's next stage first, then the deep
+    // ring's, so at a step's barrier only the deep ring's newest stage may
+    // still be in flight.  Prologue: shallow(0), deep(0), then stage 1 of
+    // every 3-deep ring.
+    auto a_buf = [&](int k) __attribute__((always_inline)) { return (lds_void_t*)(lds + (k % C::SA) * C::A_ELEMS); };
+    auto b_buf = [&](int k) __attribute__((always_inline)) { return (lds_void_t*)(lds + C::SA * C::A_ELEMS + (k % C::SB) * C::B_ELEMS); };
+    auto issue_a = [&](int k) __attribute__((always_inline)) { issue_operand<C::A_LOADS, C::NW>(a_buf(k), a_rsrc, a_off, (kb + k) * C::BK, wave); };
+    auto issue_b = [&](int k) __attribute__((always_inline)) { issue_operand<C::B_LOADS, C::NW>(b_buf(k), b_rsrc, b_off, (kb + k) * C::BK, wave); };
+    auto issue_shallow = [&](int k) __attribute__((always_inline)) { if constexpr (C::SA <= C::SB) issue_a(k); else issue_b(k); };
+    auto issue_deep = [&](int k) __attribute__((always_inline)) { if constexpr (C::SA <= C::SB) issue_b(k); else issue_a(k); };
+    if (KTt > 0) {
+      issue_shallow(0);
+      issue_deep(0);
+    }
+    if (KTt > 1) {
+      if constexpr (C::SA == 3) issue_a(1);
+      if constexpr (C::SB == 3) issue_b(1);
+    }
 
-    // One K step.  Stage kt has landed once at most `in_flight` later stages
-    // of this wave are still in flight; the barrier makes it true for all
-    // waves and also retires every read of the buffer refilled next.
-    // Operand fragments run one 16-wide k-substep ahead of the MFMAs (two
-    // register sets), so at most 2 (FN + FM) LDS reads are outstanding and
-    // each substep waits only for its own fragments; the next stage's
-    // global->LDS loads go out after the first substep's reads.  The
-    // steady-state steps always refill (ISSUE) and the last STAGES-1 never
-    // do, so each step body is one branch-free scheduling region.
-    auto k_step = [&](int kt, auto issue_tag, int in_flight) {
-      constexpr bool ISSUE = decltype(issue_tag)::value;
-      stage_barrier<C::LPW>(in_flight);
-      const uint16_t* sa = lds + (kt % C::STAGES) * C::STAGE_ELEMS;
-      const uint16_t* sb = sa + C::A_ELEMS;
+    // One K step.  The barrier waits for stage kt (every later stage but
+    // the deep ring's newest has been issued after it) and retires every LDS
+    // read of the buffers refilled next.  Operand fragments run one 16-wide
+    // k-substep ahead of the MFMAs (two register sets), so at most
+    // 2 (FN + FM) LDS reads are outstanding and each substep waits only for
+    // its own fragments; the next stages' global->LDS loads go out after the
+    // first substep's reads.  Steady-state steps issue both rings, the last
+    // S_DEEP-1 steps fewer, so each step body is one branch-free scheduling
+    // region.
+    auto k_step = [&](int kt, auto issue_sh_tag, auto issue_dp_tag, int in_flight) __attribute__((always_inline)) {
+      constexpr bool ISSUE_SH = decltype(issue_sh_tag)::value;
+      constexpr bool ISSUE_DP = decltype(issue_dp_tag)::value;
+      stage_barrier<C>(in_flight);
+      const uint16_t* sa = lds + (kt % C::SA) * C::A_ELEMS;
+      const uint16_t* sb = lds + C::SA * C::A_ELEMS + (kt % C::SB) * C::B_ELEMS;
       bf16x8 pw[2][C::FN], px[2][C::FM];
-      auto read_frags = [&](int kk, int slot) {
+      auto read_frags = [&](int kk, int slot) __attribute__((always_inline)) {
         const int phys = ((2 * kk + lhalf) ^ rsw) * 8;
 #pragma unroll
         for (int i = 0; i < C::FN; ++i)
@@ -417,9 +434,8 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
           px[slot][j] = *(const bf16x8*)(sa + (wave_m * C::WM + 32 * j + lrow) * C::BK + phys);
       };
       read_frags(0, 0);
-      if constexpr (ISSUE)
-        issue_stage<C>((lds_void_t*)(lds + ((kt + C::STAGES - 1) % C::STAGES) * C::STAGE_ELEMS), a_rsrc, a_off,
-                       b_rsrc, b_off, (kb + kt + C::STAGES - 1) * C::BK, wave);
+      if constexpr (ISSUE_SH) issue_shallow(kt + C::S_SHALLOW - 1);
+      if constexpr (ISSUE_DP) issue_deep(kt + C::S_DEEP - 1);
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk) {
         if (kk + 1 < C::KK) read_frags(kk + 1, (kk + 1) & 1);
@@ -429,17 +445,25 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
           for (int j = 0; j < C::FM; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pw[kk & 1][i], px[kk & 1][j], acc[i][j], 0, 0, 0);
       }
+      constexpr int NVMEM = (ISSUE_SH ? (C::SA <= C::SB ? C::A_LOADS : C::B_LOADS) : 0) +
+                            (ISSUE_DP ? (C::SA <= C::SB ? C::B_LOADS : C::A_LOADS) : 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::FN + C::FM, 0);
-      if constexpr (ISSUE) __builtin_amdgcn_sched_group_barrier(kSchedVmem, C::LPW, 0);
+      if constexpr (NVMEM > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmem, NVMEM, 0);
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk) {
         if (kk + 1 < C::KK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::FN + C::FM, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, C::FN * C::FM, 0);
       }
     };
+    using T_ = std::integral_constant<bool, true>;
+    using F_ = std::integral_constant<bool, false>;
+    // one loop per step body (a branch between bodies inside one loop makes
+    // the register allocator spill)
     int kt = 0;
-    for (; kt + C::STAGES - 1 < KTt; ++kt) k_step(kt, std::integral_constant<bool, true>{}, C::STAGES - 2);
-    for (; kt < KTt; ++kt) k_step(kt, std::integral_constant<bool, false>{}, min(C::STAGES - 2, KTt - 1 - kt));
+    for (; kt + C::S_DEEP - 1 < KTt; ++kt) k_step(kt, T_{}, T_{}, C::DEEP_LOADS);
+    if constexpr (C::S_DEEP > C::S_SHALLOW)
+      for (; kt + C::S_SHALLOW - 1 < KTt; ++kt) k_step(kt, T_{}, F_{}, (kt + 1 < KTt) ? C::DEEP_LOADS : 0);
+    for (; kt < KTt; ++kt) k_step(kt, F_{}, F_{}, (kt + 1 < KTt) ? C::DEEP_LOADS : 0);
 
     if (sk_j >= 0) {
       // stream-K piece: store the partial sums in register order (slot
@@ -604,15 +628,11 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
 }
 
 
-// ring depth: the requested number of stages, at most what fits in LDS
-constexpr int fit_stages(int bm, int bn, int bk, int stages) {
-  return stages * (bm + bn) * bk * 2 <= 160 * 1024 ? stages : (160 * 1024) / ((bm + bn) * bk * 2);
-}
-using GuCfg = Cfg<256, 256, MOE_GU_WAVES_M, MOE_GU_WAVES_N, MOE_GU_BK, fit_stages(256, 256, MOE_GU_BK, MOE_GU_STAGES)>;
-using Dn256 = Cfg<256, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_DN_BK, fit_stages(256, 256, MOE_DN_BK, MOE_DN_STAGES)>;
-using Dn128 = Cfg<128, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_DN_BK, fit_stages(128, 256, MOE_DN_BK, MOE_DN_STAGES)>;
-using Dn64 = Cfg<64, 256, 1, 4, 32, 4>;
-using Dn32 = Cfg<32, 256, 1, 4, 64, 3>;
+using GuCfg = Cfg<256, 256, MOE_GU_WAVES_M, MOE_GU_WAVES_N, MOE_GU_BK, MOE_GU_SA, MOE_GU_SB>;
+using Dn256 = Cfg<256, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_DN_BK, MOE_DN_SA, MOE_DN_SB>;
+using Dn128 = Cfg<128, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_DN_BK, MOE_DN_SA, MOE_DN_SB>;
+using Dn64 = Cfg<64, 256, 1, 4, 32, 3, 3>;
+using Dn32 = Cfg<32, 256, 1, 4, 64, 3, 3>;
 
 }  // namespace
 
