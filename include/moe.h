@@ -82,7 +82,8 @@ typedef struct moe_sizes {
  *   [10] gate/up row tiles            [11] down row tiles
  *   [12..13] uint64: 100 MHz wall clock when the last producer workgroup of
  *            the down GEMM ended (raised by every call, never reset)
- *   [14..15] uint64: the same for the last consumer workgroup */
+ *   [14..15] uint64: the same for the last consumer workgroup
+ *   [16] down row tiles of remote bands (they precede the local ones) */
 typedef struct moe_plan_view {
   size_t hdr;
   size_t c;          /* [E_l][W] rows of local expert e from owner o */
@@ -113,7 +114,7 @@ enum {
 
 typedef struct moe_combine_opts {
   int32_t mode;             /* MOE_MODE_* */
-  int32_t consumer_cus;     /* OVERLAP: CUs given to the consumer, multiple of 8 in [8, 128]; 0 = 16 */
+  int32_t consumer_cus;     /* OVERLAP: CUs given to the consumer, multiple of 8 in [8, 128]; 0 = 32 */
   int32_t consumer_blocks;  /* workgroups of the consumer; 0 = consumer_cus (OVERLAP) or 1024 */
   int32_t reserved;
   int64_t spin_timeout_ns;  /* bound on the consumer's wait for one segment's flags; 0 = 2 s */

@@ -67,6 +67,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #ifndef MOE_DN_SB
 #define MOE_DN_SB 2
 #endif
+#ifndef MOE_LOAD_AUX
+#define MOE_LOAD_AUX 0   // cache-policy bits of the operand loads (default policy measured best)
+#endif
 constexpr int kGroupM = MOE_GROUP_M;   // row tiles per column sweep
 
 // BM x BN output tile, WAVES_M x WAVES_N wavefronts, K step BK; the A and B
@@ -197,7 +200,8 @@ __device__ __forceinline__ void issue_operand(lds_void_t* dst, __amdgpu_buffer_r
 #pragma unroll
   for (int i = 0; i < NLOADS; ++i) {
     const int q = wave + i * NW;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(base + q * 1024), 16, (int)off[i], koff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(base + q * 1024), 16, (int)off[i], koff, 0,
+                                             MOE_LOAD_AUX);
   }
 }
 
@@ -223,13 +227,19 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   }
   if (hdr[H_ERROR] != 0) return;
 
-  int n_mt, n_nt;
+  // Row tiles are taken in two regions, each in grouped order: for the down
+  // GEMM the remote bands' tiles [0, n_mt_r) before the local bands' (so the
+  // tail of the tile order, which the stream-K split finishes last, holds
+  // local tiles the consumer does not wait for); gate/up has one region.
+  int n_mt, n_nt, n_mt_r;
   if constexpr (SWIGLU) {
     n_mt = hdr[H_GU_MT];
     n_nt = L.gu_ntn;
+    n_mt_r = n_mt;
   } else {
     n_mt = hdr[H_DN_MT];
     n_nt = L.dn_ntn;
+    n_mt_r = hdr[H_DN_MT_R];
   }
   const int total = n_mt * n_nt;
   const int G = g.n_prod;   // a multiple of 8, at most kMaxProducers
@@ -305,7 +315,12 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       break;
     }
     int mt, nt;
-    decode_tile(t, n_mt, n_nt, mt, nt);
+    if (t < n_mt_r * n_nt) {
+      decode_tile(t, n_mt_r, n_nt, mt, nt);
+    } else {
+      decode_tile(t - n_mt_r * n_nt, n_mt - n_mt_r, n_nt, mt, nt);
+      mt += n_mt_r;
+    }
     // row tile: its expert, first row and row limit; for the down GEMM also
     // the first band and the number of bands whose flags it sets
     int e, row0, lim, band0 = 0, nbt = 1;

@@ -29,6 +29,7 @@ enum Hdr {
   // workgroup of the down-GEMM launch as it ends (atomic max, so no reset is
   // needed between calls): words 12-13 and 14-15
   H_T_PROD_END = 12, H_T_CONS_END = 14,
+  H_DN_MT_R = 16,   // down row tiles of remote bands (they come first)
   H_WORDS = 64
 };
 

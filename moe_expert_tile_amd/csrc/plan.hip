@@ -391,6 +391,9 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   //     groups follow one another at the start of X_e), then the local bands
   //     of each expert -- cut into tiles of at most dn_merge bands
   int NDT = B * L.dn_sub;
+  int* s_ndt_r = gunit;   // one LDS word: down row tiles of the remote runs
+  if (tid == 0) *s_ndt_r = n_remote * L.dn_sub;
+  __syncthreads();
   if (L.dn_merge > 0) {
     const int P = L.dn_merge;
     int32_t* dt_row = ws + L.o_dnt_row;
@@ -418,6 +421,7 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
           return (nb + P - 1) / P;
         },
         [&](int q, int pre) {
+          if (q == E_l) *s_ndt_r = pre;   // the remote runs come first
           int e, first, nb, row0;
           run_of(q, e, first, nb, row0);
           for (int j = 0; j * P < nb; ++j) {
@@ -457,6 +461,7 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     hdr[H_RCOUNT] = rcount;
     hdr[H_GU_MT] = NMT;
     hdr[H_DN_MT] = NDT;
+    hdr[H_DN_MT_R] = *s_ndt_r;
   }
 }
 

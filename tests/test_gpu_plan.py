@@ -110,6 +110,9 @@ def test_gemm_tile_tables(name):
     got = list(zip(*(share.array(k, len(dn)).tolist() for k in
                      ["dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands"])))
     assert got == dn
+    o = share.offsets["hdr"] // 4
+    n_remote_tiles = sum(1 for _, _, f0, _ in dn if pl.bands["remote"][f0])
+    assert int(share.plan_ws[o + 16]) == n_remote_tiles
     covered = [f0 + q for _, _, f0, nb in dn for q in range(nb)]
     assert covered == list(range(pl.n_bands))
     for row0, e, f0, nb in dn:
