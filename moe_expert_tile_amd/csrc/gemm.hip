@@ -31,6 +31,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Tile shapes (compile-time; the defaults are the measured best on MI355X).
@@ -66,6 +67,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #endif
 #ifndef MOE_DN_SB
 #define MOE_DN_SB 2
+#endif
+#ifndef MOE_STORE_AUX
+// cache-policy bits of the down GEMM's output stores: sc1 (bit 4), agent
+// scope, writes through this XCD's L2, so the tile's release finds little to
+// write back (measured 3-20% faster than the default policy)
+#define MOE_STORE_AUX 16
 #endif
 #ifndef MOE_LOAD_AUX
 #define MOE_LOAD_AUX 0   // cache-policy bits of the operand loads (default policy measured best)
@@ -568,10 +575,14 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       }
     }
 
-    // epilogue: lane holds rows m = .. + (lane & 31), columns n = .. + 8*(v/4) + 4*(lane/32) + v%4
-    const int mrow0 = row0 + wave_m * C::WM + lrow;
+    // Epilogue.  A lane holds rows wave_m*WM + 32j + (lane & 31) and, per
+    // (i, q), 4 consecutive columns 32i + 8q + 4*(lane/32) of its wave's
+    // block.
     if constexpr (SWIGLU) {
+      // gate/up: h = silu(gate) * up straight from registers, 8 bytes per
+      // lane (staging this 256 x 128 tile through LDS measured 1-4% slower)
       constexpr int HB = C::BN / 2, HW = C::WN / 2;
+      const int mrow0 = row0 + wave_m * C::WM + lrow;
       const int ncol0 = nt * HB + wave_n * HW + 4 * lhalf;
 #pragma unroll
       for (int j = 0; j < C::FM; ++j) {
@@ -598,27 +609,72 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       }
       wait_vm0();
     } else {
-      const int ncol0 = nt * C::BN + wave_n * C::WN + 4 * lhalf;
+      // Down GEMM: stored straight from registers, each store instruction
+      // would touch 32 rows with 8 bytes per lane, i.e. 16-byte pieces of 32
+      // cache lines, and every one of them must be acknowledged before the
+      // tile's release.  The tile goes through LDS instead (the ring is idle
+      // now): every lane writes its bf16 values there, then each thread
+      // stores 16-byte chunks of whole output rows, so a wavefront writes
+      // whole lines.  LDS layout: row-major, BN bf16 per row, the 16-byte
+      // chunk c of row m at c ^ (m mod NCH), so that 16 lanes reading 16
+      // consecutive chunks of one row touch 16 distinct bank groups.
+      constexpr int OUT_TC = C::BN;     // output columns of the tile
+      constexpr int NCH = OUT_TC / 8;   // 16-byte chunks per output row
+      static_assert(C::BM * OUT_TC <= C::LDS_ELEMS, "output tile fits the LDS ring");
+      static_assert((NCH & (NCH - 1)) == 0 && NCH >= 16, "power-of-two chunk count");
+      __syncthreads();   // every wave is done with the ring
+      char* tl = (char*)lds;
 #pragma unroll
       for (int j = 0; j < C::FM; ++j) {
-        const int m = mrow0 + 32 * j;
-        if (m < row_end) {
-          uint16_t* orow = g.out + (int64_t)m * g.out_cols;
-          uint16_t* lrow = recv.p[L.r] + (int64_t)(ldst0 + (m - row0)) * g.out_cols;
+        const int m = wave_m * C::WM + 32 * j + lrow;
 #pragma unroll
-          for (int i = 0; i < C::FN; ++i)
+        for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              uint2 pk;
-              pk.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-              pk.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-              *(uint2*)(orow + ncol0 + 32 * i + 8 * q) = pk;
-              if (ldst0 >= 0) *(uint2*)(lrow + ncol0 + 32 * i + 8 * q) = pk;
-            }
+          for (int q = 0; q < 4; ++q) {
+            uint2 pk;
+            pk.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+            pk.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            const int ch = wave_n * (C::WN / 8) + 4 * i + q;
+            *(uint2*)(tl + m * (OUT_TC * 2) + 16 * (ch ^ (m & (NCH - 1))) + 8 * lhalf) = pk;
+          }
+      }
+      __syncthreads();
+      // rows [row0, row_end) of this tile exist; the store descriptors end
+      // at row_end, so the rows past it are dropped by the buffer bounds
+      const int64_t out_row_bytes = (int64_t)g.out_cols * 2;
+      const int col0 = nt * OUT_TC;
+      const int nrows = row_end - row0;   // > 0 unless the tile is empty
+      if (nrows > 0) {
+        const __amdgpu_buffer_rsrc_t o_rsrc =
+            make_rsrc(g.out + (int64_t)row0 * g.out_cols + col0, (int64_t)nrows * out_row_bytes);
+        __amdgpu_buffer_rsrc_t l_rsrc = o_rsrc;
+        if (ldst0 >= 0)
+          l_rsrc = make_rsrc(recv.p[L.r] + (int64_t)ldst0 * g.out_cols + col0, (int64_t)nrows * out_row_bytes);
+        constexpr int RPP = C::NT / NCH;   // rows per pass
+        constexpr int PASSES = C::BM / RPP;
+        constexpr int UNR = PASSES >= 4 ? 4 : PASSES;
+        static_assert(PASSES % UNR == 0, "whole unrolled passes");
+        const int ch = tid % NCH;
+        const int r_in = tid / NCH;
+        for (int p0 = 0; p0 < PASSES; p0 += UNR) {
+          if ((p0 * RPP) >= nrows) break;
+          v4u32 v[UNR];
+#pragma unroll
+          for (int u = 0; u < UNR; ++u) {
+            const int m = (p0 + u) * RPP + r_in;
+            v[u] = *(const v4u32*)(tl + m * (OUT_TC * 2) + 16 * (ch ^ (m & (NCH - 1))));
+          }
+#pragma unroll
+          for (int u = 0; u < UNR; ++u) {
+            const int m = (p0 + u) * RPP + r_in;
+            const uint32_t off = (uint32_t)((int64_t)m * out_row_bytes + ch * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(v[u], o_rsrc, off, 0, MOE_STORE_AUX);
+            if (ldst0 >= 0) __builtin_amdgcn_raw_buffer_store_b128(v[u], l_rsrc, off, 0, MOE_STORE_AUX);
+          }
         }
       }
-      // every wave's stores have reached L2; then one release at agent scope
-      // (L2 write-back) before the flag of this tile is set
+      // every wave's stores have reached L2; then one release at agent
+      // scope (L2 write-back) before the flags of this tile are set
       wait_vm0();
       if constexpr (FLAGS) {
         __syncthreads();
