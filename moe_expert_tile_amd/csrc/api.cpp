@@ -176,6 +176,15 @@ int prepare(int* dev) {
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// Grid of the standalone consumer: one workgroup per copy unit.  The remote
+// units are known only on the device; Σ_seg ceil(bytes_seg / chunk) is at
+// most R·d·2 / chunk plus one per segment (segments <= bands), and the
+// workgroups past the true count return at once.
+int consumer_grid(const PlanLayout& L) {
+  const int64_t bound = (int64_t)L.R * L.d * 2 / kCopyChunk + L.bands_cap + 1;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(bound, 65535));
+}
+
 void record(void* ev, hipStream_t s) {
   if (ev) (void)hipEventRecord((hipEvent_t)ev, s);
 }
@@ -308,7 +317,7 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
 
   if (o.mode == MOE_MODE_COPY_ONLY) {
     record(o.events[4], st);
-    rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, timeout, o.consumer_blocks ? o.consumer_blocks : 1024,
+    rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, timeout, o.consumer_blocks ? o.consumer_blocks : consumer_grid(L),
                                 st));
     record(o.events[5], st);
     return rc;
@@ -323,7 +332,7 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
     record(o.events[3], st);
     if (rc) return rc;
     record(o.events[4], st);
-    rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, timeout, o.consumer_blocks ? o.consumer_blocks : 1024,
+    rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, timeout, o.consumer_blocks ? o.consumer_blocks : consumer_grid(L),
                                 st));
     record(o.events[5], st);
     return rc;

@@ -14,13 +14,14 @@
 // Memory ordering: the producer stores a tile, releases at agent scope and
 // sets flags[tile] = epoch with an agent-scope store.  Here wave 0 polls the
 // flags with agent-scope loads; every later read of the tile also uses
-// agent-scope loads (they bypass the non-coherent caches of this XCD), so no
-// cache-wide invalidation is issued and the producer's L2 contents on the
-// same XCD survive.
+// agent-scope (sc1) loads, 16 bytes per lane, which bypass the non-coherent
+// caches of this XCD, so no cache-wide invalidation is issued and the
+// producer's L2 contents on the same XCD survive.
 //
 // Work split: each segment is cut into units of kCopyChunk bytes; unit u goes
 // to consumer workgroup u mod n_cons, units in schedule order.  A workgroup
-// waits for a segment once, on its first unit of that segment.  The wait is
+// finds its first unit's segment by binary search and waits for a segment
+// once, on its first unit of that segment.  The wait is
 // bounded: after `timeout` ticks of the 100 MHz constant clock it records
 // MOE_ETIMEOUT in the plan's error word and every consumer workgroup leaves.
 #pragma once
@@ -29,9 +30,19 @@
 
 namespace moe {
 
-__device__ __forceinline__ uint64_t agent_load64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+typedef unsigned int cv4u32 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): accesses past the end read
+// zero and drop their stores (gfx9-family word 3: 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t copy_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
+
+// cache-policy bit sc1 (bit 4): the same agent-scope load an agent-scope
+// atomic load compiles to, so a line cached by this XCD before the
+// producer's release is not returned stale
+constexpr int kAgentLoad = 16;
 
 // One consumer workgroup of NT threads; `cid` in [0, n_cons).  `s_go` is one
 // int of the caller's LDS (the caller's only LDS object, so that the
@@ -51,11 +62,23 @@ __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_
   const int32_t* sunit = ws + L.o_sunit;
   // remote segments come first in schedule order; their units end where the
   // first local segment's begin
-  const int U = sunit[hdr[H_RSEGS]];
+  const int n_rs = hdr[H_RSEGS];
+  const int U = sunit[n_rs];
+  if (cid >= U) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t d = L.d;
   const int tpb = L.dn_tpb;
-  int seg = 0, ready = -1;
+  // segment of this workgroup's first unit: the last s with sunit[s] <= cid
+  int seg = 0;
+  {
+    int lo = 0, hi = n_rs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sunit[mid] <= cid) lo = mid; else hi = mid - 1;
+    }
+    seg = lo;
+  }
+  int ready = -1;
   for (int u = cid; u < U; u += n_cons) {
     while (sunit[seg + 1] <= u) ++seg;
     if (seg != ready) {
@@ -88,36 +111,20 @@ __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_
       if (!go) return;
       ready = seg;
     }
+    // unit u: bytes [lo, lo + kCopyChunk) of the segment, clipped to its end
+    // by the buffer bounds; every load is issued before the first store
     const int64_t bytes = (int64_t)srows[seg] * d * 2;
     const int64_t lo = (int64_t)(u - sunit[seg]) * kCopyChunk;
-    const int64_t hi = min(lo + (int64_t)kCopyChunk, bytes);
-    const uint64_t* src = (const uint64_t*)(y + (int64_t)ssrc[seg] * d);
-    uint4* dst = (uint4*)(recv.p[sdst[seg]] + (int64_t)sdoff[seg] * d);
-    // V vectors of 16 bytes per thread per pass, all loads issued before the stores
-    constexpr int V = 4;
-    for (int64_t off = lo + tid * 16; off < hi; off += (int64_t)NT * 16 * V) {
-      uint64_t a[V], b[V];
+    const int64_t n = min((int64_t)kCopyChunk, bytes - lo);
+    const __amdgpu_buffer_rsrc_t src = copy_rsrc((const char*)(y + (int64_t)ssrc[seg] * d) + lo, n);
+    const __amdgpu_buffer_rsrc_t dst = copy_rsrc((char*)(recv.p[sdst[seg]] + (int64_t)sdoff[seg] * d) + lo, n);
+    constexpr int VPT = kCopyChunk / (NT * 16);   // 16-byte vectors per thread
+    static_assert(VPT >= 1 && VPT * NT * 16 == kCopyChunk, "whole vectors per unit");
+    cv4u32 v[VPT];
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const int64_t o = off + (int64_t)i * NT * 16;
-        if (o < hi) {
-          a[i] = agent_load64(src + o / 8);
-          b[i] = agent_load64(src + o / 8 + 1);
-        }
-      }
+    for (int k = 0; k < VPT; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b128(src, (k * NT + tid) * 16, 0, kAgentLoad);
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const int64_t o = off + (int64_t)i * NT * 16;
-        if (o < hi) {
-          uint4 v;
-          v.x = (uint32_t)a[i];
-          v.y = (uint32_t)(a[i] >> 32);
-          v.z = (uint32_t)b[i];
-          v.w = (uint32_t)(b[i] >> 32);
-          dst[o / 16] = v;
-        }
-      }
-    }
+    for (int k = 0; k < VPT; ++k) __builtin_amdgcn_raw_buffer_store_b128(v[k], dst, (k * NT + tid) * 16, 0, 0);
   }
 }
 
