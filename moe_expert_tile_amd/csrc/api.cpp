@@ -265,9 +265,9 @@ int moe_plan(const moe_shape* s, const int32_t* topk_ids, const uint16_t* x_recv
   if (rc) return rc;
   // the plan builder copies the per-block histograms into LDS only when the
   // whole request fits well inside the device's per-workgroup LDS
-  const int64_t stage_bytes =
-      ((int64_t)build_lds_words(L.W, L.E_l, L.E) + (int64_t)L.NB * (L.E_l + 2) + (int64_t)L.NB_r * L.E) * 4;
-  L.build_stage = stage_bytes <= std::min<int64_t>(g_dev[dev].lds_per_block, kBuildLdsBytes);
+  const int64_t stage_words = (int64_t)build_lds(L.W, L.E_l, L.E, 0, 0, false).total +
+                              (int64_t)L.NB * (L.E_l + 2) + (int64_t)L.NB_r * L.E;
+  L.build_stage = stage_words * 4 <= std::min<int64_t>(g_dev[dev].lds_per_block, kBuildLdsBytes);
   return hip_rc(launch_plan(L, topk_ids, x_recv, (int32_t*)plan_ws, x_layout, (hipStream_t)stream));
 }
 

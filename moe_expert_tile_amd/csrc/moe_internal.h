@@ -10,7 +10,7 @@ namespace moe {
 constexpr int kMaxWorld = 64;
 constexpr int kPairsPerBlock = 512;    // (token, slot) pairs per planner workgroup
 constexpr int kPlanThreads = 256;
-constexpr int kBuildThreads = 1024;    // the single-workgroup plan builder
+constexpr int kBuildThreads = 256;     // the single-workgroup plan builder
 constexpr int kCopyChunk = 32768;      // bytes per consumer copy unit
 constexpr int kGuBM = 256;             // gate/up GEMM tile rows
 constexpr int kGuBN = 256;             // gate/up GEMM tile cols (128 gate + 128 up)
@@ -62,13 +62,41 @@ struct RecvPtrs {
   uint16_t* p[kMaxWorld];
 };
 
-// LDS words of plan_build_kernel: the expert x owner tables and the per-group
-// scratch stay on chip; only the results are written out.
-inline int build_lds_words(int W, int E_l, int E) {
+// LDS carve-out of plan_build_kernel, in int words: the expert x owner tables
+// and the per-group scratch stay on chip, and when `stage` is set the
+// per-block histograms are copied in too.  The host sizes the launch's
+// dynamic LDS with the same function the kernel carves it with.
+struct BuildLds {
+  int c, grp, base, gstart, low, me, rowoff, rb, order, baser, gupre, dnpre, sh, misc;
+  int stage_bh, stage_bhr, total;
+};
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline BuildLds build_lds(int W, int E_l, int E, int NB, int NB_r, bool stage) {
+  BuildLds s;
   const int EW = E_l * W;
-  return 6 * EW + W + 3 * E_l + 1 + E + 64;
+  int o = 0;
+  s.c = o; o += EW;
+  s.grp = o; o += EW;
+  s.base = o; o += EW;
+  s.gstart = o; o += EW + 1;
+  s.low = o; o += W;
+  s.me = o; o += E_l;
+  s.rowoff = o; o += E_l + 1;
+  s.rb = o; o += E_l;
+  s.order = o; o += E_l;
+  s.baser = o; o += E;
+  s.gupre = o; o += E_l + 1;
+  s.dnpre = o; o += 2 * E_l + 1;
+  s.sh = o; o += 16;
+  s.misc = o; o += 8;
+  s.stage_bh = o; if (stage) o += NB * (E_l + 2);
+  s.stage_bhr = o; if (stage) o += NB_r * E;
+  s.total = o;
+  return s;
 }
-constexpr int kBuildLdsBytes = 32 * 1024;   // cap on plan_build's dynamic LDS
+constexpr int kBuildLdsBytes = 64 * 1024;   // cap on plan_build's dynamic LDS (the default dynamic limit)
 
 // host-side helpers (api.cpp)
 bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb,

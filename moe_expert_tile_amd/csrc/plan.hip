@@ -1,18 +1,21 @@
 // Planner: Stage A of the tile-signal notes ("MoE 计算-通信细粒度重叠：用 Tile 级信号把
 // All-to-All 藏在 GEMM 背后", §3 and §4.2-§4.5, segments §5.2), on the device.
 //
-//   K1 plan_count   one workgroup per 2048 (token, slot) pairs of one owner:
+//   K1 plan_count   one workgroup per 512 (token, slot) pairs of one owner:
 //                   LDS histograms of the local experts, of "below this rank's
 //                   experts" (for receive offsets) and, for the rank's own
 //                   tokens, of all experts (for the owner-side slot table).
-//   K2 plan_build   one workgroup: scans over the histograms -> group counts,
-//                   padded group offsets, X_e sizes, rule (ii) expert order,
-//                   band list S (remote bands first), combine plan, segments,
-//                   gate/up tile table, padding entries of src_index.
+//   K2 plan_build   one workgroup of 256 threads: scans over the histograms
+//                   -> group counts, padded group offsets, X_e sizes, rule
+//                   (ii) expert order, band list S (remote bands first),
+//                   combine plan, segments and their copy units, GEMM row-tile
+//                   tables, padding entries of src_index.  Its tables live in
+//                   LDS; nothing it writes to memory is read back.
 //   K3 plan_place   one workgroup per pair block again: stable rank of every
-//                   pair inside its (expert, owner) group with wave ballots +
-//                   LDS carries -> src_index of every real layout row, and the
-//                   owner-side slot of each of the rank's own pairs.
+//                   pair inside its (expert, owner) group with bit-sliced wave
+//                   ballots + LDS carries -> src_index of every real layout
+//                   row, and the owner-side slot of each of the rank's own
+//                   pairs.
 //   K4 plan_gather  one wavefront per layout row: X[row] = x_recv[src] or 0,
 //                   16-byte coalesced loads and stores.
 //
@@ -29,32 +32,65 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Exclusive scan of one int per thread over the whole workgroup.
-__device__ int block_excl_scan(int v, int* sh, int* total) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nw = (blockDim.x + 63) >> 6;
-  int x = v;
+// Inclusive scan over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
+    const int y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
-  if (lane == 63) sh[w] = x;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < nw; ++i) { int t = sh[i]; sh[i] = run; run += t; }
-    sh[32] = run;
+  return x;
+}
+
+// Exclusive scan of a pair of ints per thread over the workgroup (at most
+// kBuildThreads threads): wavefront scans, then every thread adds the totals
+// of the wavefronts below its own (read in parallel from LDS).  `sh` holds
+// 2 ints per wavefront.  Two barriers; `sh` is free again on return.
+__device__ int2 block_scan2(int a, int b, int* sh, int2* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nw = (blockDim.x + 63) >> 6;
+  int xa = a, xb = b;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ya = __shfl_up(xa, off, 64);
+    const int yb = __shfl_up(xb, off, 64);
+    if (lane >= off) {
+      xa += ya;
+      xb += yb;
+    }
+  }
+  if (lane == 63) {
+    sh[2 * w] = xa;
+    sh[2 * w + 1] = xb;
   }
   __syncthreads();
-  int res = sh[w] + x - v;
-  *total = sh[32];
+  int pa = 0, pb = 0, ta = 0, tb = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int u = sh[2 * i], v = sh[2 * i + 1];
+    ta += u;
+    tb += v;
+    if (i < w) {
+      pa += u;
+      pb += v;
+    }
+  }
   __syncthreads();
-  return res;
+  *total = make_int2(ta, tb);
+  return make_int2(pa + xa - a, pb + xb - b);
+}
+
+__device__ __forceinline__ int block_scan(int v, int* sh, int* total) {
+  int2 t;
+  const int2 p = block_scan2(v, 0, sh, &t);
+  *total = t.x;
+  return p.x;
 }
 
 // Exclusive scan over n items: val(i) gives item i, out(i, prefix) receives
-// its exclusive prefix.  Items are split into contiguous per-thread chunks.
+// its exclusive prefix.  Items are split into contiguous per-thread chunks;
+// val(i) is read before out(i) is called, so the scan may work in place.
+// Ends with a barrier: out's LDS writes are visible on return.
 template <class F, class G>
 __device__ int scan_items(int n, F val, G out, int* sh) {
   const int per = (n + blockDim.x - 1) / blockDim.x;
@@ -62,10 +98,44 @@ __device__ int scan_items(int n, F val, G out, int* sh) {
   int local = 0;
   for (int i = lo; i < hi; ++i) local += val(i);
   int total;
-  int run = block_excl_scan(local, sh, &total);
-  for (int i = lo; i < hi; ++i) { int v = val(i); out(i, run); run += v; }
+  int run = block_scan(local, sh, &total);
+  for (int i = lo; i < hi; ++i) { const int v = val(i); out(i, run); run += v; }
   __syncthreads();
   return total;
+}
+
+// The same over pairs: val(i) returns int2 (x, y), out(i, prefix) receives
+// the exclusive int2 prefix.  Returns the int2 totals.
+template <class F, class G>
+__device__ int2 scan_items2(int n, F val, G out, int* sh) {
+  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
+  int la = 0, lb = 0;
+  for (int i = lo; i < hi; ++i) {
+    const int2 v = val(i);
+    la += v.x;
+    lb += v.y;
+  }
+  int2 total;
+  int2 run = block_scan2(la, lb, sh, &total);
+  for (int i = lo; i < hi; ++i) {
+    const int2 v = val(i);
+    out(i, run);
+    run.x += v.x;
+    run.y += v.y;
+  }
+  __syncthreads();
+  return total;
+}
+
+// Largest i in [0, n) with a[i] <= x (a ascending, a[0] <= x).
+__device__ __forceinline__ int upper_index(const int* a, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
 __device__ __forceinline__ int owner_of_block(const PlanLayout& L, int b) {
@@ -112,20 +182,22 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   const int W = L.W, r = L.r, E_l = L.E_l, E = L.E, tb = L.tb_m;
   const int HB = E_l + 2;
   const int EW = E_l * W;
+  const BuildLds S = build_lds(W, E_l, E, L.NB, L.NB_r, L.build_stage != 0);
   int32_t* hdr = ws + L.o_hdr;
-  int* c = smem;                 // [E_l][W]
-  int* grp = c + EW;             // [E_l][W]
-  int* base = grp + EW;          // [W][E_l]
-  int* gstart = base + EW;       // [E_l*W] per-group band start
-  int* gseg = gstart + EW;       // [E_l*W] per-group segment base
-  int* gunit = gseg + EW;        // [E_l*W] per-group copy-unit base
-  int* low = gunit + EW;         // [W]
-  int* me = low + W;             // [E_l]
-  int* rowoff = me + E_l;        // [E_l + 1]
-  int* rb = rowoff + E_l + 1;    // [E_l]
-  int* order = rb + E_l;         // [E_l]
-  int* baser = order + E_l;      // [E]
-  int* sh = baser + E;           // [64] scan scratch
+  int* c = smem + S.c;             // [E_l][W] group sizes
+  int* grp = smem + S.grp;         // [E_l][W] group offsets inside X_e
+  int* base = smem + S.base;       // [W][E_l] receive-buffer bases
+  int* gstart = smem + S.gstart;   // [E_l*W + 1] first band of every group in S order
+  int* low = smem + S.low;         // [W]
+  int* me = smem + S.me;           // [E_l]
+  int* rowoff = smem + S.rowoff;   // [E_l + 1]
+  int* rb = smem + S.rb;           // [E_l]
+  int* order = smem + S.order;     // [E_l]
+  int* baser = smem + S.baser;     // [E]
+  int* gupre = smem + S.gupre;     // [E_l + 1] gate/up row tiles before each expert (rule (ii) order)
+  int* dnpre = smem + S.dnpre;     // [2 E_l + 1] down row tiles before each run
+  int* sh = smem + S.sh;           // scan scratch
+  int* misc = smem + S.misc;       // [0] remote segments
   const int32_t* bh = ws + L.o_bh;
   int32_t* bp = ws + L.o_bp;
   int32_t* brecv = ws + L.o_brecv;
@@ -133,9 +205,9 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   int32_t* bpr = ws + L.o_bpr;
   if (L.build_stage) {
     // the per-block histograms are read many times below: one coalesced
-    // parallel copy into LDS, after the tables (the host sized the LDS for it)
-    int* s_bh = sh + 64;
-    int* s_bhr = s_bh + L.NB * HB;
+    // parallel copy into LDS (the host sized the LDS for it)
+    int* s_bh = smem + S.stage_bh;
+    int* s_bhr = smem + S.stage_bhr;
     for (int i = tid; i < L.NB * HB; i += nt) s_bh[i] = bh[i];
     for (int i = tid; i < L.NB_r * E; i += nt) s_bhr[i] = bhr[i];
     __syncthreads();
@@ -143,11 +215,17 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     bhr = s_bhr;
   }
 
-  // (a) routing errors
-  int bad_local = 0;
-  for (int b = tid; b < L.NB; b += nt) bad_local += bh[(int64_t)b * HB + E_l + 1];
-  int bad_total;
-  (void)block_excl_scan(bad_local, sh, &bad_total);
+  // (a) received-row base of every block (owners in order) and routing
+  //     errors, in one scan over the blocks
+  const int2 rtot = scan_items2(
+      L.NB,
+      [&](int b) {
+        int s = 0;
+        for (int e = 0; e < E_l; ++e) s += bh[(int64_t)b * HB + e];
+        return make_int2(s, bh[(int64_t)b * HB + E_l + 1]);
+      },
+      [&](int b, int2 pre) { brecv[b] = pre.x; }, sh);
+  const int rcount = rtot.x, bad_total = rtot.y;
 
   // (b) group counts c[e][o], low[o], per-block prefixes within each owner
   // (the histogram entries are loaded 8 at a time ahead of the dependent
@@ -167,16 +245,7 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     }
     if (x < E_l) c[x * W + o] = run; else low[o] = run;
   }
-  // (c) received-row base of every block
-  int rcount = scan_items(
-      L.NB,
-      [&](int b) {
-        int s = 0;
-        for (int e = 0; e < E_l; ++e) s += bh[(int64_t)b * HB + e];
-        return s;
-      },
-      [&](int b, int pre) { brecv[b] = pre; }, sh);
-  // (d) the rank's own tokens: per-expert counts and per-block prefixes
+  // (c) the rank's own tokens: per-expert counts and per-block prefixes
   for (int g = tid; g < E; g += nt) {
     int run = 0;
     for (int b0 = 0; b0 < L.NB_r; b0 += 8) {
@@ -194,8 +263,6 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   __syncthreads();
   (void)scan_items(
       E, [&](int g) { return baser[g]; }, [&](int g, int pre) { baser[g] = pre; }, sh);
-  // scan_items reads item g (val) before it calls out(g), so the counts can be
-  // replaced by their prefixes in place
 
   if (bad_total > 0 || rcount != L.R) {
     if (tid == 0) {
@@ -206,7 +273,8 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     return;
   }
 
-  // (e) layout: padded group offsets inside X_e, remote owners ascending then r
+  // (d) layout: padded group offsets inside X_e, remote owners ascending then
+  //     r; receive-buffer bases: owner o's pairs below global expert r*E_l + e
   for (int e = tid; e < E_l; e += nt) {
     int run = 0;
     for (int q = 0; q < W; ++q) {
@@ -217,16 +285,11 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     }
     me[e] = run;
   }
-  // receive-buffer bases: owner o's pairs below global expert r*E_l + e
   for (int o = tid; o < W; o += nt) {
     int run = low[o];
     for (int e = 0; e < E_l; ++e) { base[o * E_l + e] = run; run += c[e * W + o]; }
   }
-  __syncthreads();
-  const int M = scan_items(
-      E_l, [&](int e) { return me[e]; }, [&](int e, int pre) { rowoff[e] = pre; }, sh);
-  if (tid == 0) rowoff[E_l] = M;
-  // remote bands per expert and rule (ii) order: more remote bands first, ties to lower id
+  // remote bands per expert, for rule (ii)
   for (int e = tid; e < E_l; e += nt) {
     int n = 0;
     for (int o = 0; o < W; ++o)
@@ -234,6 +297,9 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     rb[e] = n;
   }
   __syncthreads();
+  const int M = scan_items(
+      E_l, [&](int e) { return me[e]; }, [&](int e, int pre) { rowoff[e] = pre; }, sh);
+  // rule (ii) order: more remote bands first, ties to the lower id
   for (int e = tid; e < E_l; e += nt) {
     int rank = 0;
     const int mine = rb[e];
@@ -243,9 +309,10 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     }
     order[rank] = e;
   }
+  if (tid == 0) rowoff[E_l] = M;
   __syncthreads();
 
-  // (f) groups in schedule order: remote groups of experts in rule (ii) order
+  // (e) groups in schedule order: remote groups of experts in rule (ii) order
   //     (owners ascending, r skipped), then the local group of every expert.
   const int NGR = E_l * (W - 1);
   const int NG = E_l * W;
@@ -259,36 +326,28 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
       o = r;
     }
   };
-  auto group_nb = [&](int gi) {
-    int e, o;
-    group_eo(gi, e, o);
-    return (c[e * W + o] + tb - 1) / tb;
-  };
-  const int B = scan_items(NG, group_nb, [&](int gi, int pre) { gstart[gi] = pre; }, sh);
-  int nrem_local = 0;
-  for (int gi = tid; gi < NGR; gi += nt) nrem_local += group_nb(gi);
-  int n_remote;
-  (void)block_excl_scan(nrem_local, sh, &n_remote);
+  const int B = scan_items(
+      NG,
+      [&](int gi) {
+        int e, o;
+        group_eo(gi, e, o);
+        return (c[e * W + o] + tb - 1) / tb;
+      },
+      [&](int gi, int pre) { gstart[gi] = pre; }, sh);
   if (B > L.bands_cap) {
     if (tid == 0) { hdr[H_ERROR] = 2; for (int i = 1; i < H_WORDS; ++i) hdr[i] = 0; }
     return;
   }
+  const int n_remote = NGR < NG ? gstart[NGR] : B;
+  // band s belongs to the last group whose first band is <= s (never empty)
+  auto group_of = [&](int band) { return upper_index(gstart, NG, band); };
 
-  // (g) bands in S order, one thread per band.  Band s belongs to the last
-  //     group whose first band is <= s (that group is never empty).
+  // (f) bands in S order, one thread per band
   int32_t* bexp = ws + L.o_bexp;
   int32_t* bdst = ws + L.o_bdst;
   int32_t* bsrc = ws + L.o_bsrc;
   int32_t* bdoff = ws + L.o_bdoff;
   int32_t* bval = ws + L.o_bval;
-  auto group_of = [&](int band) {
-    int lo = 0, hi = NG - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (gstart[mid] <= band) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-  };
   for (int b = tid; b < B; b += nt) {
     const int gi = group_of(b);
     int e, o;
@@ -300,27 +359,37 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     bdoff[b] = base[o * E_l + e] + q * tb;
     bval[b] = min(tb, c[e * W + o] - q * tb);
   }
-  __syncthreads();   // the band arrays are read back below
 
-  // segments (§5.2): the first and the last remote band alone; otherwise runs
-  // of <= mgb bands that restart at every group boundary.  Every band decides
-  // whether it starts a segment; a scan numbers the starts; each segment then
-  // reads its fields off its first band (segments never cross a group, so the
-  // first band's destination offset and source row are the segment's) and
-  // sums its <= 64 bands' valid rows; a second scan places the copy units.
+  // (g) segments (§5.2): the first and the last remote band alone; otherwise
+  //     runs of <= mgb bands that restart at every group boundary.  Every band
+  //     decides whether it starts a segment and, if so, the segment's length,
+  //     rows and copy units (a segment never crosses a group, so it is read off
+  //     the group); one scan over the bands numbers the segments and places
+  //     their copy units.
   const int mgb = L.mgb;
-  auto starts_segment = [&](int b) {
-    const int gi = group_of(b);
+  auto starts_segment = [&](int b, int gi) {
     const int gs = gstart[gi];
-    if (b == gs) return 1;
+    if (b == gs) return true;
     if (gi < NGR) {
-      if (b == n_remote - 1) return 1;
+      if (b == n_remote - 1) return true;
       const int run0 = gs > 1 ? gs : 1;
-      return ((b - run0) % mgb) == 0 ? 1 : 0;
+      return ((b - run0) % mgb) == 0;
     }
-    return ((b - gs) % mgb) == 0 ? 1 : 0;
+    return ((b - gs) % mgb) == 0;
   };
   const int64_t row_bytes = (int64_t)L.d * 2;
+  // (starts, units, bands, rows) of band b
+  auto seg_of = [&](int b, int& nb, int& rows) {
+    const int gi = group_of(b);
+    if (!starts_segment(b, gi)) return false;
+    const int ge = gstart[gi + 1];   // the group's end
+    nb = 1;
+    while (b + nb < ge && !starts_segment(b + nb, gi)) ++nb;
+    int e, o;
+    group_eo(gi, e, o);
+    rows = min(nb * tb, c[e * W + o] - (b - gstart[gi]) * tb);
+    return true;
+  };
   auto units_of = [&](int rows) { return (int)((rows * row_bytes + kCopyChunk - 1) / kCopyChunk); };
   int32_t* sfirst = ws + L.o_sfirst;
   int32_t* snb = ws + L.o_snb;
@@ -329,36 +398,43 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   int32_t* ssrc = ws + L.o_ssrc;
   int32_t* srows = ws + L.o_srows;
   int32_t* sunit = ws + L.o_sunit;
-  int* s_nrsegs = gseg;   // one LDS word (the per-group table is not needed)
-  if (tid == 0) *s_nrsegs = -1;
+  if (tid == 0) {
+    gstart[NG] = B;
+    misc[0] = -1;
+  }
   __syncthreads();
-  const int NS = scan_items(
-      B, starts_segment,
-      [&](int b, int pre) {
-        if (starts_segment(b)) sfirst[pre] = b;
-        if (b == n_remote) *s_nrsegs = pre;   // the first local band starts a segment
+  const int2 stot = scan_items2(
+      B,
+      [&](int b) {
+        int nb, rows;
+        if (!seg_of(b, nb, rows)) return make_int2(0, 0);
+        return make_int2(1, units_of(rows));
+      },
+      [&](int b, int2 pre) {
+        int nb, rows;
+        if (!seg_of(b, nb, rows)) return;
+        const int i = pre.x;
+        const int gi = group_of(b);
+        int e, o;
+        group_eo(gi, e, o);
+        const int q = b - gstart[gi];
+        sfirst[i] = b;
+        snb[i] = nb;
+        sdst[i] = o;
+        sdoff[i] = base[o * E_l + e] + q * tb;
+        ssrc[i] = rowoff[e] + grp[e * W + o] + q * tb;
+        srows[i] = rows;
+        sunit[i] = pre.y;
+        if (b == n_remote) misc[0] = i;   // the first local band starts a segment
       },
       sh);
-  const int n_rsegs = (*s_nrsegs >= 0) ? *s_nrsegs : NS;
-  for (int i = tid; i < NS; i += nt) {
-    const int b0 = sfirst[i];
-    const int b1 = (i + 1 < NS) ? sfirst[i + 1] : B;
-    int rows = 0;
-    for (int b = b0; b < b1; ++b) rows += bval[b];
-    snb[i] = b1 - b0;
-    sdst[i] = bdst[b0];
-    sdoff[i] = bdoff[b0];
-    ssrc[i] = bsrc[b0];
-    srows[i] = rows;
-  }
-  __syncthreads();   // srows is read back by the scan
-  const int U = scan_items(
-      NS, [&](int i) { return units_of(srows[i]); }, [&](int i, int pre) { sunit[i] = pre; }, sh);
+  const int NS = stot.x, U = stot.y;
+  const int n_rsegs = misc[0] >= 0 ? misc[0] : NS;
   if (tid == 0) sunit[NS] = U;
 
-  // (h) padding entries of src_index: the tail of every remote group
+  // (h) padding entries of src_index: the tail of every remote group, one
+  //     wavefront per group, its lanes over the group's (< tb) pad rows
   int32_t* src = ws + L.o_src;
-  // one wavefront per group, its lanes over the group's (< tb) pad rows
   {
     const int wv = tid >> 6, nwv = nt >> 6, ln = tid & 63;
     for (int gi = wv; gi < NGR; gi += nwv) {
@@ -371,29 +447,27 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     }
   }
 
-  // (i) gate/up m-tiles: every X_e cut into kGuBM-row tiles, experts in order
+  // (i) gate/up m-tiles: every X_e cut into kGuBM-row tiles, experts in
+  //     rule (ii) order; one thread per tile
   int32_t* mt_row = ws + L.o_gumt_row;
   int32_t* mt_exp = ws + L.o_gumt_exp;
   const int NMT = scan_items(
       E_l, [&](int q) { return (me[order[q]] + kGuBM - 1) / kGuBM; },
-      [&](int q, int pre) {
-        const int e = order[q];
-        const int n = (me[e] + kGuBM - 1) / kGuBM;
-        for (int i = 0; i < n; ++i) {
-          mt_row[pre + i] = rowoff[e] + i * kGuBM;
-          mt_exp[pre + i] = e;
-        }
-      },
-      sh);
+      [&](int q, int pre) { gupre[q] = pre; }, sh);
+  for (int t = tid; t < NMT; t += nt) {
+    const int q = upper_index(gupre, E_l, t);
+    const int e = order[q];
+    mt_row[t] = rowoff[e] + (t - gupre[q]) * kGuBM;
+    mt_exp[t] = e;
+  }
 
   // (j) down m-tiles, when tb_M divides 256: the runs of row-contiguous
   //     bands in S order -- the remote bands of each expert (its remote
   //     groups follow one another at the start of X_e), then the local bands
-  //     of each expert -- cut into tiles of at most dn_merge bands
+  //     of each expert -- cut into tiles of at most dn_merge bands; one
+  //     thread per tile
   int NDT = B * L.dn_sub;
-  int* s_ndt_r = gunit;   // one LDS word: down row tiles of the remote runs
-  if (tid == 0) *s_ndt_r = n_remote * L.dn_sub;
-  __syncthreads();
+  int ndt_r = n_remote * L.dn_sub;
   if (L.dn_merge > 0) {
     const int P = L.dn_merge;
     int32_t* dt_row = ws + L.o_dnt_row;
@@ -420,18 +494,18 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
           run_of(q, e, first, nb, row0);
           return (nb + P - 1) / P;
         },
-        [&](int q, int pre) {
-          if (q == E_l) *s_ndt_r = pre;   // the remote runs come first
-          int e, first, nb, row0;
-          run_of(q, e, first, nb, row0);
-          for (int j = 0; j * P < nb; ++j) {
-            dt_row[pre + j] = row0 + j * P * tb;
-            dt_exp[pre + j] = e;
-            dt_band[pre + j] = first + j * P;
-            dt_nb[pre + j] = min(P, nb - j * P);
-          }
-        },
-        sh);
+        [&](int q, int pre) { dnpre[q] = pre; }, sh);
+    ndt_r = dnpre[E_l];   // the remote runs come first
+    for (int t = tid; t < NDT; t += nt) {
+      const int q = upper_index(dnpre, 2 * E_l, t);
+      int e, first, nb, row0;
+      run_of(q, e, first, nb, row0);
+      const int j = t - dnpre[q];
+      dt_row[t] = row0 + j * P * tb;
+      dt_exp[t] = e;
+      dt_band[t] = first + j * P;
+      dt_nb[t] = min(P, nb - j * P);
+    }
   }
 
   // results used by later kernels and by inspection
@@ -461,25 +535,35 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     hdr[H_RCOUNT] = rcount;
     hdr[H_GU_MT] = NMT;
     hdr[H_DN_MT] = NDT;
-    hdr[H_DN_MT_R] = *s_ndt_r;
+    hdr[H_DN_MT_R] = ndt_r;
   }
 }
 
-// in-wave stable rank of `v` among lanes holding the same value (v >= 0);
-// the lowest lane of each value writes the wave's count into cnt[v]
-__device__ __forceinline__ int wave_match_rank(int v, int* cnt) {
+// In-wave stable rank of `v` among the lanes holding the same value
+// (v in [0, 2^bits); lanes with v < 0 take no part): the lanes with equal
+// values are found with one ballot per bit of v (a lane keeps the lanes that
+// agree with it on every bit), so the cost is `bits` ballots whatever the
+// number of distinct values.  The lowest lane of each value writes the wave's
+// count of that value into cnt[v].
+__device__ __forceinline__ int wave_match_rank(int v, int bits, int* cnt) {
   const int lane = threadIdx.x & 63;
-  uint64_t todo = __ballot(v >= 0);
-  int rank = 0;
-  while (todo) {
-    const int leader = __ffsll((long long)todo) - 1;
-    const int lv = __shfl(v, leader, 64);
-    const uint64_t m = __ballot(v == lv);
-    if (v == lv) rank = __popcll(m & lanes_below(lane));
-    if (lane == leader) cnt[lv] = __popcll(m);
-    todo &= ~m;
+  uint64_t same = __ballot(v >= 0);
+  for (int i = 0; i < bits; ++i) {
+    const bool bit = (v >> i) & 1;
+    const uint64_t ones = __ballot(bit);
+    same &= bit ? ones : ~ones;
   }
+  if (v < 0) return 0;
+  const int rank = __popcll(same & lanes_below(lane));
+  if (rank == 0) cnt[v] = __popcll(same);
   return rank;
+}
+
+// bits needed for values in [0, n)
+__device__ __forceinline__ int bits_for(int n) {
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_place_kernel(PlanLayout L, const int32_t* __restrict__ topk,
@@ -513,14 +597,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_place_kernel(PlanLayout L, 
   const int32_t* baser = ws + L.o_baser;
   int32_t* pos = ws + L.o_pos;
   const int lo = L.r * E_l;
+  const int bits_e = bits_for(E_l + 1), bits_g = bits_for(E);
   for (int p_base = p0; p_base < p1; p_base += blockDim.x) {
     const int p = p_base + tid;
     const int g = (p < p1) ? topk[p] : -1;
     const int e = (g >= lo && g < lo + E_l) ? g - lo : -1;
-    const int re = wave_match_rank(e, wc + w * NX);
-    const int rl = wave_match_rank(e >= 0 ? E_l : -1, wc + w * NX);
+    const int re = wave_match_rank(e, bits_e, wc + w * NX);
+    const int rl = wave_match_rank(e >= 0 ? E_l : -1, bits_e, wc + w * NX);
     int rg = 0;
-    if (own) rg = wave_match_rank((g >= 0 && g < E) ? g : -1, wc_g + w * E);
+    if (own) rg = wave_match_rank((g >= 0 && g < E) ? g : -1, bits_g, wc_g + w * E);
     __syncthreads();
     if (e >= 0) {
       int rank_e = run[e] + re, rank_l = run[E_l] + rl;
@@ -581,7 +666,7 @@ hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t*
     const size_t sh_count = (size_t)(L.E_l + 2 + L.E) * sizeof(int);
     hipLaunchKernelGGL(plan_count_kernel, dim3(L.NB), dim3(kPlanThreads), sh_count, s, L, topk, ws);
   }
-  const int words = build_lds_words(L.W, L.E_l, L.E) + (L.build_stage ? L.NB * (L.E_l + 2) + L.NB_r * L.E : 0);
+  const int words = build_lds(L.W, L.E_l, L.E, L.NB, L.NB_r, L.build_stage != 0).total;
   hipLaunchKernelGGL(plan_build_kernel, dim3(1), dim3(kBuildThreads), (size_t)words * sizeof(int), s, L, ws);
   if (L.NB > 0) {
     const int nw = kPlanThreads / 64;
