@@ -67,7 +67,7 @@ struct RecvPtrs {
 // per-block histograms are copied in too.  The host sizes the launch's
 // dynamic LDS with the same function the kernel carves it with.
 struct BuildLds {
-  int c, grp, base, gstart, low, me, rowoff, rb, order, baser, gupre, dnpre, sh, misc;
+  int c, grp, base, gstart, low, me, rowoff, rb, order, baser, gupre, dnpre, pad_st, pad_ct, sh, misc;
   int stage_bh, stage_bhr, total;
 };
 #if defined(__HIPCC__)
@@ -89,6 +89,8 @@ inline BuildLds build_lds(int W, int E_l, int E, int NB, int NB_r, bool stage) {
   s.baser = o; o += E;
   s.gupre = o; o += E_l + 1;
   s.dnpre = o; o += 2 * E_l + 1;
+  s.pad_st = o; o += EW;
+  s.pad_ct = o; o += EW;
   s.sh = o; o += 16;
   s.misc = o; o += 8;
   s.stage_bh = o; if (stage) o += NB * (E_l + 2);

@@ -32,14 +32,16 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Inclusive scan over the 64 lanes of a wavefront.
+// Inclusive scan over the 64 lanes of a wavefront with DPP row shifts (scan
+// within each row of 16 lanes) and row broadcasts (lane 15 into the next row,
+// lane 31 into rows 2 and 3); disabled or out-of-row source lanes add 0.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 (rows 1, 3)
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 (rows 2, 3)
   return x;
 }
 
@@ -50,16 +52,7 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 __device__ int2 block_scan2(int a, int b, int* sh, int2* total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nw = (blockDim.x + 63) >> 6;
-  int xa = a, xb = b;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int ya = __shfl_up(xa, off, 64);
-    const int yb = __shfl_up(xb, off, 64);
-    if (lane >= off) {
-      xa += ya;
-      xb += yb;
-    }
-  }
+  const int xa = wave_incl_scan(a), xb = wave_incl_scan(b);
   if (lane == 63) {
     sh[2 * w] = xa;
     sh[2 * w + 1] = xb;
@@ -208,8 +201,18 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     // parallel copy into LDS (the host sized the LDS for it)
     int* s_bh = smem + S.stage_bh;
     int* s_bhr = smem + S.stage_bhr;
-    for (int i = tid; i < L.NB * HB; i += nt) s_bh[i] = bh[i];
-    for (int i = tid; i < L.NB_r * E; i += nt) s_bhr[i] = bhr[i];
+    auto stage = [&](int* dst, const int32_t* src, int n) {
+      for (int i0 = tid; i0 < n; i0 += 8 * nt) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (i0 + u * nt < n) ? src[i0 + u * nt] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u * nt < n) dst[i0 + u * nt] = v[u];
+      }
+    };
+    stage(s_bh, bh, L.NB * HB);
+    stage(s_bhr, bhr, L.NB_r * E);
     __syncthreads();
     bh = s_bh;
     bhr = s_bhr;
@@ -339,58 +342,65 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     return;
   }
   const int n_remote = NGR < NG ? gstart[NGR] : B;
-  // band s belongs to the last group whose first band is <= s (never empty)
-  auto group_of = [&](int band) { return upper_index(gstart, NG, band); };
 
-  // (f) bands in S order, one thread per band
+  // (f) bands in S order, one thread per group (a group's bands are
+  //     consecutive in S), and the padding rows of every remote group
   int32_t* bexp = ws + L.o_bexp;
   int32_t* bdst = ws + L.o_bdst;
   int32_t* bsrc = ws + L.o_bsrc;
   int32_t* bdoff = ws + L.o_bdoff;
   int32_t* bval = ws + L.o_bval;
-  for (int b = tid; b < B; b += nt) {
-    const int gi = group_of(b);
+  int* pad_st = smem + S.pad_st;
+  int* pad_ct = smem + S.pad_ct;
+  for (int gi = tid; gi < NG; gi += nt) {
     int e, o;
     group_eo(gi, e, o);
-    const int q = b - gstart[gi];
-    bexp[b] = e;
-    bdst[b] = o;
-    bsrc[b] = rowoff[e] + grp[e * W + o] + q * tb;
-    bdoff[b] = base[o * E_l + e] + q * tb;
-    bval[b] = min(tb, c[e * W + o] - q * tb);
+    const int n = c[e * W + o];
+    const int nb = (n + tb - 1) / tb;
+    const int gs = gstart[gi];
+    const int rowb = rowoff[e] + grp[e * W + o];
+    const int dstb = base[o * E_l + e];
+    for (int q = 0; q < nb; ++q) {
+      bexp[gs + q] = e;
+      bdst[gs + q] = o;
+      bsrc[gs + q] = rowb + q * tb;
+      bdoff[gs + q] = dstb + q * tb;
+      bval[gs + q] = min(tb, n - q * tb);
+    }
+    if (gi < NGR) {
+      pad_st[gi] = rowb + n;
+      pad_ct[gi] = nb * tb - n;
+    }
   }
 
   // (g) segments (§5.2): the first and the last remote band alone; otherwise
-  //     runs of <= mgb bands that restart at every group boundary.  Every band
-  //     decides whether it starts a segment and, if so, the segment's length,
-  //     rows and copy units (a segment never crosses a group, so it is read off
-  //     the group); one scan over the bands numbers the segments and places
-  //     their copy units.
+  //     runs of <= mgb bands that restart at every group boundary.  A segment
+  //     never crosses a group, so each group's thread walks its bands; one
+  //     scan over the groups numbers the segments and places their copy
+  //     units.
   const int mgb = L.mgb;
-  auto starts_segment = [&](int b, int gi) {
-    const int gs = gstart[gi];
-    if (b == gs) return true;
-    if (gi < NGR) {
-      if (b == n_remote - 1) return true;
-      const int run0 = gs > 1 ? gs : 1;
-      return ((b - run0) % mgb) == 0;
-    }
-    return ((b - gs) % mgb) == 0;
-  };
   const int64_t row_bytes = (int64_t)L.d * 2;
-  // (starts, units, bands, rows) of band b
-  auto seg_of = [&](int b, int& nb, int& rows) {
-    const int gi = group_of(b);
-    if (!starts_segment(b, gi)) return false;
-    const int ge = gstart[gi + 1];   // the group's end
-    nb = 1;
-    while (b + nb < ge && !starts_segment(b + nb, gi)) ++nb;
+  auto units_of = [&](int rows) { return (int)((rows * row_bytes + kCopyChunk - 1) / kCopyChunk); };
+  // calls f(first band, bands, rows) for every segment of group gi, in order
+  auto walk_segments = [&](int gi, auto&& f) {
     int e, o;
     group_eo(gi, e, o);
-    rows = min(nb * tb, c[e * W + o] - (b - gstart[gi]) * tb);
-    return true;
+    const int n = c[e * W + o];
+    const int gs = gstart[gi], ge = gs + (n + tb - 1) / tb;
+    const bool remote = gi < NGR;
+    const int run0 = gs > 1 ? gs : 1;
+    auto starts = [&](int b) {
+      if (b == gs) return true;
+      if (remote) return b == n_remote - 1 || ((b - run0) % mgb) == 0;
+      return ((b - gs) % mgb) == 0;
+    };
+    for (int b = gs; b < ge;) {
+      int nb = 1;
+      while (b + nb < ge && !starts(b + nb)) ++nb;
+      f(b, nb, min(nb * tb, n - (b - gs) * tb), e, o);
+      b += nb;
+    }
   };
-  auto units_of = [&](int rows) { return (int)((rows * row_bytes + kCopyChunk - 1) / kCopyChunk); };
   int32_t* sfirst = ws + L.o_sfirst;
   int32_t* snb = ws + L.o_snb;
   int32_t* sdst = ws + L.o_sdst;
@@ -398,52 +408,54 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   int32_t* ssrc = ws + L.o_ssrc;
   int32_t* srows = ws + L.o_srows;
   int32_t* sunit = ws + L.o_sunit;
-  if (tid == 0) {
-    gstart[NG] = B;
-    misc[0] = -1;
-  }
-  __syncthreads();
+  __syncthreads();   // pad tables
   const int2 stot = scan_items2(
-      B,
-      [&](int b) {
-        int nb, rows;
-        if (!seg_of(b, nb, rows)) return make_int2(0, 0);
-        return make_int2(1, units_of(rows));
+      NG,
+      [&](int gi) {
+        int ns = 0, nu = 0;
+        walk_segments(gi, [&](int, int, int rows, int, int) {
+          ++ns;
+          nu += units_of(rows);
+        });
+        return make_int2(ns, nu);
       },
-      [&](int b, int2 pre) {
-        int nb, rows;
-        if (!seg_of(b, nb, rows)) return;
-        const int i = pre.x;
-        const int gi = group_of(b);
-        int e, o;
-        group_eo(gi, e, o);
-        const int q = b - gstart[gi];
-        sfirst[i] = b;
-        snb[i] = nb;
-        sdst[i] = o;
-        sdoff[i] = base[o * E_l + e] + q * tb;
-        ssrc[i] = rowoff[e] + grp[e * W + o] + q * tb;
-        srows[i] = rows;
-        sunit[i] = pre.y;
-        if (b == n_remote) misc[0] = i;   // the first local band starts a segment
+      [&](int gi, int2 pre) {
+        if (gi == NGR) misc[0] = pre.x;   // the remote segments come first
+        int i = pre.x, u = pre.y;
+        walk_segments(gi, [&](int b, int nb, int rows, int e, int o) {
+          const int q = b - gstart[gi];
+          sfirst[i] = b;
+          snb[i] = nb;
+          sdst[i] = o;
+          sdoff[i] = base[o * E_l + e] + q * tb;
+          ssrc[i] = rowoff[e] + grp[e * W + o] + q * tb;
+          srows[i] = rows;
+          sunit[i] = u;
+          ++i;
+          u += units_of(rows);
+        });
       },
       sh);
   const int NS = stot.x, U = stot.y;
-  const int n_rsegs = misc[0] >= 0 ? misc[0] : NS;
+  const int n_rsegs = misc[0];
   if (tid == 0) sunit[NS] = U;
 
-  // (h) padding entries of src_index: the tail of every remote group, one
-  //     wavefront per group, its lanes over the group's (< tb) pad rows
+  // (h) padding entries of src_index: one wavefront per remote group, its
+  //     lanes over the group's (< tb) pad rows; four groups' extents are read
+  //     at a time
   int32_t* src = ws + L.o_src;
   {
     const int wv = tid >> 6, nwv = nt >> 6, ln = tid & 63;
-    for (int gi = wv; gi < NGR; gi += nwv) {
-      int e, o;
-      group_eo(gi, e, o);
-      const int n = c[e * W + o];
-      const int padded = ((n + tb - 1) / tb) * tb;
-      const int row0 = rowoff[e] + grp[e * W + o];
-      for (int q = n + ln; q < padded; q += 64) src[row0 + q] = -1;
+    for (int g0 = 4 * wv; g0 < NGR; g0 += 4 * nwv) {
+      int st[4], ct[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        st[u] = (g0 + u < NGR) ? pad_st[g0 + u] : 0;
+        ct[u] = (g0 + u < NGR) ? pad_ct[g0 + u] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        for (int q = ln; q < ct[u]; q += 64) src[st[u] + q] = -1;
     }
   }
 
