@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--mode", default="overlap", choices=["overlap", "serial"])
-    ap.add_argument("--consumer-cus", type=int, default=32)
+    ap.add_argument("--consumer-cus", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",

@@ -114,7 +114,7 @@ enum {
 
 typedef struct moe_combine_opts {
   int32_t mode;             /* MOE_MODE_* */
-  int32_t consumer_cus;     /* OVERLAP: CUs given to the consumer, multiple of 8 in [8, 128]; 0 = 32 */
+  int32_t consumer_cus;     /* OVERLAP: CUs given to the consumer, multiple of 8 in [8, 128]; 0 = 16 */
   int32_t consumer_blocks;  /* workgroups of the consumer; 0 = consumer_cus (OVERLAP) or one per
                                32 KiB copy unit, bounded on the host (SERIAL, COPY_ONLY) */
   int32_t reserved;
@@ -178,7 +178,11 @@ int moe_plan(const moe_shape* shape, const int32_t* topk_ids, const uint16_t* x_
  *   opts       may be NULL (OVERLAP, defaults).
  * Every mode runs on `stream` alone.  OVERLAP launches the down GEMM with
  * consumer_blocks extra workgroups past its producers; they take the last
- * CUs to be filled and copy while the producers compute.
+ * CUs to be filled and copy while the producers compute.  Copy units are
+ * claimed in schedule order from a counter in the plan header; producers
+ * that run out of tiles claim units too, once every producer has started.
+ * The plan header's claim counters are reset by the gate/up launch of the
+ * same call, so two calls on one plan workspace must not overlap.
  */
 int moe_expert_combine(const moe_shape* shape, const void* plan_ws, const uint16_t* x_layout,
                        const uint16_t* w_gate_up, const uint16_t* w_down,

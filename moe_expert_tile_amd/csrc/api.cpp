@@ -280,7 +280,7 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
   if (o.mode < MOE_MODE_OVERLAP || o.mode > MOE_MODE_COPY_ONLY) return MOE_EINVAL;
-  if (o.consumer_cus == 0) o.consumer_cus = 32;
+  if (o.consumer_cus == 0) o.consumer_cus = 16;
   if (o.consumer_cus < 8 || o.consumer_cus > 128 || o.consumer_cus % 8 != 0) return MOE_EINVAL;
   if (o.consumer_blocks < 0 || o.consumer_blocks > 65536) return MOE_EINVAL;
   if (o.spin_timeout_ns < 0) return MOE_EINVAL;

@@ -18,12 +18,15 @@
 // caches of this XCD, so no cache-wide invalidation is issued and the
 // producer's L2 contents on the same XCD survive.
 //
-// Work split: each segment is cut into units of kCopyChunk bytes; unit u goes
-// to consumer workgroup u mod n_cons, units in schedule order.  A workgroup
-// finds its first unit's segment by binary search and waits for a segment
-// once, on its first unit of that segment.  The wait is
-// bounded: after `timeout` ticks of the 100 MHz constant clock it records
-// MOE_ETIMEOUT in the plan's error word and every consumer workgroup leaves.
+// Work split: each segment is cut into units of kCopyChunk bytes, numbered
+// in schedule order.  The standalone consumer kernel gives unit u to
+// workgroup u mod n_cons.  In the overlapped down-GEMM launch the units are
+// claimed from a counter in schedule order, by the launch's consumer
+// workgroups and by producers that have run out of tiles (consume_claimed).
+// A workgroup waits for a segment once, on its first unit of that segment.
+// The wait is bounded: after `timeout` ticks of the 100 MHz constant clock it
+// records MOE_ETIMEOUT in the plan's error word and every consumer workgroup
+// leaves.
 #pragma once
 
 #include "moe_internal.h"
@@ -44,9 +47,85 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t copy_rsrc(const void* base, in
 // producer's release is not returned stale
 constexpr int kAgentLoad = 16;
 
-// One consumer workgroup of NT threads; `cid` in [0, n_cons).  `s_go` is one
-// int of the caller's LDS (the caller's only LDS object, so that the
-// compiler's LDS-DMA wait tracking in the GEMM stays exact).
+// Segment of copy unit u, searching forward from `seg` (units only grow):
+// a few steps ahead, then a binary search over the rest.
+__device__ __forceinline__ int segment_of_unit(const int32_t* sunit, int n_rs, int seg, int u) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (sunit[seg + 1] > u) return seg;
+    ++seg;
+  }
+  int lo = seg, hi = n_rs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sunit[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Wave 0 waits until every tile flag of segment `seg` equals `epoch`
+// (bounded by `timeout` ticks of the 100 MHz clock; on timeout the plan's
+// error word becomes MOE_ETIMEOUT); returns 0 if the workgroup must stop.
+// Every thread of the workgroup calls it.
+__device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, const int32_t* sfirst,
+                                            const int32_t* snb, const uint32_t* __restrict__ flags, uint32_t epoch,
+                                            int64_t timeout, int seg, int* s_go) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int tpb = L.dn_tpb;
+  if (tid < 64) {
+    const int f0 = sfirst[seg] * tpb, f1 = (sfirst[seg] + snb[seg]) * tpb;
+    const uint64_t t0 = wall_clock64();
+    int go = 1;
+    for (;;) {
+      bool ok = true;
+      for (int i = f0 + lane; i < f1; i += 64)
+        ok &= (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch);
+      if (__ballot(!ok) == 0) break;
+      if ((int64_t)(wall_clock64() - t0) > timeout) {
+        if (lane == 0)
+          __hip_atomic_store(hdr + H_ERROR, 4 /* MOE_ETIMEOUT */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        go = 0;
+        break;
+      }
+      if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        go = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (lane == 0) *s_go = go;
+  }
+  __syncthreads();
+  const int go = *s_go;
+  __syncthreads();
+  return go;
+}
+
+// Copy unit u of segment seg: bytes [lo, lo + kCopyChunk) of the segment,
+// clipped to its end by the buffer bounds, every load before the first store.
+template <int NT>
+__device__ __forceinline__ void copy_unit(const PlanLayout& L, const int32_t* ssrc, const int32_t* sdst,
+                                          const int32_t* sdoff, const int32_t* srows, const int32_t* sunit,
+                                          const uint16_t* __restrict__ y, const RecvPtrs& recv, int seg, int u) {
+  const int tid = threadIdx.x;
+  const int64_t d = L.d;
+  const int64_t bytes = (int64_t)srows[seg] * d * 2;
+  const int64_t lo = (int64_t)(u - sunit[seg]) * kCopyChunk;
+  const int64_t n = min((int64_t)kCopyChunk, bytes - lo);
+  const __amdgpu_buffer_rsrc_t src = copy_rsrc((const char*)(y + (int64_t)ssrc[seg] * d) + lo, n);
+  const __amdgpu_buffer_rsrc_t dst = copy_rsrc((char*)(recv.p[sdst[seg]] + (int64_t)sdoff[seg] * d) + lo, n);
+  constexpr int VPT = kCopyChunk / (NT * 16);
+  static_assert(VPT >= 1 && VPT * NT * 16 == kCopyChunk, "whole vectors per unit");
+  cv4u32 v[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b128(src, (k * NT + tid) * 16, 0, kAgentLoad);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) __builtin_amdgcn_raw_buffer_store_b128(v[k], dst, (k * NT + tid) * 16, 0, 0);
+}
+
+// One consumer workgroup of NT threads; `cid` in [0, n_cons), units assigned
+// statically (standalone consumer kernel).  `s_go` is one int of the
+// caller's LDS.
 template <int NT>
 __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_t* __restrict__ y,
                                  const uint32_t* __restrict__ flags, uint32_t epoch, const RecvPtrs& recv,
@@ -65,66 +144,67 @@ __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_
   const int n_rs = hdr[H_RSEGS];
   const int U = sunit[n_rs];
   if (cid >= U) return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int64_t d = L.d;
-  const int tpb = L.dn_tpb;
-  // segment of this workgroup's first unit: the last s with sunit[s] <= cid
-  int seg = 0;
-  {
-    int lo = 0, hi = n_rs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sunit[mid] <= cid) lo = mid; else hi = mid - 1;
-    }
-    seg = lo;
-  }
-  int ready = -1;
+  int seg = 0, ready = -1;
   for (int u = cid; u < U; u += n_cons) {
-    while (sunit[seg + 1] <= u) ++seg;
+    seg = segment_of_unit(sunit, n_rs, seg, u);
     if (seg != ready) {
-      if (tid < 64) {
-        const int f0 = sfirst[seg] * tpb, f1 = (sfirst[seg] + snb[seg]) * tpb;
-        const uint64_t t0 = wall_clock64();
-        int go = 1;
-        for (;;) {
-          bool ok = true;
-          for (int i = f0 + lane; i < f1; i += 64)
-            ok &= (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch);
-          if (__ballot(!ok) == 0) break;
-          if ((int64_t)(wall_clock64() - t0) > timeout) {
-            if (lane == 0)
-              __hip_atomic_store(hdr + H_ERROR, 4 /* MOE_ETIMEOUT */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            go = 0;
-            break;
-          }
-          if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-            go = 0;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-        if (lane == 0) *s_go = go;
-      }
-      __syncthreads();
-      const int go = *s_go;
-      __syncthreads();
-      if (!go) return;
+      if (!wait_segment(L, hdr, sfirst, snb, flags, epoch, timeout, seg, s_go)) return;
       ready = seg;
     }
-    // unit u: bytes [lo, lo + kCopyChunk) of the segment, clipped to its end
-    // by the buffer bounds; every load is issued before the first store
-    const int64_t bytes = (int64_t)srows[seg] * d * 2;
-    const int64_t lo = (int64_t)(u - sunit[seg]) * kCopyChunk;
-    const int64_t n = min((int64_t)kCopyChunk, bytes - lo);
-    const __amdgpu_buffer_rsrc_t src = copy_rsrc((const char*)(y + (int64_t)ssrc[seg] * d) + lo, n);
-    const __amdgpu_buffer_rsrc_t dst = copy_rsrc((char*)(recv.p[sdst[seg]] + (int64_t)sdoff[seg] * d) + lo, n);
-    constexpr int VPT = kCopyChunk / (NT * 16);   // 16-byte vectors per thread
-    static_assert(VPT >= 1 && VPT * NT * 16 == kCopyChunk, "whole vectors per unit");
-    cv4u32 v[VPT];
+    copy_unit<NT>(L, ssrc, sdst, sdoff, srows, sunit, y, recv, seg, u);
+  }
+}
+
+// Consumer with claimed work, for the overlapped down-GEMM launch: the
+// remote copy units are handed out kClaimUnits at a time, in schedule order,
+// from the counter hdr[H_CLAIM] (zeroed by the gate/up launch before it).
+// The launch's consumer workgroups run it from the start; producers that
+// have run out of tiles join them, so the dedicated consumer can be small
+// and the copies left when the last tiles finish are shared by every CU.
+// Each workgroup asks for its next claim while it copies the current one.
+// `s_word` is two ints of the caller's LDS.
+constexpr int kClaimUnits = 2;
+
+template <int NT>
+__device__ void consume_claimed(const PlanLayout& L, int32_t* ws, const uint16_t* __restrict__ y,
+                                const uint32_t* __restrict__ flags, uint32_t epoch, const RecvPtrs& recv,
+                                int64_t timeout, int* s_word) {
+  int32_t* hdr = ws + L.o_hdr;
+  if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
+  const int32_t* sfirst = ws + L.o_sfirst;
+  const int32_t* snb = ws + L.o_snb;
+  const int32_t* sdst = ws + L.o_sdst;
+  const int32_t* sdoff = ws + L.o_sdoff;
+  const int32_t* ssrc = ws + L.o_ssrc;
+  const int32_t* srows = ws + L.o_srows;
+  const int32_t* sunit = ws + L.o_sunit;
+  const int n_rs = hdr[H_RSEGS];
+  const int U = sunit[n_rs];
+  const int n_claims = (U + kClaimUnits - 1) / kClaimUnits;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_word[1] = __hip_atomic_fetch_add(hdr + H_CLAIM, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  int k = s_word[1];
+  __syncthreads();
+  int seg = 0, ready = -1;
+  while (k < n_claims) {
+    // the next claim is in flight while this one is copied
+    if (tid == 0) s_word[1] = __hip_atomic_fetch_add(hdr + H_CLAIM, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b128(src, (k * NT + tid) * 16, 0, kAgentLoad);
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) __builtin_amdgcn_raw_buffer_store_b128(v[k], dst, (k * NT + tid) * 16, 0, 0);
+    for (int j = 0; j < kClaimUnits; ++j) {
+      const int u = k * kClaimUnits + j;
+      if (u < U) {
+        seg = segment_of_unit(sunit, n_rs, seg, u);
+        if (seg != ready) {
+          if (!wait_segment(L, hdr, sfirst, snb, flags, epoch, timeout, seg, s_word)) return;
+          ready = seg;
+        }
+        copy_unit<NT>(L, ssrc, sdst, sdoff, srows, sunit, y, recv, seg, u);
+      }
+    }
+    __syncthreads();
+    k = s_word[1];
+    __syncthreads();
   }
 }
 

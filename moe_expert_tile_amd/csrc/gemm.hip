@@ -220,19 +220,29 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   constexpr int WAVES_N = C::BN / C::WN;
   const int wave_m = wave / WAVES_N, wave_n = wave % WAVES_N;
   int32_t* hdr = g.ws + L.o_hdr;
+  if constexpr (SWIGLU) {
+    // the overlapped down GEMM that follows on this stream claims its copy
+    // units from these counters
+    if (blockIdx.x == 0 && tid == 0) {
+      hdr[H_CLAIM] = 0;
+      hdr[H_STARTED] = 0;
+    }
+  }
+  const bool overlapped = FLAGS && (int)gridDim.x > g.n_prod;
   if constexpr (FLAGS) {
     // overlapped combine (§5.3): the workgroups past the producers are the
     // consumer.  They are dispatched after every producer of their XCD and
     // hold the GEMM's LDS footprint, so each has a CU of its own; producers
     // never wait for them.
     if ((int)blockIdx.x >= g.n_prod) {
-      consume_segments<C::NT>(L, g.ws, g.out, g.flags, g.epoch, recv, g.timeout, blockIdx.x - g.n_prod,
-                              gridDim.x - g.n_prod, (int*)lds);
+      consume_claimed<C::NT>(L, g.ws, g.out, g.flags, g.epoch, recv, g.timeout, (int*)lds);
       if (tid == 0) stamp_max(hdr, H_T_CONS_END);
       return;
     }
   }
   if (hdr[H_ERROR] != 0) return;
+  if (overlapped && tid == 0)
+    __hip_atomic_fetch_add(hdr + H_STARTED, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Row tiles are taken in two regions, each in grouped order: for the down
   // GEMM the remote bands' tiles [0, n_mt_r) before the local bands' (so the
@@ -695,6 +705,21 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   }
   if constexpr (FLAGS) {
     if (tid == 0) stamp_max(hdr, H_T_PROD_END);
+    if (overlapped) {
+      // out of tiles: help copy the remaining remote segments, but only once
+      // every producer has started -- a producer still waiting for a CU could
+      // otherwise be kept from it by workgroups that wait for its tiles
+      __syncthreads();   // every wave is done with the LDS ring
+      int* s_word = (int*)lds;
+      if (tid == 0) s_word[0] = __hip_atomic_load(hdr + H_STARTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const bool all_started = s_word[0] == g.n_prod;
+      __syncthreads();
+      if (all_started) {
+        consume_claimed<C::NT>(L, g.ws, g.out, g.flags, g.epoch, recv, g.timeout, s_word);
+        if (tid == 0) stamp_max(hdr, H_T_CONS_END);
+      }
+    }
   }
 }
 

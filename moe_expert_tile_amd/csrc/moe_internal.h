@@ -30,6 +30,10 @@ enum Hdr {
   // needed between calls): words 12-13 and 14-15
   H_T_PROD_END = 12, H_T_CONS_END = 14,
   H_DN_MT_R = 16,   // down row tiles of remote bands (they come first)
+  // overlapped down-GEMM launch: copy-unit claims handed out so far, and
+  // producers that have started; both zeroed by the gate/up launch, which
+  // precedes every down GEMM on the same stream
+  H_CLAIM = 18, H_STARTED = 19,
   H_WORDS = 64
 };
 
