@@ -265,9 +265,10 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   const int32_t* rowoff = g.ws + L.o_rowoff;
 
   // Work split.  The first `full` tiles (whole rounds of G) are taken whole:
-  // tile slot, slot + G, ...  When the last round would be at most 3/4 full
-  // and tiles are long (KT >= kMinSkKT), its sk_tiles tiles are shared out
-  // along K instead ("stream-K"): their
+  // tile slot, slot + G, ...  When the last round (or the only one, with
+  // fewer tiles than workgroups) would be at most 3/4 full and tiles have at
+  // least kMinSkKT K steps, its sk_tiles tiles are shared out along K instead
+  // ("stream-K"): their
   // sk_tiles * KT K steps are cut into G_sk equal ranges, one per slot below
   // G_sk, each at least kMinSkSteps long.  A range spans at most two tiles;
   // each part (a piece) accumulates its K steps and stores its fp32 partial
@@ -276,7 +277,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   // runs the tile's epilogue.
   int full = total, sk_tiles = 0, G_sk = 0;
   int64_t W_sk = 0;
-  if (L.sk_slots >= 2 * G && total > G && KT >= kMinSkKT) {
+  if (L.sk_slots >= 2 * G && total > 0 && KT >= kMinSkKT) {
     const int rem = total % G;
     if (rem != 0 && 4 * rem <= 3 * G) {
       full = total - rem;
@@ -552,21 +553,22 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       constexpr int FH = (C::FN + 1) / 2;   // blocks of i per half
       for (int w = wa; w < G_sk && sk_lo(w) < a1; ++w) {
         const int pw_idx = (sk_lo(w) / KT == sk_j) ? 0 : 1;
-        const uint64_t* part = (const uint64_t*)(sk_part + (int64_t)(2 * w + pw_idx) * C::BM * C::BN);
+        // 16-byte agent-scope (sc1) loads: the partial may come from another
+        // XCD, so this XCD's cached lines of the slot must not be used
+        const __amdgpu_buffer_rsrc_t prs =
+            make_rsrc(sk_part + (int64_t)(2 * w + pw_idx) * C::BM * C::BN, (int64_t)C::BM * C::BN * 4);
 #pragma unroll
         for (int h = 0; h < C::FN; h += FH) {
-          uint64_t ld[FH][C::FM][4][2];
+          v4u32 ld[FH][C::FM][4];
 #pragma unroll
           for (int i = 0; i < FH; ++i)
 #pragma unroll
             for (int j = 0; j < C::FM; ++j)
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                if (h + i < C::FN) {
-                  const int64_t o = (int64_t)((((h + i) * C::FM + j) * 4 + q) * C::NT + tid) * 2;
-                  ld[i][j][q][0] = __hip_atomic_load(part + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                  ld[i][j][q][1] = __hip_atomic_load(part + o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+                if (h + i < C::FN)
+                  ld[i][j][q] = __builtin_amdgcn_raw_buffer_load_b128(
+                      prs, (((h + i) * C::FM + j) * 4 + q) * C::NT * 16 + tid * 16, 0, 16);
               }
 #pragma unroll
           for (int i = 0; i < FH; ++i)
@@ -575,10 +577,8 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 if (h + i < C::FN) {
-                  acc[h + i][j][4 * q] += __uint_as_float((uint32_t)ld[i][j][q][0]);
-                  acc[h + i][j][4 * q + 1] += __uint_as_float((uint32_t)(ld[i][j][q][0] >> 32));
-                  acc[h + i][j][4 * q + 2] += __uint_as_float((uint32_t)ld[i][j][q][1]);
-                  acc[h + i][j][4 * q + 3] += __uint_as_float((uint32_t)(ld[i][j][q][1] >> 32));
+#pragma unroll
+                  for (int c = 0; c < 4; ++c) acc[h + i][j][4 * q + c] += __uint_as_float(ld[i][j][q][c]);
                 }
               }
         }

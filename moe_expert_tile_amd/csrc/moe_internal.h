@@ -17,9 +17,12 @@ constexpr int kGuBN = 256;             // gate/up GEMM tile cols (128 gate + 128
 constexpr int kDnBN = 256;             // down GEMM tile cols
 constexpr int kMaxProducers = 256;     // persistent GEMM workgroups at most (one per CU on MI355X)
 constexpr int kMinSkSteps = 16;        // shortest K range of a stream-K piece
-constexpr int kMinSkKT = 128;          // stream-K only for tiles of at least this many K steps: the
-                                       // partials' round trip costs ~60-100 us per launch, which
-                                       // only a long tail round repays
+// stream-K only for tiles of at least this many K steps.  Measured: with 24-112
+// steps (the Qwen3- and DeepSeek-like GEMMs, and decode's 32-step gate/up on
+// 96 of 256 CUs) the partials' round trip through memory, limited by each
+// CU's ~35 GB/s load pipeline like the tiles themselves, cost as much as the
+// tail round it removes or more.
+constexpr int kMinSkKT = 128;
 
 // header words of the plan workspace (mirrors the public description)
 enum Hdr {
