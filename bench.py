@@ -9,7 +9,7 @@ Mixtral-8x7B-like layer (W=4 ranks, 8 experts, 4096 tokens per owner,
 d=4096, f=14336, top-2, tb_M=128), rank 0's share.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode overlap|serial]
-                    [--consumer-cus C] [--no-cpu-baseline]
+                    [--consumer-cus C] [--mgb B] [--no-cpu-baseline]
 
 Prints one JSON line.  value = tokens/s = (tokens per owner) / (time per
 step): the per-GPU rate if every rank took as long as rank 0.
@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--mode", default="overlap", choices=["overlap", "serial"])
     ap.add_argument("--consumer-cus", type=int, default=16)
+    ap.add_argument("--mgb", type=int, default=None,
+                    help="segment merge factor (bands per middle segment); default: the workload's (1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -143,7 +145,7 @@ def main():
     import moe_expert_tile_amd as m
     import synth
 
-    cfg = synth.get_config(args.workload)
+    cfg = synth.get_config(args.workload) if args.mgb is None else synth.get_config(args.workload, mgb=args.mgb)
     ids, w = synth.routing(cfg)
     x_owner = synth.activations(cfg)
     x_recv, _ = synth.dispatch(cfg, ids, x_owner)
@@ -265,6 +267,28 @@ def main():
     torch.cuda.synchronize()
     ms_serial = (time.perf_counter() - t0s) / n_serial * 1e3
 
+    # The same step with gathered rows: the plan builds the metadata only and
+    # the gate/up GEMM reads each layout row from x_recv through src_index,
+    # so the layout X is never materialized (no gather kernel, no pad fill).
+    def step_gathered():
+        share.plan(ids_d, xr_d, materialize=False)
+        share.combine(wgu_d, wd_d, mode=mode, consumer_cus=args.consumer_cus, x_recv=xr_d)
+        share.scale(w_r)
+
+    for _ in range(3):
+        step_gathered()
+    torch.cuda.synchronize()
+    n_g = max(5, args.steps // 2)
+    t0g = time.perf_counter()
+    for _ in range(n_g):
+        step_gathered()
+    torch.cuda.synchronize()
+    ms_gathered = (time.perf_counter() - t0g) / n_g * 1e3
+    t_plan_meta = amortized(lambda: share.plan(ids_d, xr_d, materialize=False))
+    st = share.status()
+    if st != m.MOE_OK:
+        raise SystemExit(f"device status after gathered-row steps: {m.status_string(st)}")
+
     gu_tflops = work["gateup_flop"] / t_gu
     result = {
         "metric": METRIC,
@@ -315,6 +339,11 @@ def main():
             "overlap_ratio": None if tail is None else round(max(0.0, min(1.0, 1.0 - tail / t_copy)), 4),
             "serial_ms_per_step": round(ms_serial, 4),
             "speedup_vs_serial": round(ms_serial / ms, 4),
+        },
+        "gathered_rows": {
+            "ms_per_step": round(ms_gathered, 4),
+            "tokens_per_s": round(T_r / (ms_gathered * 1e-3), 1),
+            "plan_metadata_back_to_back_us": round(t_plan_meta * 1e6, 2),
         },
         "work": {k: v for k, v in work.items()},
     }

@@ -122,6 +122,10 @@ typedef struct moe_combine_opts {
   void* events[6];          /* optional hipEvent_t, recorded on `stream`: [0]/[1] around the gate/up GEMM,
                                [2]/[3] around the down GEMM, [4]/[5] around the consumer (in OVERLAP both
                                pairs bracket the one launch that runs both); NULL entries are skipped */
+  const void* x_recv;       /* gathered rows: when x_layout is NULL, the gate/up GEMM reads layout row m
+                               straight from x_recv[src_index[m]] (device bf16 [R, d], the array given to
+                               moe_plan) and padding rows as zeros, so X is never materialized; requires
+                               R*d*2 < 2^31 bytes.  Ignored when x_layout is given. */
 } moe_combine_opts;
 
 /* Text of a status code. */
@@ -149,6 +153,9 @@ int moe_plan_offsets(const moe_shape* shape, moe_plan_view* out);
  *             every (owner, token, slot) with expert on rank r, lexicographic.
  *   plan_ws   device, plan_bytes from moe_query_sizes; written.
  *   x_layout  device bf16 [rows_cap, d]; rows [0, M) written (padding = +0).
+ *             May be NULL: then only the metadata is built, X is not
+ *             materialized, and moe_expert_combine must gather its rows from
+ *             x_recv (moe_combine_opts.x_recv).
  * Owner o's receive buffer (see moe_expert_combine) is [T_o*k, d], ordered by
  * (global expert, token).  Errors in the routing are reported through the
  * error word; all later kernels of this plan then do nothing.
@@ -168,7 +175,8 @@ int moe_plan(const moe_shape* shape, const int32_t* topk_ids, const uint16_t* x_
  * recv[dst] + dst_off*d; padding rows are never copied.  Rows of local bands
  * (destination r) never leave the rank: the down GEMM's epilogue writes them
  * into recv[r] itself, besides y.
- *   x_layout   device bf16 [rows_cap, d] from moe_plan.
+ *   x_layout   device bf16 [rows_cap, d] from moe_plan, or NULL with opts->x_recv set
+ *              (gathered rows, see moe_combine_opts).
  *   w_gate_up  device bf16 [E_l, 2f, d]: rows 0..f-1 gate, f..2f-1 up (K-contiguous).
  *   w_down     device bf16 [E_l, d, f] (K-contiguous).
  *   h, y       device bf16 [rows_cap, f] and [rows_cap, d]; scratch written here.

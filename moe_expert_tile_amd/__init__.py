@@ -56,7 +56,8 @@ class moe_plan_view(ctypes.Structure):
 class moe_combine_opts(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("consumer_cus", ctypes.c_int32),
                 ("consumer_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("spin_timeout_ns", ctypes.c_int64), ("events", ctypes.c_void_p * 6)]
+                ("spin_timeout_ns", ctypes.c_int64), ("events", ctypes.c_void_p * 6),
+                ("x_recv", ctypes.c_void_p)]
 
 
 class MoEError(RuntimeError):
@@ -159,13 +160,16 @@ def moe_plan(shape: Shape, topk_ids, x_recv, plan_ws, x_layout, stream=None) -> 
 def moe_expert_combine(shape: Shape, plan_ws, x_layout, w_gate_up, w_down, h, y, flags, epoch: int,
                        recv: List, mode: int = MODE_OVERLAP, consumer_cus: int = 0,
                        consumer_blocks: int = 0, spin_timeout_ns: int = 0,
-                       events: Optional[Sequence] = None, stream=None) -> None:
+                       events: Optional[Sequence] = None, stream=None, x_recv=None) -> None:
+    """x_layout=None with x_recv given: the gate/up GEMM gathers its rows from
+    x_recv through the plan's src_index (the layout is never materialized)."""
     arr = (ctypes.c_void_p * max(1, len(recv)))(*[_ptr(r) for r in recv])
     opts = moe_combine_opts()
     opts.mode = mode
     opts.consumer_cus = consumer_cus
     opts.consumer_blocks = consumer_blocks
     opts.spin_timeout_ns = spin_timeout_ns
+    opts.x_recv = _ptr(x_recv)
     if events is not None:
         for i, ev in enumerate(events):
             opts.events[i] = None if ev is None else int(ev.cuda_event)
@@ -219,17 +223,21 @@ class RankShare:
                      for t in shape.tokens]
         self.out = torch.empty((max(1, shape.tokens[s.rank]), s.hidden), dtype=torch.bfloat16, device=dev)
 
-    def plan(self, topk_ids, x_recv, stream=None):
-        moe_plan(self.shape, topk_ids, x_recv, self.plan_ws, self.x_layout, stream)
+    def plan(self, topk_ids, x_recv, stream=None, materialize=True):
+        """materialize=False: plan metadata only (no layout X); combine must
+        then be given x_recv to gather from."""
+        moe_plan(self.shape, topk_ids, x_recv, self.plan_ws, self.x_layout if materialize else None, stream)
 
     def combine(self, w_gate_up, w_down, mode=MODE_OVERLAP, consumer_cus=0, consumer_blocks=0,
-                spin_timeout_ns=0, events=None, stream=None, epoch=None):
+                spin_timeout_ns=0, events=None, stream=None, epoch=None, x_recv=None):
+        """x_recv given: gathered rows (the gate/up GEMM reads x_recv through
+        src_index instead of the layout X)."""
         if epoch is None:
             self.epoch += 1
             epoch = self.epoch
-        moe_expert_combine(self.shape, self.plan_ws, self.x_layout, w_gate_up, w_down, self.h, self.y,
-                           self.flags, epoch, self.recv, mode, consumer_cus, consumer_blocks,
-                           spin_timeout_ns, events, stream)
+        moe_expert_combine(self.shape, self.plan_ws, self.x_layout if x_recv is None else None, w_gate_up,
+                           w_down, self.h, self.y, self.flags, epoch, self.recv, mode, consumer_cus,
+                           consumer_blocks, spin_timeout_ns, events, stream, x_recv=x_recv)
 
     def scale(self, topk_w_self, stream=None):
         moe_scale(self.shape, self.plan_ws, self.recv[self.shape.c.rank], topk_w_self, self.out, stream)

@@ -255,7 +255,7 @@ int moe_plan(const moe_shape* s, const int32_t* topk_ids, const uint16_t* x_recv
   if (!plan_ws || !aligned(plan_ws, 256)) return MOE_EINVAL;
   if (pairs > 0 && (!topk_ids || !aligned(topk_ids, 4))) return MOE_EINVAL;
   if (s->recv_rows > 0 && (!x_recv || !aligned(x_recv, 16))) return MOE_EINVAL;
-  if (!x_layout || !aligned(x_layout, 16)) return MOE_EINVAL;
+  if (x_layout && !aligned(x_layout, 16)) return MOE_EINVAL;   // NULL: metadata only
   PlanLayout L;
   if (!make_layout(s->world, s->rank, s->experts_per_rank, s->top_k, s->hidden, s->ffn, s->tb_m, s->mgb, s->tokens,
                    s->recv_rows, &L))
@@ -287,9 +287,20 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   if (epoch == 0) return MOE_EINVAL;
   if (!plan_ws || !aligned(plan_ws, 256)) return MOE_EINVAL;
   const bool compute = (o.mode != MOE_MODE_COPY_ONLY);
+  // A rows of the gate/up GEMM: the materialized layout, or gathered from
+  // x_recv through src_index (padding rows read past the buffer's bound)
+  const uint16_t* a_rows = x_layout;
+  bool gathered = false;
   if (compute) {
-    if (!x_layout || !aligned(x_layout, 16) || !w_gate_up || !aligned(w_gate_up, 16) || !w_down ||
-        !aligned(w_down, 16) || !h || !aligned(h, 16))
+    if (!x_layout) {
+      const int64_t a_bytes = s->recv_rows * (int64_t)s->hidden * 2;
+      if (!o.x_recv || !aligned(o.x_recv, 16) || a_bytes >= (1ll << 31)) return MOE_EINVAL;
+      a_rows = (const uint16_t*)o.x_recv;
+      gathered = true;
+    } else if (!aligned(x_layout, 16)) {
+      return MOE_EINVAL;
+    }
+    if (!w_gate_up || !aligned(w_gate_up, 16) || !w_down || !aligned(w_down, 16) || !h || !aligned(h, 16))
       return MOE_EINVAL;
   }
   if (!y || !aligned(y, 16) || !flags || !aligned(flags, 4) || !recv) return MOE_EINVAL;
@@ -323,7 +334,7 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
     return rc;
   }
   record(o.events[0], st);
-  rc = hip_rc(launch_gateup(L, ws_rw, x_layout, w_gate_up, h, epoch, full_grid, st));
+  rc = hip_rc(launch_gateup(L, ws_rw, a_rows, gathered, w_gate_up, h, epoch, full_grid, st));
   record(o.events[1], st);
   if (rc) return rc;
   if (o.mode == MOE_MODE_SERIAL) {

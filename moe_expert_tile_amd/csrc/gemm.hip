@@ -133,6 +133,8 @@ struct GemmArgs {
   int half;               // SWIGLU: f (offset of the up rows); else 0
   int n_prod;             // producer workgroups (the rest of the grid consumes)
   int64_t timeout;        // consumer wait bound, 100 MHz ticks
+  const int32_t* gather;  // gathered A rows: row m of the layout is a[gather[m]] (< 0: zeros); else null
+  int64_t a_bytes;        // gathered: bytes of `a` (< 2^31)
 };
 
 __device__ __forceinline__ void stamp_max(int32_t* hdr, int word) {
@@ -385,16 +387,30 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     const int rbase = min(row0, row_end - 1);
     // buffer descriptors: A from the clamped base row to the expert's last
     // row, B over the expert's weight matrix (loads never leave them)
-    const __amdgpu_buffer_rsrc_t a_rsrc =
-        make_rsrc(g.a + (int64_t)rbase * g.K, (int64_t)(row_end - rbase) * g.K * 2);
     const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(g.w + (int64_t)e * g.w_rows * g.K, (int64_t)g.w_rows * g.K * 2);
+    __amdgpu_buffer_rsrc_t a_rsrc;
     uint32_t a_off[C::A_LOADS];
     uint32_t b_off[C::B_LOADS];
+    if (SWIGLU && g.gather != nullptr) {
+      // gathered rows: each lane's row comes from the received rows through
+      // src_index; padding rows and rows past the expert point past the
+      // buffer's bound (2^31 > a_bytes) and read as zeros
+      a_rsrc = make_rsrc(g.a, g.a_bytes);
 #pragma unroll
-    for (int i = 0; i < C::A_LOADS; ++i) {
-      const int r = (wave + i * C::NW) * C::RPB + ld_row;
-      const int rr = min(row0 + r, row_end - 1) - rbase;
-      a_off[i] = 2u * ((uint32_t)rr * (uint32_t)g.K + (uint32_t)(C::swz(r, ld_phys) * 8));
+      for (int i = 0; i < C::A_LOADS; ++i) {
+        const int r = (wave + i * C::NW) * C::RPB + ld_row;
+        const int src = (row0 + r < row_end) ? g.gather[row0 + r] : -1;
+        a_off[i] = src >= 0 ? 2u * ((uint32_t)src * (uint32_t)g.K + (uint32_t)(C::swz(r, ld_phys) * 8))
+                            : 0x80000000u;
+      }
+    } else {
+      a_rsrc = make_rsrc(g.a + (int64_t)rbase * g.K, (int64_t)(row_end - rbase) * g.K * 2);
+#pragma unroll
+      for (int i = 0; i < C::A_LOADS; ++i) {
+        const int r = (wave + i * C::NW) * C::RPB + ld_row;
+        const int rr = min(row0 + r, row_end - 1) - rbase;
+        a_off[i] = 2u * ((uint32_t)rr * (uint32_t)g.K + (uint32_t)(C::swz(r, ld_phys) * 8));
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
@@ -590,7 +606,9 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     // block.
     if constexpr (SWIGLU) {
       // gate/up: h = silu(gate) * up straight from registers, 8 bytes per
-      // lane (staging this 256 x 128 tile through LDS measured 1-4% slower)
+      // lane (staging this 256 x 128 tile through LDS measured 1-4% slower,
+      // and pairing lanes l, l+32 with v_permlane32_swap into 16-byte
+      // stores 0.4-1.8% slower)
       constexpr int HB = C::BN / 2, HW = C::WN / 2;
       const int mrow0 = row0 + wave_m * C::WM + lrow;
       const int ncol0 = nt * HB + wave_n * HW + 4 * lhalf;
@@ -732,9 +750,10 @@ using Dn32 = Cfg<32, 256, 1, 4, 64, 3, 3>;
 
 }  // namespace
 
-hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const uint16_t* x, const uint16_t* wgu, uint16_t* h,
-                         uint32_t epoch, int grid, hipStream_t s) {
-  GemmArgs a{ws, x, wgu, h, nullptr, epoch, L.d, L.f, 2 * L.f, L.f, grid, 0};
+hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const uint16_t* x, bool gathered, const uint16_t* wgu,
+                         uint16_t* h, uint32_t epoch, int grid, hipStream_t s) {
+  GemmArgs a{ws, x, wgu, h, nullptr, epoch, L.d, L.f, 2 * L.f, L.f, grid, 0,
+             gathered ? ws + L.o_src : nullptr, gathered ? (int64_t)L.R * L.d * 2 : 0};
   RecvPtrs none{};
   hipLaunchKernelGGL((grouped_gemm_kernel<GuCfg, true, false>), dim3(grid), dim3(GuCfg::NT), 0, s, L, a, none);
   return hipGetLastError();
@@ -743,7 +762,7 @@ hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const uint16_t* x, co
 hipError_t launch_down(const PlanLayout& L, int32_t* ws, const uint16_t* h, const uint16_t* wd, uint16_t* y,
                        uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks, int n_prod,
                        int grid, hipStream_t s) {
-  GemmArgs a{ws, h, wd, y, flags, epoch, L.f, L.d, L.d, 0, n_prod, timeout_ticks};
+  GemmArgs a{ws, h, wd, y, flags, epoch, L.f, L.d, L.d, 0, n_prod, timeout_ticks, nullptr, 0};
   switch (L.dn_bm) {
     case 256:
       hipLaunchKernelGGL((grouped_gemm_kernel<Dn256, false, true>), dim3(grid), dim3(Dn256::NT), 0, s, L, a, recv);

@@ -114,8 +114,10 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb,
 // launchers (defined next to their kernels); all asynchronous on `s`
 hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t* x_recv,
                        int32_t* ws, uint16_t* x_layout, hipStream_t s);
-hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const uint16_t* x, const uint16_t* wgu, uint16_t* h,
-                         uint32_t epoch, int grid, hipStream_t s);
+// gate/up GEMM: A rows from the layout `x` [rows_cap, d], or (gathered) from
+// x_recv [R, d] through the plan's src_index
+hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const uint16_t* x, bool gathered, const uint16_t* wgu,
+                         uint16_t* h, uint32_t epoch, int grid, hipStream_t s);
 // down GEMM: `n_prod` persistent producer workgroups; the grid's remaining
 // workgroups (if any) are consumers (consume.h).  Local bands are also
 // written to recv.p[L.r].

@@ -685,6 +685,7 @@ hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t*
     const size_t sh_place = (size_t)((L.E_l + 1) * (nw + 1) + L.E * (nw + 1)) * sizeof(int);
     hipLaunchKernelGGL(plan_place_kernel, dim3(L.NB), dim3(kPlanThreads), sh_place, s, L, topk, ws);
   }
+  if (x_layout == nullptr) return hipGetLastError();   // metadata only: the GEMM gathers its rows
   const int rows_per_block = 4;
   int grid = (L.rows_cap + rows_per_block - 1) / rows_per_block;
   if (grid > 4096) grid = 4096;

@@ -92,6 +92,18 @@ def test_bad_pointers_are_rejected_before_any_hip_call():
                              stream=0)
     assert ei.value.status == m.MOE_EINVAL                        # null receive buffer
     with pytest.raises(m.MoEError) as ei:
+        m.moe_expert_combine(s, good, None, good, good, good, good, good, 1, [good] * 4, stream=0)
+    assert ei.value.status == m.MOE_EINVAL                        # no layout and nothing to gather from
+    with pytest.raises(m.MoEError) as ei:
+        m.moe_expert_combine(s, good, None, good, good, good, good, good, 1, [good] * 4, stream=0,
+                             x_recv=good + 4)
+    assert ei.value.status == m.MOE_EINVAL                        # misaligned x_recv to gather from
+    big = _shape(hidden=65536, ffn=128, tokens=[8192] * 4, recv_rows=16384, top_k=2)
+    with pytest.raises(m.MoEError) as ei:
+        m.moe_expert_combine(big, good, None, good, good, good, good, good, 1, [good] * 4, stream=0,
+                             x_recv=good)
+    assert ei.value.status == m.MOE_EINVAL                        # R*d*2 = 2^31 bytes: too large to gather
+    with pytest.raises(m.MoEError) as ei:
         m.moe_scale(s, good, good, good, good + 2, stream=0)
     assert ei.value.status == m.MOE_EINVAL
     assert m.moe_device_status(0, stream=0) == m.MOE_EINVAL

@@ -10,6 +10,8 @@
   layout row; repeated overlapped epochs without a flag reset, with y
   poisoned by NaN before each call, copy exactly their own y and give the
   same y again; serial and overlapped y agree within the tolerance.
+* Gathered rows: the gate/up GEMM reading the layout's rows from x_recv
+  through src_index instead of a materialized X gives the same bits.
 * Scale (§2.2 step 5): sampled tokens of the rank's own output against the
   oracle, whose receive rows come from the oracle's own FFN.
 """
@@ -126,6 +128,48 @@ def test_overlapped_combine_over_epochs(name):
     assert tol_ratio(y_first, y_serial, name == "tiny") <= 1.0
     if name in ("tiny_unit", "decode_tb32"):
         assert np.array_equal(y_first, y_serial)
+
+
+@pytest.mark.parametrize("name", ["tiny_unit", "mixtral", "qwen3", "dsv3_skew", "decode_tb32", "decode_tb64"])
+def test_gathered_rows_equal_the_layout_path(name):
+    """Gathered A rows: a plan that does not materialize the layout X, and a
+    gate/up GEMM that reads every layout row from x_recv through src_index
+    (padding rows as zeros), give h, y and receive buffers bit-identical to
+    the materialized layout's in the serial mode, and in the overlapped mode
+    receive buffers that are exactly the plan applied to their own y; the
+    layout buffer is never written."""
+    import moe_expert_tile_amd as m
+    c, share, wgu_d, wd_d = planned(name, m.MODE_SERIAL)
+    cfg, pl = c["cfg"], c["plan"]
+    H, Y = host_bits(share.h[:pl.M]), host_bits(share.y[:pl.M])
+    recv_ref = [host_bits(r) for r in share.recv]
+    written = OC.written_rows(pl)
+    g = m.RankShare(shape_of(cfg, pl.R))
+    g.x_layout.fill_(float("nan"))
+    xr = dev_bf16(c["x_recv"])
+    g.plan(torch.from_numpy(c["ids"]).cuda(), xr, materialize=False)
+    for mode in (m.MODE_SERIAL, m.MODE_OVERLAP):
+        for o in range(cfg.W):
+            g.recv[o].copy_(dev_bf16(synth.foreign_rows(cfg, o)))
+        g.h.fill_(float("nan"))
+        g.y.fill_(float("nan"))
+        g.combine(wgu_d, wd_d, mode=mode, x_recv=xr)
+        assert g.status() == m.MOE_OK
+        assert np.array_equal(host_bits(g.h[:pl.M]), H), mode
+        y = host_bits(g.y[:pl.M])
+        if mode == m.MODE_SERIAL:
+            assert np.array_equal(y, Y)
+            for o in range(cfg.W):
+                assert np.array_equal(host_bits(g.recv[o]), recv_ref[o]), o
+        else:
+            assert tol_ratio(y, Y) <= 1.0
+            for o in range(cfg.W):
+                exp = synth.foreign_rows(cfg, o)
+                dst, src = written[o]
+                exp[dst] = y[src]
+                assert np.array_equal(host_bits(g.recv[o][: exp.shape[0]]), exp), o
+    assert bool(torch.isnan(g.x_layout[: min(pl.M, 512)].float()).all())
+    del g
 
 
 @pytest.mark.parametrize("name", WORKLOADS)
