@@ -47,6 +47,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t copy_rsrc(const void* base, in
 // producer's release is not returned stale
 constexpr int kAgentLoad = 16;
 
+#ifndef MOE_POLL_MAX_NAPS
+#define MOE_POLL_MAX_NAPS 32   // longest pause between flag polls, in units of 128 clocks
+#endif
+
 // Segment of copy unit u, searching forward from `seg` (units only grow):
 // a few steps ahead, then a binary search over the rest.
 __device__ __forceinline__ int segment_of_unit(const int32_t* sunit, int n_rs, int seg, int u) {
@@ -76,22 +80,29 @@ __device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, c
     const int f0 = sfirst[seg] * tpb, f1 = (sfirst[seg] + snb[seg]) * tpb;
     const uint64_t t0 = wall_clock64();
     int go = 1;
-    for (;;) {
+    // exponential back-off between polls (128 clocks doubling to ~4K), and
+    // the clock and the shared error word read only every 16th poll: many
+    // waiting workgroups polling a few cache lines slow the producers down
+    int naps = 1;
+    for (int poll = 1;; ++poll) {
       bool ok = true;
       for (int i = f0 + lane; i < f1; i += 64)
         ok &= (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch);
       if (__ballot(!ok) == 0) break;
-      if ((int64_t)(wall_clock64() - t0) > timeout) {
-        if (lane == 0)
-          __hip_atomic_store(hdr + H_ERROR, 4 /* MOE_ETIMEOUT */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        go = 0;
-        break;
+      if ((poll & 15) == 0) {
+        if ((int64_t)(wall_clock64() - t0) > timeout) {
+          if (lane == 0)
+            __hip_atomic_store(hdr + H_ERROR, 4 /* MOE_ETIMEOUT */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          go = 0;
+          break;
+        }
+        if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+          go = 0;
+          break;
+        }
       }
-      if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-        go = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+      for (int z = 0; z < naps; ++z) __builtin_amdgcn_s_sleep(2);
+      naps = min(2 * naps, MOE_POLL_MAX_NAPS);
     }
     if (lane == 0) *s_go = go;
   }
