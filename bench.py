@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--mgb", type=int, default=None,
                     help="segment merge factor (bands per middle segment); default: the workload's (1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gathered", action="store_true",
+                    help="skip the gathered-rows variant (profiling runs that count one kind of gate/up launch)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device to device 3 times (a plain copy of known "
@@ -275,19 +277,21 @@ def main():
         share.combine(wgu_d, wd_d, mode=mode, consumer_cus=args.consumer_cus, x_recv=xr_d)
         share.scale(w_r)
 
-    for _ in range(3):
-        step_gathered()
-    torch.cuda.synchronize()
-    n_g = max(5, args.steps // 2)
-    t0g = time.perf_counter()
-    for _ in range(n_g):
-        step_gathered()
-    torch.cuda.synchronize()
-    ms_gathered = (time.perf_counter() - t0g) / n_g * 1e3
-    t_plan_meta = amortized(lambda: share.plan(ids_d, xr_d, materialize=False))
-    st = share.status()
-    if st != m.MOE_OK:
-        raise SystemExit(f"device status after gathered-row steps: {m.status_string(st)}")
+    ms_gathered = t_plan_meta = None
+    if not args.no_gathered:
+        for _ in range(3):
+            step_gathered()
+        torch.cuda.synchronize()
+        n_g = max(5, args.steps // 2)
+        t0g = time.perf_counter()
+        for _ in range(n_g):
+            step_gathered()
+        torch.cuda.synchronize()
+        ms_gathered = (time.perf_counter() - t0g) / n_g * 1e3
+        t_plan_meta = amortized(lambda: share.plan(ids_d, xr_d, materialize=False))
+        st = share.status()
+        if st != m.MOE_OK:
+            raise SystemExit(f"device status after gathered-row steps: {m.status_string(st)}")
 
     gu_tflops = work["gateup_flop"] / t_gu
     result = {
@@ -340,7 +344,7 @@ def main():
             "serial_ms_per_step": round(ms_serial, 4),
             "speedup_vs_serial": round(ms_serial / ms, 4),
         },
-        "gathered_rows": {
+        "gathered_rows": None if ms_gathered is None else {
             "ms_per_step": round(ms_gathered, 4),
             "tokens_per_s": round(T_r / (ms_gathered * 1e-3), 1),
             "plan_metadata_back_to_back_us": round(t_plan_meta * 1e6, 2),

@@ -8,20 +8,25 @@
 //
 // gfx950 design (not the pages' CUTLASS one):
 //   * v_mfma_f32_32x32x16_bf16, fp32 accumulation, 64-wide wavefronts;
-//     4 wavefronts per workgroup, each owning a WM x WN register tile.
+//     8 wavefronts per workgroup (2 per SIMD), each owning a WM x WN register
+//     tile of a 256 x 256 output tile (gate/up: 128 gate + 128 up columns
+//     of the same indices, so SwiGLU is fused in the epilogue).
 //   * The MFMA's first operand is the weight tile (rows = output columns n),
 //     the second the activation tile (rows = output rows m), so each lane ends
-//     with 4 consecutive output columns per accumulator quad: 8-byte bf16
-//     stores, and the SwiGLU gate/up pair of a column sits in one lane.
+//     with 4 consecutive output columns per accumulator quad, and the SwiGLU
+//     gate/up pair of a column sits in one lane.
 //   * K steps of 64: both operands are K-contiguous in HBM, copied straight
-//     into LDS with 16-byte buffer loads (no staging registers), two LDS
-//     stages, 16-byte chunks XOR-swizzled by (row mod 8) so that the
-//     ds_read_b128 operand fetches are bank-conflict free.
+//     into LDS with 16-byte buffer loads (no staging registers) into one ring
+//     per operand, 16-byte chunks XOR-swizzled so that the ds_read_b128
+//     operand fetches are bank-conflict free on the 64-bank LDS.
+//   * Epilogues: gate/up stores h from registers; the down GEMM stages its
+//     tile through LDS and writes whole lines with write-through stores, then
+//     releases the tile and sets its flags.
 //   * Persistent grid (a multiple of 8 workgroups).  Workgroup w runs on XCD
 //     w mod 8; it takes slot (w mod 8) * (G/8) + w/8 of every round of G
 //     tiles, so each XCD works on a contiguous run of the tile order, and the
-//     tile order groups GM row tiles per column sweep so the run shares
-//     operand rows in that XCD's L2.
+//     two-level tile order (decode_tile) makes that run a block of 8 row
+//     tiles x 4 column tiles whose operands share the XCD's L2.
 #include <type_traits>
 
 #include "consume.h"
@@ -35,8 +40,12 @@ typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Tile shapes (compile-time; the defaults are the measured best on MI355X).
-#ifndef MOE_GROUP_M
-#define MOE_GROUP_M 8
+#ifndef MOE_XCD_ROWS
+// XCDs sharing a weight block in the two-level tile order (1, 2, 4, 8).
+// Measured: 2 takes 2% off the Mixtral-like down GEMM; the gate/up GEMMs and
+// the other workloads are within noise of 1; 8 is slower on the
+// DeepSeek-like GEMMs.
+#define MOE_XCD_ROWS 2
 #endif
 #ifndef MOE_GU_WAVES_M
 #define MOE_GU_WAVES_M 4
@@ -77,7 +86,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #ifndef MOE_LOAD_AUX
 #define MOE_LOAD_AUX 0   // cache-policy bits of the operand loads (default policy measured best)
 #endif
-constexpr int kGroupM = MOE_GROUP_M;   // row tiles per column sweep
+constexpr int kXcdRows = MOE_XCD_ROWS;
+static_assert(kXcdRows == 1 || kXcdRows == 2 || kXcdRows == 4 || kXcdRows == 8, "XCD rows");
 
 // BM x BN output tile, WAVES_M x WAVES_N wavefronts, K step BK; the A and B
 // operands have their own global -> LDS rings, SA and SB stages deep (2 or
@@ -166,15 +176,58 @@ __device__ __forceinline__ void stage_barrier(int n) {
 // scheduling-group masks of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x8, kSchedVmem = 0x10, kSchedDsRead = 0x100;
 
-// Tile t of a (n_mt x n_nt) grid in grouped order -> (mt, nt): groups of
-// kGroupM row tiles sweep all column tiles.
+// Tile t of a (n_mt x n_nt) grid -> (mt, nt), in a two-level order.  A
+// round of the persistent grid hands each XCD 32 consecutive tiles; those
+// form a block of 8 row tiles x 4 column tiles (12 operand blocks for 32
+// tiles in that XCD's L2).  The 8 XCDs' blocks form a chip block of
+// 8*XR row tiles x 4*(8/XR) column tiles, so that XR XCDs read the same
+// weight blocks (and 8/XR the same activation blocks) at the same time,
+// which turns more of their L2 misses into Infinity Cache hits instead of
+// HBM reads.  Chip blocks sweep the columns of a row group, row groups follow
+// one another; ragged edges give smaller blocks.  XR = 1 is the plain
+// grouped order (groups of 8 row tiles sweeping all column tiles).
 __device__ __forceinline__ void decode_tile(int t, int n_mt, int n_nt, int& mt, int& nt) {
-  const int per_group = kGroupM * n_nt;
-  const int g = t / per_group;
-  const int in = t - g * per_group;
-  const int gm = min(kGroupM, n_mt - g * kGroupM);
-  mt = g * kGroupM + in % gm;
-  nt = in / gm;
+  constexpr int XR = kXcdRows, XC = 8 / kXcdRows;
+  constexpr int BR = 8 * XR, BC = 4 * XC;
+  const int full_rg = n_mt / BR;
+  int rg, rr, t1;
+  if (t < full_rg * BR * n_nt) {
+    rg = t / (BR * n_nt);
+    rr = BR;
+    t1 = t - rg * BR * n_nt;
+  } else {
+    rg = full_rg;
+    rr = n_mt - full_rg * BR;
+    t1 = t - full_rg * BR * n_nt;
+  }
+  const int full_cb = n_nt / BC;
+  int cb, cc, t2;
+  if (t1 < full_cb * rr * BC) {
+    cb = t1 / (rr * BC);
+    cc = BC;
+    t2 = t1 - cb * rr * BC;
+  } else {
+    cb = full_cb;
+    cc = n_nt - full_cb * BC;
+    t2 = t1 - full_cb * rr * BC;
+  }
+  // 8 x 4 blocks of the chip block, column blocks outer, rows fastest inside
+  const int nsr = (rr + 7) / 8, nsc = (cc + 3) / 4;
+  mt = rg * BR;
+  nt = cb * BC;
+  for (int sx = 0; sx < nsc; ++sx) {
+    const int cw = min(4, cc - 4 * sx);
+    for (int sr = 0; sr < nsr; ++sr) {
+      const int rh = min(8, rr - 8 * sr);
+      const int n = rh * cw;
+      if (t2 < n) {
+        mt += 8 * sr + t2 % rh;
+        nt += 4 * sx + t2 / rh;
+        return;
+      }
+      t2 -= n;
+    }
+  }
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
