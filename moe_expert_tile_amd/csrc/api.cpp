@@ -110,6 +110,7 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->o_bhr = take((int64_t)L->NB_r * L->E);
   L->o_bpr = take((int64_t)L->NB_r * L->E);
   L->o_baser = take(L->E);
+  L->o_pad = take(2 * EW);
   L->o_gumt_row = take(L->gu_mt_cap);
   L->o_gumt_exp = take(L->gu_mt_cap);
   L->o_dnt_row = take(B); L->o_dnt_exp = take(B); L->o_dnt_band = take(B); L->o_dnt_nb = take(B);
@@ -265,9 +266,11 @@ int moe_plan(const moe_shape* s, const int32_t* topk_ids, const uint16_t* x_recv
   if (rc) return rc;
   // the plan builder copies the per-block histograms into LDS only when the
   // whole request fits well inside the device's per-workgroup LDS
-  const int64_t stage_words = (int64_t)build_lds(L.W, L.E_l, L.E, 0, 0, false).total +
-                              (int64_t)L.NB * (L.E_l + 2) + (int64_t)L.NB_r * L.E;
-  L.build_stage = stage_words * 4 <= std::min<int64_t>(g_dev[dev].lds_per_block, kBuildLdsBytes);
+  const int64_t lds_cap = std::min<int64_t>(g_dev[dev].lds_per_block, kBuildLdsBytes);
+  L.band_table = (L.bands_cap <= kBandTableMax &&
+                  (int64_t)build_lds(L.W, L.E_l, L.E, 0, 0, L.bands_cap, false).total * 4 <= lds_cap)
+                     ? L.bands_cap : 0;
+  L.build_stage = (int64_t)build_lds(L.W, L.E_l, L.E, L.NB, L.NB_r, L.band_table, true).total * 4 <= lds_cap;
   return hip_rc(launch_plan(L, topk_ids, x_recv, (int32_t*)plan_ws, x_layout, (hipStream_t)stream));
 }
 

@@ -49,6 +49,7 @@ struct PlanLayout {
   int dn_merge;                        // > 0: down m-tiles of up to dn_merge row-contiguous bands (table)
   int gu_ntn;                          // gate/up GEMM n tiles (f / 128)
   int build_stage;                     // plan_build copies the block histograms into LDS
+  int band_table;                      // plan_build's band -> group table in LDS (bands_cap, or 0)
   int sk_slots;                        // stream-K partial-sum slots (256x256 fp32 each) in the workspace
   int64_t o_hdr, o_c, o_low, o_grp, o_me, o_rowoff, o_rb, o_order, o_base;
   int64_t o_bexp, o_bdst, o_bsrc, o_bdoff, o_bval;
@@ -56,6 +57,7 @@ struct PlanLayout {
   int64_t o_src, o_pos;
   int64_t o_bh, o_bp, o_brecv, o_bhr, o_bpr, o_baser;
   int64_t o_gumt_row, o_gumt_exp;
+  int64_t o_pad;                       // [2][E_l*W]: first padding row and padding rows of every remote group
   int64_t o_dnt_row, o_dnt_exp, o_dnt_band, o_dnt_nb;
   int64_t o_skc;                       // uint64 [2][kMaxProducers] stream-K tile counters (gate/up, down)
   int64_t o_skp;                       // float [sk_slots][256*256] stream-K partial sums
@@ -74,13 +76,13 @@ struct RecvPtrs {
 // per-block histograms are copied in too.  The host sizes the launch's
 // dynamic LDS with the same function the kernel carves it with.
 struct BuildLds {
-  int c, grp, base, gstart, low, me, rowoff, rb, order, baser, gupre, dnpre, pad_st, pad_ct, sh, misc;
-  int stage_bh, stage_bhr, total;
+  int c, grp, base, gstart, low, me, rowoff, rb, order, baser, gupre, dnpre, sh, misc;
+  int band_g, stage_bh, stage_bhr, total;
 };
 #if defined(__HIPCC__)
 __host__ __device__
 #endif
-inline BuildLds build_lds(int W, int E_l, int E, int NB, int NB_r, bool stage) {
+inline BuildLds build_lds(int W, int E_l, int E, int NB, int NB_r, int band_table, bool stage) {
   BuildLds s;
   const int EW = E_l * W;
   int o = 0;
@@ -96,16 +98,17 @@ inline BuildLds build_lds(int W, int E_l, int E, int NB, int NB_r, bool stage) {
   s.baser = o; o += E;
   s.gupre = o; o += E_l + 1;
   s.dnpre = o; o += 2 * E_l + 1;
-  s.pad_st = o; o += EW;
-  s.pad_ct = o; o += EW;
   s.sh = o; o += 16;
   s.misc = o; o += 8;
-  s.stage_bh = o; if (stage) o += NB * (E_l + 2);
+  s.band_g = o; o += band_table;              // group of every band (0: not kept)
+  o = (o + 3) & ~3;                           // 16-byte aligned staging
+  s.stage_bh = o; if (stage) o += (NB * (E_l + 2) + 3) & ~3;
   s.stage_bhr = o; if (stage) o += NB_r * E;
   s.total = o;
   return s;
 }
 constexpr int kBuildLdsBytes = 64 * 1024;   // cap on plan_build's dynamic LDS (the default dynamic limit)
+constexpr int kBandTableMax = 8192;          // plan_build keeps a band -> group table up to this many bands
 
 // host-side helpers (api.cpp)
 bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb,

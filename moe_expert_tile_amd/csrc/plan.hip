@@ -9,13 +9,13 @@
 //                   -> group counts, padded group offsets, X_e sizes, rule
 //                   (ii) expert order, band list S (remote bands first),
 //                   combine plan, segments and their copy units, GEMM row-tile
-//                   tables, padding entries of src_index.  Its tables live in
-//                   LDS; nothing it writes to memory is read back.
+//                   tables, padding extent of every remote group.  Its tables
+//                   live in LDS; nothing it writes to memory is read back.
 //   K3 plan_place   one workgroup per pair block again: stable rank of every
 //                   pair inside its (expert, owner) group with bit-sliced wave
 //                   ballots + LDS carries -> src_index of every real layout
 //                   row, and the owner-side slot of each of the rank's own
-//                   pairs.
+//                   pairs; the blocks also write the padding entries (-1).
 //   K4 plan_gather  one wavefront per layout row: X[row] = x_recv[src] or 0,
 //                   16-byte coalesced loads and stores.
 //
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   const int W = L.W, r = L.r, E_l = L.E_l, E = L.E, tb = L.tb_m;
   const int HB = E_l + 2;
   const int EW = E_l * W;
-  const BuildLds S = build_lds(W, E_l, E, L.NB, L.NB_r, L.build_stage != 0);
+  const BuildLds S = build_lds(W, E_l, E, L.NB, L.NB_r, L.band_table, L.build_stage != 0);
   int32_t* hdr = ws + L.o_hdr;
   int* c = smem + S.c;             // [E_l][W] group sizes
   int* grp = smem + S.grp;         // [E_l][W] group offsets inside X_e
@@ -201,15 +201,22 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     // parallel copy into LDS (the host sized the LDS for it)
     int* s_bh = smem + S.stage_bh;
     int* s_bhr = smem + S.stage_bhr;
+    // 16-byte loads, 8 in flight per thread (both ends 16-byte aligned);
+    // the last n mod 4 words one by one
     auto stage = [&](int* dst, const int32_t* src, int n) {
-      for (int i0 = tid; i0 < n; i0 += 8 * nt) {
-        int v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (i0 + u * nt < n) ? src[i0 + u * nt] : 0;
+      const int n4 = n >> 2;
+      const int4* s4 = (const int4*)src;
+      int4* d4 = (int4*)dst;
+      for (int i0 = tid; i0 < n4; i0 += 8 * nt) {
+        int4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (i0 + u * nt < n) dst[i0 + u * nt] = v[u];
+          if (i0 + u * nt < n4) v[u] = s4[i0 + u * nt];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u * nt < n4) d4[i0 + u * nt] = v[u];
       }
+      for (int i = 4 * n4 + tid; i < n; i += nt) dst[i] = src[i];
     };
     stage(s_bh, bh, L.NB * HB);
     stage(s_bhr, bhr, L.NB_r * E);
@@ -344,14 +351,16 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   const int n_remote = NGR < NG ? gstart[NGR] : B;
 
   // (f) bands in S order, one thread per group (a group's bands are
-  //     consecutive in S), and the padding rows of every remote group
+  //     consecutive in S), a band -> group table in LDS when it fits, and
+  //     the padding rows of every remote group
   int32_t* bexp = ws + L.o_bexp;
   int32_t* bdst = ws + L.o_bdst;
   int32_t* bsrc = ws + L.o_bsrc;
   int32_t* bdoff = ws + L.o_bdoff;
   int32_t* bval = ws + L.o_bval;
-  int* pad_st = smem + S.pad_st;
-  int* pad_ct = smem + S.pad_ct;
+  int* band_g = L.band_table > 0 ? smem + S.band_g : nullptr;
+  int32_t* pad_st = ws + L.o_pad;         // read by plan_place, which writes the padding entries
+  int32_t* pad_ct = pad_st + EW;
   for (int gi = tid; gi < NG; gi += nt) {
     int e, o;
     group_eo(gi, e, o);
@@ -361,6 +370,7 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     const int rowb = rowoff[e] + grp[e * W + o];
     const int dstb = base[o * E_l + e];
     for (int q = 0; q < nb; ++q) {
+      if (band_g) band_g[gs + q] = gi;
       bexp[gs + q] = e;
       bdst[gs + q] = o;
       bsrc[gs + q] = rowb + q * tb;
@@ -374,32 +384,38 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   }
 
   // (g) segments (§5.2): the first and the last remote band alone; otherwise
-  //     runs of <= mgb bands that restart at every group boundary.  A segment
-  //     never crosses a group, so each group's thread walks its bands; one
-  //     scan over the groups numbers the segments and places their copy
-  //     units.
+  //     runs of <= mgb bands that restart at every group boundary.  Every
+  //     band decides whether it starts a segment and, if so, the segment's
+  //     bands, rows and copy units (a segment never crosses a group, so they
+  //     are read off the group); one pair scan over the bands numbers the
+  //     segments and places their copy units.
   const int mgb = L.mgb;
   const int64_t row_bytes = (int64_t)L.d * 2;
   auto units_of = [&](int rows) { return (int)((rows * row_bytes + kCopyChunk - 1) / kCopyChunk); };
-  // calls f(first band, bands, rows) for every segment of group gi, in order
-  auto walk_segments = [&](int gi, auto&& f) {
+  if (tid == 0) gstart[NG] = B;
+  __syncthreads();   // band table, gstart[NG]
+  auto group_of = [&](int b) { return band_g ? band_g[b] : upper_index(gstart, NG, b); };
+  // does band b (of group gi, first band gs) start a segment
+  auto starts = [&](int b, int gi, int gs) {
+    if (b == gs) return true;
+    if (gi < NGR) {
+      const int run0 = gs > 1 ? gs : 1;
+      return b == n_remote - 1 || ((b - run0) % mgb) == 0;
+    }
+    return ((b - gs) % mgb) == 0;
+  };
+  // segment starting at band b: its bands and rows (false if b starts none)
+  auto seg_at = [&](int b, int& gi, int& nb, int& rows) {
+    gi = group_of(b);
+    const int gs = gstart[gi];
+    if (!starts(b, gi, gs)) return false;
+    const int ge = gstart[gi + 1];
+    nb = 1;
+    while (b + nb < ge && !starts(b + nb, gi, gs)) ++nb;
     int e, o;
     group_eo(gi, e, o);
-    const int n = c[e * W + o];
-    const int gs = gstart[gi], ge = gs + (n + tb - 1) / tb;
-    const bool remote = gi < NGR;
-    const int run0 = gs > 1 ? gs : 1;
-    auto starts = [&](int b) {
-      if (b == gs) return true;
-      if (remote) return b == n_remote - 1 || ((b - run0) % mgb) == 0;
-      return ((b - gs) % mgb) == 0;
-    };
-    for (int b = gs; b < ge;) {
-      int nb = 1;
-      while (b + nb < ge && !starts(b + nb)) ++nb;
-      f(b, nb, min(nb * tb, n - (b - gs) * tb), e, o);
-      b += nb;
-    }
+    rows = min(nb * tb, c[e * W + o] - (b - gs) * tb);
+    return true;
   };
   int32_t* sfirst = ws + L.o_sfirst;
   int32_t* snb = ws + L.o_snb;
@@ -408,56 +424,35 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   int32_t* ssrc = ws + L.o_ssrc;
   int32_t* srows = ws + L.o_srows;
   int32_t* sunit = ws + L.o_sunit;
-  __syncthreads();   // pad tables
+  if (tid == 0) misc[0] = -1;
+  __syncthreads();
   const int2 stot = scan_items2(
-      NG,
-      [&](int gi) {
-        int ns = 0, nu = 0;
-        walk_segments(gi, [&](int, int, int rows, int, int) {
-          ++ns;
-          nu += units_of(rows);
-        });
-        return make_int2(ns, nu);
+      B,
+      [&](int b) {
+        int gi, nb, rows;
+        if (!seg_at(b, gi, nb, rows)) return make_int2(0, 0);
+        return make_int2(1, units_of(rows));
       },
-      [&](int gi, int2 pre) {
-        if (gi == NGR) misc[0] = pre.x;   // the remote segments come first
-        int i = pre.x, u = pre.y;
-        walk_segments(gi, [&](int b, int nb, int rows, int e, int o) {
-          const int q = b - gstart[gi];
-          sfirst[i] = b;
-          snb[i] = nb;
-          sdst[i] = o;
-          sdoff[i] = base[o * E_l + e] + q * tb;
-          ssrc[i] = rowoff[e] + grp[e * W + o] + q * tb;
-          srows[i] = rows;
-          sunit[i] = u;
-          ++i;
-          u += units_of(rows);
-        });
+      [&](int b, int2 pre) {
+        int gi, nb, rows;
+        if (!seg_at(b, gi, nb, rows)) return;
+        int e, o;
+        group_eo(gi, e, o);
+        const int q = b - gstart[gi];
+        const int i = pre.x;
+        sfirst[i] = b;
+        snb[i] = nb;
+        sdst[i] = o;
+        sdoff[i] = base[o * E_l + e] + q * tb;
+        ssrc[i] = rowoff[e] + grp[e * W + o] + q * tb;
+        srows[i] = rows;
+        sunit[i] = pre.y;
+        if (b == n_remote) misc[0] = i;   // the first local band starts a segment
       },
       sh);
   const int NS = stot.x, U = stot.y;
-  const int n_rsegs = misc[0];
+  const int n_rsegs = misc[0] >= 0 ? misc[0] : NS;
   if (tid == 0) sunit[NS] = U;
-
-  // (h) padding entries of src_index: one wavefront per remote group, its
-  //     lanes over the group's (< tb) pad rows; four groups' extents are read
-  //     at a time
-  int32_t* src = ws + L.o_src;
-  {
-    const int wv = tid >> 6, nwv = nt >> 6, ln = tid & 63;
-    for (int g0 = 4 * wv; g0 < NGR; g0 += 4 * nwv) {
-      int st[4], ct[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        st[u] = (g0 + u < NGR) ? pad_st[g0 + u] : 0;
-        ct[u] = (g0 + u < NGR) ? pad_ct[g0 + u] : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        for (int q = ln; q < ct[u]; q += 64) src[st[u] + q] = -1;
-    }
-  }
 
   // (i) gate/up m-tiles: every X_e cut into kGuBM-row tiles, experts in
   //     rule (ii) order; one thread per tile
@@ -608,6 +603,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_place_kernel(PlanLayout L, 
   const int32_t* bpr = ws + L.o_bpr + (int64_t)(b - L.blk_off[L.r]) * E;
   const int32_t* baser = ws + L.o_baser;
   int32_t* pos = ws + L.o_pos;
+  // the padding entries of src_index: the tail of every remote group, the
+  // groups shared out over the blocks
+  {
+    const int NGR = E_l * (W - 1);
+    const int32_t* pad_st = ws + L.o_pad;
+    const int32_t* pad_ct = pad_st + E_l * W;
+    for (int gi = blockIdx.x; gi < NGR; gi += gridDim.x) {
+      const int st = pad_st[gi], ct = pad_ct[gi];
+      for (int q = threadIdx.x; q < ct; q += blockDim.x) src[st + q] = -1;
+    }
+  }
   const int lo = L.r * E_l;
   const int bits_e = bits_for(E_l + 1), bits_g = bits_for(E);
   for (int p_base = p0; p_base < p1; p_base += blockDim.x) {
@@ -678,7 +684,7 @@ hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t*
     const size_t sh_count = (size_t)(L.E_l + 2 + L.E) * sizeof(int);
     hipLaunchKernelGGL(plan_count_kernel, dim3(L.NB), dim3(kPlanThreads), sh_count, s, L, topk, ws);
   }
-  const int words = build_lds(L.W, L.E_l, L.E, L.NB, L.NB_r, L.build_stage != 0).total;
+  const int words = build_lds(L.W, L.E_l, L.E, L.NB, L.NB_r, L.band_table, L.build_stage != 0).total;
   hipLaunchKernelGGL(plan_build_kernel, dim3(1), dim3(kBuildThreads), (size_t)words * sizeof(int), s, L, ws);
   if (L.NB > 0) {
     const int nw = kPlanThreads / 64;
