@@ -130,6 +130,39 @@ def test_overlapped_combine_over_epochs(name):
         assert np.array_equal(y_first, y_serial)
 
 
+@pytest.mark.parametrize("name,mgb,cus", [("qwen3", 1, 8), ("qwen3", 4, 64), ("decode_tb32", 4, 8),
+                                          ("decode_tb64", 2, 64), ("tiny_unit", 4, 128)])
+def test_overlapped_combine_consumer_budgets(name, mgb, cus):
+    """The overlapped combine with other consumer budgets and segment merge
+    factors (§5.2, §5.3): copy units are claimed in schedule order by the
+    consumer workgroups and by producers out of tiles; over two epochs, with
+    y poisoned by NaN before each, the receive buffers are exactly the plan
+    (built with this mgb) applied to that call's own y."""
+    import moe_expert_tile_amd as m
+    c = case(name, mgb)
+    cfg, pl = c["cfg"], c["plan"]
+    say(f"[budget] {name} mgb={mgb} consumer_cus={cus}")
+    share = m.RankShare(shape_of(cfg.replace(mgb=mgb), pl.R))
+    share.plan(torch.from_numpy(c["ids"]).cuda(), dev_bf16(c["x_recv"]))
+    wgu, wd = weights(name)
+    wgu_d, wd_d = dev_bf16(wgu), dev_bf16(wd)
+    hdr = share.header()
+    assert hdr["segments"] == pl.segs["first_band"].shape[0]
+    written = OC.written_rows(pl)
+    for it in range(2):
+        share.y.fill_(float("nan"))
+        for o in range(cfg.W):
+            share.recv[o].copy_(dev_bf16(synth.foreign_rows(cfg, o)))
+        share.combine(wgu_d, wd_d, mode=m.MODE_OVERLAP, consumer_cus=cus)
+        assert share.status() == m.MOE_OK
+        Y = host_bits(share.y[:pl.M])
+        for o in range(cfg.W):
+            exp = synth.foreign_rows(cfg, o)
+            dst, src = written[o]
+            exp[dst] = Y[src]
+            assert np.array_equal(host_bits(share.recv[o][: exp.shape[0]]), exp), (it, o)
+
+
 @pytest.mark.parametrize("name", ["tiny_unit", "mixtral", "qwen3", "dsv3_skew", "decode_tb32", "decode_tb64"])
 def test_gathered_rows_equal_the_layout_path(name):
     """Gathered A rows: a plan that does not materialize the layout X, and a
