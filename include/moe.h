@@ -125,7 +125,8 @@ typedef struct moe_combine_opts {
   const void* x_recv;       /* gathered rows: when x_layout is NULL, the gate/up GEMM reads layout row m
                                straight from x_recv[src_index[m]] (device bf16 [R, d], the array given to
                                moe_plan) and padding rows as zeros, so X is never materialized; requires
-                               R*d*2 < 2^31 bytes.  Ignored when x_layout is given. */
+                               R*d*2 < 2^31 bytes; may be NULL when R = 0.  Ignored when x_layout is
+                               given. */
 } moe_combine_opts;
 
 /* Text of a status code. */

@@ -297,7 +297,8 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   if (compute) {
     if (!x_layout) {
       const int64_t a_bytes = s->recv_rows * (int64_t)s->hidden * 2;
-      if (!o.x_recv || !aligned(o.x_recv, 16) || a_bytes >= (1ll << 31)) return MOE_EINVAL;
+      if (a_bytes >= (1ll << 31)) return MOE_EINVAL;
+      if (s->recv_rows > 0 && (!o.x_recv || !aligned(o.x_recv, 16))) return MOE_EINVAL;
       a_rows = (const uint16_t*)o.x_recv;
       gathered = true;
     } else if (!aligned(x_layout, 16)) {

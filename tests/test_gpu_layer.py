@@ -104,7 +104,8 @@ EDGE_CASES = {
 def test_edge_case_rank_share(case_name):
     """Plan bit-exact; every layout row's y within tolerance; the receive
     buffers hold exactly the plan's rows; the rank's output within tolerance
-    of the oracle fed with the same receive buffer."""
+    of the oracle fed with the same receive buffer; with gathered rows (no
+    layout X) the same y and receive buffers bit for bit."""
     import moe_expert_tile_amd as m
     p = dict(EDGE_CASES[case_name])
     cfg, ids, w = _custom(**p)
@@ -148,6 +149,20 @@ def test_edge_case_rank_share(case_name):
         recv_r = host_bits(sh.recv[r])
         ref = OS.scale(recv_r, w_r, pl.pos)
         assert tol_ratio(host_bits(sh.out[:T]), ref) <= 1.0
+    # the same share with gathered rows (no layout X): the same y and the same
+    # receive buffers, bit for bit
+    recv_mat = [host_bits(t) for t in sh.recv]
+    for o in range(cfg.W):
+        sh.recv[o].copy_(dev_bf16(sentinel[o]))
+    sh.y.fill_(float("nan"))
+    sh.plan(ids_d, xr, materialize=False)
+    sh.combine(dev_bf16(wgu), dev_bf16(wd), mode=m.MODE_OVERLAP, consumer_cus=16,
+               x_recv=xr if pl.R else None)
+    assert sh.status() == m.MOE_OK
+    if pl.M:
+        assert np.array_equal(host_bits(sh.y[: pl.M]), Y[: pl.M])
+    for o in range(cfg.W):
+        assert np.array_equal(host_bits(sh.recv[o]), recv_mat[o]), o
 
 
 def test_bad_expert_id_is_reported_and_nothing_runs():
