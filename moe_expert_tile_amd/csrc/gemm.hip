@@ -177,18 +177,31 @@ __device__ __forceinline__ void stage_barrier(int n) {
 constexpr int kSchedMfma = 0x8, kSchedVmem = 0x10, kSchedDsRead = 0x100;
 
 // Tile t of a (n_mt x n_nt) grid -> (mt, nt), in a two-level order.  A
-// round of the persistent grid hands each XCD 32 consecutive tiles; those
-// form a block of 8 row tiles x 4 column tiles (12 operand blocks for 32
-// tiles in that XCD's L2).  The 8 XCDs' blocks form a chip block of
-// 8*XR row tiles x 4*(8/XR) column tiles, so that XR XCDs read the same
-// weight blocks (and 8/XR the same activation blocks) at the same time,
+// round of the persistent grid hands each XCD G/8 consecutive tiles; those
+// form a block of SR row tiles x SC column tiles with SR * SC = G/8 when G/8
+// factors so (8 x 4 for 32 producers per XCD, 6 x 5 for 30, 7 x 4 for 28;
+// else 8 x 4, not aligned with the rounds), so a round's tiles on one XCD
+// share SR + SC operand blocks in its L2.  The 8 XCDs' blocks form a chip
+// block of SR*XR row tiles x SC*(8/XR) column tiles, so that XR XCDs read the
+// same weight blocks (and 8/XR the same activation blocks) at the same time,
 // which turns more of their L2 misses into Infinity Cache hits instead of
 // HBM reads.  Chip blocks sweep the columns of a row group, row groups follow
-// one another; ragged edges give smaller blocks.  XR = 1 is the plain
-// grouped order (groups of 8 row tiles sweeping all column tiles).
-__device__ __forceinline__ void decode_tile(int t, int n_mt, int n_nt, int& mt, int& nt) {
+// one another; ragged edges give smaller blocks.
+__device__ __forceinline__ void xcd_block_shape(int per_xcd, int& SR, int& SC) {
+  SR = 8;
+  SC = 4;
+  for (int sc = 8; sc >= 2; --sc) {
+    if (per_xcd % sc == 0 && per_xcd / sc >= sc) {
+      SR = per_xcd / sc;
+      SC = sc;
+      return;
+    }
+  }
+}
+
+__device__ __forceinline__ void decode_tile(int t, int n_mt, int n_nt, int SR, int SC, int& mt, int& nt) {
   constexpr int XR = kXcdRows, XC = 8 / kXcdRows;
-  constexpr int BR = 8 * XR, BC = 4 * XC;
+  const int BR = SR * XR, BC = SC * XC;
   const int full_rg = n_mt / BR;
   int rg, rr, t1;
   if (t < full_rg * BR * n_nt) {
@@ -211,18 +224,18 @@ __device__ __forceinline__ void decode_tile(int t, int n_mt, int n_nt, int& mt, 
     cc = n_nt - full_cb * BC;
     t2 = t1 - full_cb * rr * BC;
   }
-  // 8 x 4 blocks of the chip block, column blocks outer, rows fastest inside
-  const int nsr = (rr + 7) / 8, nsc = (cc + 3) / 4;
+  // SR x SC blocks of the chip block, column blocks outer, rows fastest inside
+  const int nsr = (rr + SR - 1) / SR, nsc = (cc + SC - 1) / SC;
   mt = rg * BR;
   nt = cb * BC;
   for (int sx = 0; sx < nsc; ++sx) {
-    const int cw = min(4, cc - 4 * sx);
+    const int cw = min(SC, cc - SC * sx);
     for (int sr = 0; sr < nsr; ++sr) {
-      const int rh = min(8, rr - 8 * sr);
+      const int rh = min(SR, rr - SR * sr);
       const int n = rh * cw;
       if (t2 < n) {
-        mt += 8 * sr + t2 % rh;
-        nt += 4 * sx + t2 / rh;
+        mt += SR * sr + t2 % rh;
+        nt += SC * sx + t2 / rh;
         return;
       }
       t2 -= n;
@@ -316,6 +329,8 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   const int total = n_mt * n_nt;
   const int G = g.n_prod;   // a multiple of 8, at most kMaxProducers
   const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  int blk_r, blk_c;   // the per-XCD block of the tile order
+  xcd_block_shape(G >> 3, blk_r, blk_c);
   const int KT = g.K / C::BK;
   const int32_t* rowoff = g.ws + L.o_rowoff;
 
@@ -389,9 +404,9 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     }
     int mt, nt;
     if (t < n_mt_r * n_nt) {
-      decode_tile(t, n_mt_r, n_nt, mt, nt);
+      decode_tile(t, n_mt_r, n_nt, blk_r, blk_c, mt, nt);
     } else {
-      decode_tile(t - n_mt_r * n_nt, n_mt - n_mt_r, n_nt, mt, nt);
+      decode_tile(t - n_mt_r * n_nt, n_mt - n_mt_r, n_nt, blk_r, blk_c, mt, nt);
       mt += n_mt_r;
     }
     // row tile: its expert, first row and row limit; for the down GEMM also
