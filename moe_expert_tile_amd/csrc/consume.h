@@ -47,6 +47,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t copy_rsrc(const void* base, in
 // producer's release is not returned stale
 constexpr int kAgentLoad = 16;
 
+// cache-policy bits of the copy's stores: nt (bit 1) and sc1 (bit 4), so the
+// copied rows stream through without displacing the producers' operand lines
+// from this XCD's L2 (same-box: the Qwen3- and DeepSeek-like overlapped down
+// GEMMs ~1% faster, Mixtral-like unchanged)
+constexpr int kStreamStore = 18;
+
 #ifndef MOE_POLL_MAX_NAPS
 #define MOE_POLL_MAX_NAPS 32   // longest pause between flag polls, in units of 128 clocks
 #endif
@@ -131,7 +137,7 @@ __device__ __forceinline__ void copy_unit(const PlanLayout& L, const int32_t* ss
 #pragma unroll
   for (int k = 0; k < VPT; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b128(src, (k * NT + tid) * 16, 0, kAgentLoad);
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) __builtin_amdgcn_raw_buffer_store_b128(v[k], dst, (k * NT + tid) * 16, 0, 0);
+  for (int k = 0; k < VPT; ++k) __builtin_amdgcn_raw_buffer_store_b128(v[k], dst, (k * NT + tid) * 16, 0, kStreamStore);
 }
 
 // One consumer workgroup of NT threads; `cid` in [0, n_cons), units assigned
