@@ -237,6 +237,33 @@ def main():
     t_scale_k = amortized(lambda: share.scale(w_r))
     # standalone consumer: flags already equal the last epoch, all CUs
     t_copy = amortized(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch))
+    # ... and with only the consumer's CU budget of workgroups
+    t_copy_budget = amortized(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch,
+                                                    consumer_blocks=args.consumer_cus))
+
+    # The same kernels with a cold Infinity Cache: each launch follows a read
+    # of a 1 GiB buffer (4x the 256 MB cache; a read leaves no dirty lines to
+    # write back during the kernel), and the reads' own time, measured alone,
+    # is subtracted.
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+
+    def amortized_cold(fn, n=20):
+        def run(with_fn):
+            share.combine(wgu_d, wd_d, mode=m.MODE_SERIAL)
+            e0, e1 = m.timing_events(2)
+            e0.record(stream)
+            for _ in range(n):
+                flush_buf.max()
+                if with_fn:
+                    fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e-3
+        return max(0.0, run(True) - run(False)) / n
+
+    t_scale_cold = amortized_cold(lambda: share.scale(w_r))
+    t_copy_cold = amortized_cold(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch))
+    del flush_buf
     st = share.status()
     if st != m.MOE_OK:
         raise SystemExit(f"device status after standalone launches: {m.status_string(st)}")
@@ -325,6 +352,9 @@ def main():
             "expert_combine": round(t_ec * 1e6, 2), "scale_in_step": round(t_scale * 1e6, 2),
             "plan_back_to_back": round(t_plan_k * 1e6, 2), "scale_back_to_back": round(t_scale_k * 1e6, 2),
             "consumer_standalone_back_to_back": round(t_copy * 1e6, 2),
+            "consumer_standalone_at_budget": round(t_copy_budget * 1e6, 2),
+            "consumer_standalone_cold_cache": round(t_copy_cold * 1e6, 2),
+            "scale_cold_cache": round(t_scale_cold * 1e6, 2),
         },
         "rates": {
             "gateup_TFLOPs": round(gu_tflops / 1e12, 2),
@@ -335,6 +365,9 @@ def main():
             "plan_frac_hbm": round(work["plan_bytes"] / t_plan_k / PEAK_HBM, 4),
             "combine_frac_hbm": round(work["combine_bytes"] / t_copy / PEAK_HBM, 4),
             "scale_frac_hbm": round(work["scale_bytes"] / t_scale_k / PEAK_HBM, 4),
+            "combine_at_budget_GBs": round(work["combine_bytes"] / t_copy_budget / 1e9, 1),
+            "combine_frac_hbm_cold": round(work["combine_bytes"] / t_copy_cold / PEAK_HBM, 4) if t_copy_cold else None,
+            "scale_frac_hbm_cold": round(work["scale_bytes"] / t_scale_cold / PEAK_HBM, 4) if t_scale_cold else None,
             "down_frac_mfma": round(work["down_flop"] / t_dn / PEAK_BF16, 4),
             "routed_rows_per_s": round(R / (ms * 1e-3), 1),
         },
