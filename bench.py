@@ -243,23 +243,19 @@ def main():
 
     # The same kernels with a cold Infinity Cache: each launch follows a read
     # of a 1 GiB buffer (4x the 256 MB cache; a read leaves no dirty lines to
-    # write back during the kernel), and the reads' own time, measured alone,
-    # is subtracted.
+    # write back during the kernel) and is timed alone by its own pair of
+    # events (it is queued while the read runs); median of n launches.
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
 
-    def amortized_cold(fn, n=20):
-        def run(with_fn):
-            share.combine(wgu_d, wd_d, mode=m.MODE_SERIAL)
-            e0, e1 = m.timing_events(2)
-            e0.record(stream)
-            for _ in range(n):
-                flush_buf.max()
-                if with_fn:
-                    fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e-3
-        return max(0.0, run(True) - run(False)) / n
+    def amortized_cold(fn, n=15):
+        evs = [m.timing_events(2) for _ in range(n)]
+        for a, b in evs:
+            flush_buf.max()
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e-3
 
     t_scale_cold = amortized_cold(lambda: share.scale(w_r))
     t_copy_cold = amortized_cold(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch))
