@@ -78,9 +78,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #define MOE_DN_SB 2
 #endif
 #ifndef MOE_STORE_AUX
-// cache-policy bits of the down GEMM's output stores: sc1 (bit 4), agent
-// scope, writes through this XCD's L2, so the tile's release finds little to
-// write back (measured 3-20% faster than the default policy)
+// cache-policy bits of the down GEMM's output stores: sc1 (bit 4), device
+// scope, written through this XCD's L2; the flag publication relies on it
+// (measured 3-20% faster than the default policy even with a release fence)
 #define MOE_STORE_AUX 16
 #endif
 #ifndef MOE_LOAD_AUX
@@ -769,13 +769,22 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
           }
         }
       }
-      // every wave's stores have reached L2; then one release at agent
-      // scope (L2 write-back) before the flags of this tile are set
+      // Publication.  Every row this tile hands to the consumer was stored
+      // at device scope (sc1: written through this XCD's L2 to the memory
+      // side, the point where all XCDs' agent-scope loads meet; the same
+      // instruction form as a relaxed agent-scope atomic store), and each
+      // wave waits until its stores are acknowledged; after the barrier one
+      // lane sets the flags with agent-scope stores.  So the data is visible
+      // to every XCD before any flag is, without the L2 write-back an
+      // agent-scope release fence would add: that write-back (buffer_wbl2)
+      // only matters for ordinary write-back stores, and walking the L2 once
+      // per tile cost 7-10% of the short-K down GEMMs.  The consumer's side
+      // is an agent-scope acquire (L2 invalidate) and sc1 loads.
+      static_assert((MOE_STORE_AUX & 16) != 0, "flag publication needs device-scope (sc1) output stores");
       wait_vm0();
       if constexpr (FLAGS) {
         __syncthreads();
         if (tid == 0) {
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
           if (L.dn_merge > 0) {
             // one flag per covered band (a band has n_nt flags, one per column tile)
             for (int b = 0; b < nbt; ++b)
