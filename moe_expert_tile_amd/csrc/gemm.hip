@@ -86,6 +86,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #ifndef MOE_LOAD_AUX
 #define MOE_LOAD_AUX 0   // cache-policy bits of the operand loads (default policy measured best)
 #endif
+constexpr int kDeviceScope = 16;   // sc1 cache-policy bit: device scope, written through the XCD's L2
 constexpr int kXcdRows = MOE_XCD_ROWS;
 static_assert(kXcdRows == 1 || kXcdRows == 2 || kXcdRows == 4 || kXcdRows == 8, "XCD rows");
 
@@ -587,20 +588,27 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       // 2*slot + piece, [float4 c][thread]), publish them, count this piece's
       // K steps on the tile's epoch-tagged counter; the piece that completes
       // KT adds every other piece's partials and goes on to the epilogue.
-      float4* mine = (float4*)(sk_part + (int64_t)(2 * slot + piece) * C::BM * C::BN);
+      // Published like the down GEMM's tiles: device-scope (sc1) stores,
+      // acknowledged by every wave before the counter update, and read back
+      // with sc1 loads, so no L2 write-back is needed.
+      const __amdgpu_buffer_rsrc_t mine =
+          make_rsrc(sk_part + (int64_t)(2 * slot + piece) * C::BM * C::BN, (int64_t)C::BM * C::BN * 4);
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
 #pragma unroll
         for (int j = 0; j < C::FM; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            mine[((i * C::FM + j) * 4 + q) * C::NT + tid] =
-                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          for (int q = 0; q < 4; ++q) {
+            v4u32 pv;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) pv[c] = __float_as_uint(acc[i][j][4 * q + c]);
+            __builtin_amdgcn_raw_buffer_store_b128(pv, mine, (((i * C::FM + j) * 4 + q) * C::NT + tid) * 16, 0,
+                                                   kDeviceScope);
+          }
       wait_vm0();
       __syncthreads();   // also: every wave is done with the LDS ring
       int* s_last = (int*)lds;
       if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         uint64_t* ctr = sk_ctr + sk_j;
         uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         uint32_t cnt;
@@ -652,7 +660,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
               for (int q = 0; q < 4; ++q) {
                 if (h + i < C::FN)
                   ld[i][j][q] = __builtin_amdgcn_raw_buffer_load_b128(
-                      prs, (((h + i) * C::FM + j) * 4 + q) * C::NT * 16 + tid * 16, 0, 16);
+                      prs, (((h + i) * C::FM + j) * 4 + q) * C::NT * 16 + tid * 16, 0, kDeviceScope);
               }
 #pragma unroll
           for (int i = 0; i < FH; ++i)
@@ -780,7 +788,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       // only matters for ordinary write-back stores, and walking the L2 once
       // per tile cost 7-10% of the short-K down GEMMs.  The consumer's side
       // is an agent-scope acquire (L2 invalidate) and sc1 loads.
-      static_assert((MOE_STORE_AUX & 16) != 0, "flag publication needs device-scope (sc1) output stores");
+      static_assert((MOE_STORE_AUX & kDeviceScope) != 0, "flag publication needs device-scope (sc1) output stores");
       wait_vm0();
       if constexpr (FLAGS) {
         __syncthreads();
