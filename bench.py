@@ -191,11 +191,17 @@ def main():
     st = share.status()
     if st != m.MOE_OK:
         raise SystemExit(f"device status after warmup: {m.status_string(st)}")
+    # the timed steps carry no events (an event record between two kernels
+    # can cost GPU time); the per-stage times come from the same number of
+    # steps again, each ABI call between its own pair of events
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     st = share.status()
     if st != m.MOE_OK:
         raise SystemExit(f"device status after timed steps: {m.status_string(st)}")
