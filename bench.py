@@ -53,14 +53,30 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemm_mixtral_traffic.txt")
-GEMM_SOURCE = os.path.join(ROOT, "moe_expert_tile_amd", "csrc", "gemm.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "moe_expert_tile_amd", "csrc", n)
+                for n in ("gemm.hip", "consume.h", "moe_internal.h")]
+
+
+def gemm_code_digest():
+    """sha256 of the GEMM kernel's sources with comments and whitespace
+    removed: counters taken on one revision stay valid across comment-only
+    edits and become void on any change to the code."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        src = open(path).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
+        h.update(b"\0")
+    return h.hexdigest()
 
 
 def measured_traffic(workload):
     """HBM bytes per gate/up GEMM launch from the committed counter summary,
     or None when there is none for this workload or the kernel source has
     changed since the counters were taken."""
-    import hashlib
     if workload != "mixtral" or not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -68,8 +84,7 @@ def measured_traffic(workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-    if kv.get("gemm_source_sha256") != sha:
+    if kv.get("gemm_code_sha256") != gemm_code_digest():
         return None
     f_fetch = float(kv["copy_bytes"]) / (1024.0 * float(kv["copy_fetch_kib"]))
     f_write = float(kv["copy_bytes"]) / (1024.0 * float(kv["copy_write_kib"]))

@@ -170,9 +170,11 @@ int moe_plan(const moe_shape* shape, const int32_t* topk_ids, const uint16_t* x_
  * the combine.  The gate/up GEMM writes h = silu(X W_gate^T) * (X W_up^T)
  * (fp32 accumulation, h rounded once to bf16).  The down GEMM takes its tiles
  * in schedule order (workgroup i takes tiles i, i+g, ...; §5.1), writes
- * y = h W_down^T (bf16) and, in its epilogue, releases the tile and sets
- * flags[tile] = epoch.  The consumer waits (acquire, bounded) until every
- * tile of a remote segment is flagged and copies the segment's valid rows to
+ * y = h W_down^T (bf16) and, in its epilogue, publishes the tile: its rows
+ * are stored at device scope and acknowledged before flags[tile] = epoch is
+ * set, so they are visible on every XCD first.  The consumer waits (bounded)
+ * until every tile of a remote segment is flagged, reads the rows at device
+ * scope and copies the segment's valid rows to
  * recv[dst] + dst_off*d; padding rows are never copied.  Rows of local bands
  * (destination r) never leave the rank: the down GEMM's epilogue writes them
  * into recv[r] itself, besides y.

@@ -20,8 +20,8 @@
 //     per operand, 16-byte chunks XOR-swizzled so that the ds_read_b128
 //     operand fetches are bank-conflict free on the 64-bank LDS.
 //   * Epilogues: gate/up stores h from registers; the down GEMM stages its
-//     tile through LDS and writes whole lines with write-through stores, then
-//     releases the tile and sets its flags.
+//     tile through LDS and writes whole lines with device-scope
+//     (write-through) stores, waits for them, then sets the tile's flags.
 //   * Persistent grid (a multiple of 8 workgroups).  Workgroup w runs on XCD
 //     w mod 8; it takes slot (w mod 8) * (G/8) + w/8 of every round of G
 //     tiles, so each XCD works on a contiguous run of the tile order, and the
