@@ -5,11 +5,18 @@
 // One wavefront per run of 256 16-byte output vectors of a token: each lane
 // keeps 4k row loads in flight (each a contiguous 1 KB access across the
 // wavefront), fp32 fused multiply-adds in slot order, one round-to-nearest-
-// even conversion per value, 16-byte stores.
+// even conversion per value, 16-byte stores.  The returned rows are read
+// once, mostly from HBM, with nontemporal loads: measured 4-9% faster in the
+// step and 3-8% with a cold Infinity Cache, though 10% slower when the rows
+// are still in that cache.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
+
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+constexpr int kBufWord3 = 0x00020000;   // raw buffer access: data format 32, other fields zero
+constexpr int kNontemporal = 2;         // nt cache-policy bit
 
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
@@ -44,10 +51,15 @@ __global__ __launch_bounds__(256) void scale_kernel(PlanLayout L, const int32_t*
       for (int c = 0; c < 8; ++c) acc[q][c] = 0.f;
     for (int j = 0; j < k; ++j) {
       const float wj = w[t * k + j];
-      const uint4* row = recv + (int64_t)pos[t * k + j] * vec;
+      // one row: loads past its end (a ragged last run) read zeros
+      const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(recv + (int64_t)pos[t * k + j] * vec), (short)0, (int)(vec * 16), kBufWord3);
       uint4 x[VPT];
 #pragma unroll
-      for (int q = 0; q < VPT; ++q) x[q] = (v0 + 64 * q < vec) ? row[v0 + 64 * q] : make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < VPT; ++q) {
+        const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(row, (int)((v0 + 64 * q) * 16), 0, kNontemporal);
+        x[q] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
 #pragma unroll
       for (int q = 0; q < VPT; ++q) {
         acc[q][0] = fmaf(wj, bf_lo(x[q].x), acc[q][0]);
