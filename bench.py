@@ -280,6 +280,15 @@ def main():
 
     t_scale_cold = amortized_cold(lambda: share.scale(w_r))
     t_copy_cold = amortized_cold(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch))
+    # context for the copy: the runtime's own device-to-device copy of as
+    # many bytes as the consumer reads (and writes), timed the same way
+    half = int(work["combine_bytes"]) // 2
+    t_dev_copy_cold = None
+    if half > 0:
+        cp_src = torch.empty(half, dtype=torch.uint8, device="cuda")
+        cp_dst = torch.empty_like(cp_src)
+        t_dev_copy_cold = amortized_cold(lambda: cp_dst.copy_(cp_src))
+        del cp_src, cp_dst
     del flush_buf
     st = share.status()
     if st != m.MOE_OK:
@@ -371,6 +380,7 @@ def main():
             "consumer_standalone_back_to_back": round(t_copy * 1e6, 2),
             "consumer_standalone_at_budget": round(t_copy_budget * 1e6, 2),
             "consumer_standalone_cold_cache": round(t_copy_cold * 1e6, 2),
+            "device_copy_same_bytes_cold_cache": round(t_dev_copy_cold * 1e6, 2) if t_dev_copy_cold else None,
             "scale_cold_cache": round(t_scale_cold * 1e6, 2),
         },
         "rates": {
@@ -384,6 +394,8 @@ def main():
             "scale_frac_hbm": round(work["scale_bytes"] / t_scale_k / PEAK_HBM, 4),
             "combine_at_budget_GBs": round(work["combine_bytes"] / t_copy_budget / 1e9, 1),
             "combine_frac_hbm_cold": round(work["combine_bytes"] / t_copy_cold / PEAK_HBM, 4) if t_copy_cold else None,
+            "device_copy_frac_hbm_cold": (round(work["combine_bytes"] / t_dev_copy_cold / PEAK_HBM, 4)
+                                          if t_dev_copy_cold else None),
             "scale_frac_hbm_cold": round(work["scale_bytes"] / t_scale_cold / PEAK_HBM, 4) if t_scale_cold else None,
             "down_frac_mfma": round(work["down_flop"] / t_dn / PEAK_BF16, 4),
             "routed_rows_per_s": round(R / (ms * 1e-3), 1),

@@ -179,8 +179,11 @@ __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_
 // have run out of tiles join them, so the dedicated consumer can be small
 // and the copies left when the last tiles finish are shared by every CU.
 // Each workgroup asks for its next claim while it copies the current one.
+// A claim is 8 units (256 KB): against 2-unit claims the overlapped down
+// GEMM measured 0.7-1.6% faster (fewer atomics on one word while it runs),
+// and the copy's tail after the last producer stayed at 1-3 us.
 // `s_word` is two ints of the caller's LDS.
-constexpr int kClaimUnits = 2;
+constexpr int kClaimUnits = 8;
 
 template <int NT>
 __device__ void consume_claimed(const PlanLayout& L, int32_t* ws, const uint16_t* __restrict__ y,
