@@ -179,11 +179,13 @@ __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_
 // have run out of tiles join them, so the dedicated consumer can be small
 // and the copies left when the last tiles finish are shared by every CU.
 // Each workgroup asks for its next claim while it copies the current one.
-// A claim is 8 units (256 KB): against 2-unit claims the overlapped down
-// GEMM measured 0.7-1.6% faster (fewer atomics on one word while it runs),
-// and the copy's tail after the last producer stayed at 1-3 us.
+// A claim is U / (2 x the launch's workgroups) units, between 1 and 8: on
+// large layers 8-unit claims (256 KB) made the overlapped down GEMM
+// 0.7-1.6% faster than 2-unit ones (fewer atomics on one word while it
+// runs), but a decode-size layer has only ~130 units, and a few long claims
+// copied one unit after another left a 25 us tail after the last producer.
 // `s_word` is two ints of the caller's LDS.
-constexpr int kClaimUnits = 8;
+constexpr int kClaimUnitsMax = 8;
 
 template <int NT>
 __device__ void consume_claimed(const PlanLayout& L, int32_t* ws, const uint16_t* __restrict__ y,
@@ -200,7 +202,8 @@ __device__ void consume_claimed(const PlanLayout& L, int32_t* ws, const uint16_t
   const int32_t* sunit = ws + L.o_sunit;
   const int n_rs = hdr[H_RSEGS];
   const int U = sunit[n_rs];
-  const int n_claims = (U + kClaimUnits - 1) / kClaimUnits;
+  const int cu = max(1, min(kClaimUnitsMax, U / (2 * (int)gridDim.x)));   // units per claim
+  const int n_claims = (U + cu - 1) / cu;
   const int tid = threadIdx.x;
   if (tid == 0) s_word[1] = __hip_atomic_fetch_add(hdr + H_CLAIM, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -210,9 +213,8 @@ __device__ void consume_claimed(const PlanLayout& L, int32_t* ws, const uint16_t
   while (k < n_claims) {
     // the next claim is in flight while this one is copied
     if (tid == 0) s_word[1] = __hip_atomic_fetch_add(hdr + H_CLAIM, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int j = 0; j < kClaimUnits; ++j) {
-      const int u = k * kClaimUnits + j;
+    for (int j = 0; j < cu; ++j) {
+      const int u = k * cu + j;
       if (u < U) {
         seg = segment_of_unit(sunit, n_rs, seg, u);
         if (seg != ready) {

@@ -387,7 +387,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     }
   }
 
-  int t_dp = slot, piece = 0;
+  int t_dp = slot, piece = 0, items = 0;
   for (;;) {
     // next work item: a whole tile, or a piece [kb, ke) of a stream-K tile
     int t, kb = 0, ke = KT, sk_j = -1;
@@ -403,6 +403,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     } else {
       break;
     }
+    ++items;
     int mt, nt;
     if (t < n_mt_r * n_nt) {
       decode_tile(t, n_mt_r, n_nt, blk_r, blk_c, mt, nt);
@@ -808,10 +809,14 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   }
   if constexpr (FLAGS) {
     if (tid == 0) stamp_max(hdr, H_T_PROD_END);
-    if (overlapped) {
+    if (overlapped && items > 0) {
       // out of tiles: help copy the remaining remote segments, but only once
       // every producer has started -- a producer still waiting for a CU could
-      // otherwise be kept from it by workgroups that wait for its tiles
+      // otherwise be kept from it by workgroups that wait for its tiles.
+      // A producer that got no tile at all (a grid larger than the tile
+      // count) leaves instead: joining at once, it would only poll flags
+      // beside the producers still computing (measured on a decode-size
+      // layer: 5 us slower down GEMM).
       __syncthreads();   // every wave is done with the LDS ring
       int* s_word = (int*)lds;
       if (tid == 0) s_word[0] = __hip_atomic_load(hdr + H_STARTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
