@@ -115,8 +115,9 @@ enum {
 typedef struct moe_combine_opts {
   int32_t mode;             /* MOE_MODE_* */
   int32_t consumer_cus;     /* OVERLAP: CUs given to the consumer, multiple of 8 in [8, 128]; 0 = 16 */
-  int32_t consumer_blocks;  /* workgroups of the consumer; 0 = consumer_cus (OVERLAP) or one per
-                               32 KiB copy unit, bounded on the host (SERIAL, COPY_ONLY) */
+  int32_t consumer_blocks;  /* workgroups of the consumer; 0 = consumer_cus (OVERLAP: at most
+                               consumer_cus, MOE_EINVAL above) or one per 32 KiB copy unit,
+                               bounded on the host (SERIAL, COPY_ONLY) */
   int32_t reserved;
   int64_t spin_timeout_ns;  /* bound on the consumer's wait for one segment's flags; 0 = 2 s */
   void* events[6];          /* optional hipEvent_t, recorded on `stream`: [0]/[1] around the gate/up GEMM,

@@ -286,6 +286,8 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   if (o.consumer_cus == 0) o.consumer_cus = 16;
   if (o.consumer_cus < 8 || o.consumer_cus > 128 || o.consumer_cus % 8 != 0) return MOE_EINVAL;
   if (o.consumer_blocks < 0 || o.consumer_blocks > 65536) return MOE_EINVAL;
+  // OVERLAP: each consumer workgroup must have a reserved CU of its own
+  if (o.mode == MOE_MODE_OVERLAP && o.consumer_blocks > o.consumer_cus) return MOE_EINVAL;
   if (o.spin_timeout_ns < 0) return MOE_EINVAL;
   if (epoch == 0) return MOE_EINVAL;
   if (!plan_ws || !aligned(plan_ws, 256)) return MOE_EINVAL;

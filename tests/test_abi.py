@@ -88,6 +88,10 @@ def test_bad_pointers_are_rejected_before_any_hip_call():
                              consumer_cus=12, stream=0)
     assert ei.value.status == m.MOE_EINVAL                        # not a multiple of 8
     with pytest.raises(m.MoEError) as ei:
+        m.moe_expert_combine(s, good, good, good, good, good, good, good, 1, [good] * 4,
+                             consumer_cus=16, consumer_blocks=17, stream=0)
+    assert ei.value.status == m.MOE_EINVAL                        # more consumer workgroups than CUs
+    with pytest.raises(m.MoEError) as ei:
         m.moe_expert_combine(s, good, good, good, good, good, good, good, 1, [good, 0, good, good],
                              stream=0)
     assert ei.value.status == m.MOE_EINVAL                        # null receive buffer
