@@ -348,7 +348,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   // runs the tile's epilogue.
   int full = total, sk_tiles = 0, G_sk = 0;
   int64_t W_sk = 0;
-  if (L.sk_slots >= 2 * G && total > 0 && KT >= kMinSkKT) {
+  if (L.sk_slots >= 2 * G && total > 0 && (KT >= kMinSkKT || (2 * total <= G && KT >= kMinSkKTOneRound))) {
     const int rem = total % G;
     if (rem != 0 && 4 * rem <= 3 * G) {
       full = total - rem;

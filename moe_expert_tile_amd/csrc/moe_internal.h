@@ -17,12 +17,19 @@ constexpr int kGuBN = 256;             // gate/up GEMM tile cols (128 gate + 128
 constexpr int kDnBN = 256;             // down GEMM tile cols
 constexpr int kMaxProducers = 256;     // persistent GEMM workgroups at most (one per CU on MI355X)
 constexpr int kMinSkSteps = 16;        // shortest K range of a stream-K piece
-// stream-K only for tiles of at least this many K steps.  Measured: with 24-112
-// steps (the Qwen3- and DeepSeek-like GEMMs, and decode's 32-step gate/up on
-// 96 of 256 CUs) the partials' round trip through memory, limited by each
-// CU's ~35 GB/s load pipeline like the tiles themselves, cost as much as the
-// tail round it removes or more.
+// stream-K for a tail round only with tiles of at least this many K steps.
+// Measured: with 24-112 steps behind full rounds (the Qwen3- and
+// DeepSeek-like GEMMs) the partials' round trip through memory, limited by
+// each CU's ~35 GB/s load pipeline like the tiles themselves, costs as much
+// as the tail round it removes or more (Qwen3-like gate/up +1-2%, down +8%).
 constexpr int kMinSkKT = 128;
+// ... but a GEMM whose tiles fill at most half of one round is split along
+// K from 2 * kMinSkSteps steps on, so that each tile gets pieces of at most
+// half its steps (decode's 120 gate/up tiles of 32 steps on 256 CUs:
+// 59 -> 55 us; its 190 tiles at tb_M 64, three quarters of a round, went
+// 62 -> 80 us).  With at least that many steps a piece never spans more
+// than two tiles.
+constexpr int kMinSkKTOneRound = 2 * kMinSkSteps;
 
 // header words of the plan workspace (mirrors the public description)
 enum Hdr {
