@@ -555,6 +555,10 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       read_frags(0, 0);
       if constexpr (ISSUE_SH) issue_shallow(kt + C::S_SHALLOW - 1);
       if constexpr (ISSUE_DP) issue_deep(kt + C::S_DEEP - 1);
+      // gate/up: this wave's MFMA block at raised wave priority, so the other
+      // wave of the SIMD does not delay it (Mixtral-like gate/up 1758 ->
+      // 1745 us; the down GEMM got 4-5% slower with it, so only here)
+      if constexpr (SWIGLU) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk) {
         if (kk + 1 < C::KK) read_frags(kk + 1, (kk + 1) & 1);
@@ -564,6 +568,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
           for (int j = 0; j < C::FM; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pw[kk & 1][i], px[kk & 1][j], acc[i][j], 0, 0, 0);
       }
+      if constexpr (SWIGLU) __builtin_amdgcn_s_setprio(0);
       constexpr int NVMEM = (ISSUE_SH ? (C::SA <= C::SB ? C::A_LOADS : C::B_LOADS) : 0) +
                             (ISSUE_DP ? (C::SA <= C::SB ? C::B_LOADS : C::A_LOADS) : 0);
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::FN + C::FM, 0);
