@@ -258,6 +258,9 @@ def main():
     t_scale_k = amortized(lambda: share.scale(w_r))
     # standalone consumer: flags already equal the last epoch, all CUs
     t_copy = amortized(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch))
+    # the per-row ablation of the copy (every remote row routed and copied
+    # on its own, as without the owner-aligned layout), all CUs
+    t_rows = amortized(lambda: share.combine(None, None, mode=m.MODE_COPY_ROWS, epoch=share.epoch))
     # ... and with only the consumer's CU budget of workgroups
     t_copy_budget = amortized(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch,
                                                     consumer_blocks=args.consumer_cus))
@@ -280,6 +283,7 @@ def main():
 
     t_scale_cold = amortized_cold(lambda: share.scale(w_r))
     t_copy_cold = amortized_cold(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch))
+    t_rows_cold = amortized_cold(lambda: share.combine(None, None, mode=m.MODE_COPY_ROWS, epoch=share.epoch))
     # context for the copy: the runtime's own device-to-device copy of as
     # many bytes as the consumer reads (and writes), timed the same way
     half = int(work["combine_bytes"]) // 2
@@ -380,6 +384,8 @@ def main():
             "consumer_standalone_back_to_back": round(t_copy * 1e6, 2),
             "consumer_standalone_at_budget": round(t_copy_budget * 1e6, 2),
             "consumer_standalone_cold_cache": round(t_copy_cold * 1e6, 2),
+            "consumer_per_row_back_to_back": round(t_rows * 1e6, 2),
+            "consumer_per_row_cold_cache": round(t_rows_cold * 1e6, 2),
             "device_copy_same_bytes_cold_cache": round(t_dev_copy_cold * 1e6, 2) if t_dev_copy_cold else None,
             "scale_cold_cache": round(t_scale_cold * 1e6, 2),
         },
@@ -394,6 +400,9 @@ def main():
             "scale_frac_hbm": round(work["scale_bytes"] / t_scale_k / PEAK_HBM, 4),
             "combine_at_budget_GBs": round(work["combine_bytes"] / t_copy_budget / 1e9, 1),
             "combine_frac_hbm_cold": round(work["combine_bytes"] / t_copy_cold / PEAK_HBM, 4) if t_copy_cold else None,
+            "combine_per_row_frac_hbm": round(work["combine_bytes"] / t_rows / PEAK_HBM, 4) if t_rows else None,
+            "combine_per_row_frac_hbm_cold": (round(work["combine_bytes"] / t_rows_cold / PEAK_HBM, 4)
+                                              if t_rows_cold else None),
             "device_copy_frac_hbm_cold": (round(work["combine_bytes"] / t_dev_copy_cold / PEAK_HBM, 4)
                                           if t_dev_copy_cold else None),
             "scale_frac_hbm_cold": round(work["scale_bytes"] / t_scale_cold / PEAK_HBM, 4) if t_scale_cold else None,

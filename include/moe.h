@@ -109,7 +109,11 @@ typedef struct moe_plan_view {
 enum {
   MOE_MODE_OVERLAP = 0,   /* down GEMM and consumer run concurrently on disjoint CUs, one launch (§5.3) */
   MOE_MODE_SERIAL = 1,    /* down GEMM to completion, then the consumer on all CUs (serial baseline) */
-  MOE_MODE_COPY_ONLY = 2  /* only the consumer, on the caller's stream; flags must already equal `epoch` */
+  MOE_MODE_COPY_ONLY = 2, /* only the consumer, on the caller's stream; flags must already equal `epoch` */
+  MOE_MODE_COPY_ROWS = 3  /* like COPY_ONLY, but the per-row ablation of the copy (tile-signal notes
+                             §4.3, the alternative to the owner-aligned layout): each remote row is
+                             routed and copied on its own, one wavefront per row, after its band's
+                             flags; same result as the consumer, for measurement */
 };
 
 typedef struct moe_combine_opts {

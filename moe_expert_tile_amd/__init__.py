@@ -21,7 +21,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ECAPACITY, MOE_EHIP, MOE_ETIMEOUT, MOE_EROUTING, MOE_EUNSUPPORTED = range(7)
-MODE_OVERLAP, MODE_SERIAL, MODE_COPY_ONLY = 0, 1, 2
+MODE_OVERLAP, MODE_SERIAL, MODE_COPY_ONLY, MODE_COPY_ROWS = 0, 1, 2, 3
 
 HDR_FIELDS = ["error", "M", "bands", "remote_bands", "segments", "remote_segments",
               "gateup_tiles", "down_tiles", "copy_units", "received_rows", "gateup_row_tiles",

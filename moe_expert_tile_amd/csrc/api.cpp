@@ -282,7 +282,7 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   moe_combine_opts o;
   memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
-  if (o.mode < MOE_MODE_OVERLAP || o.mode > MOE_MODE_COPY_ONLY) return MOE_EINVAL;
+  if (o.mode < MOE_MODE_OVERLAP || o.mode > MOE_MODE_COPY_ROWS) return MOE_EINVAL;
   if (o.consumer_cus == 0) o.consumer_cus = 16;
   if (o.consumer_cus < 8 || o.consumer_cus > 128 || o.consumer_cus % 8 != 0) return MOE_EINVAL;
   if (o.consumer_blocks < 0 || o.consumer_blocks > 65536) return MOE_EINVAL;
@@ -291,7 +291,7 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   if (o.spin_timeout_ns < 0) return MOE_EINVAL;
   if (epoch == 0) return MOE_EINVAL;
   if (!plan_ws || !aligned(plan_ws, 256)) return MOE_EINVAL;
-  const bool compute = (o.mode != MOE_MODE_COPY_ONLY);
+  const bool compute = (o.mode != MOE_MODE_COPY_ONLY && o.mode != MOE_MODE_COPY_ROWS);
   // A rows of the gate/up GEMM: the materialized layout, or gathered from
   // x_recv through src_index (padding rows read past the buffer's bound)
   const uint16_t* a_rows = x_layout;
@@ -332,6 +332,12 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   full_grid -= full_grid % 8;
   if (full_grid < 8) full_grid = 8;
 
+  if (o.mode == MOE_MODE_COPY_ROWS) {
+    record(o.events[4], st);
+    rc = hip_rc(launch_consumer_rows(L, ws_rw, y, flags, epoch, rp, timeout, st));
+    record(o.events[5], st);
+    return rc;
+  }
   if (o.mode == MOE_MODE_COPY_ONLY) {
     record(o.events[4], st);
     rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, timeout, o.consumer_blocks ? o.consumer_blocks : consumer_grid(L),

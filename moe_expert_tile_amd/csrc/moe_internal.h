@@ -137,6 +137,9 @@ hipError_t launch_down(const PlanLayout& L, int32_t* ws, const uint16_t* h, cons
 hipError_t launch_consumer(const PlanLayout& L, int32_t* ws, const uint16_t* y,
                            const uint32_t* flags, uint32_t epoch, const RecvPtrs& recv,
                            int64_t timeout_ticks, int grid, hipStream_t s);
+// per-row ablation of the copy: one wavefront per remote row (COPY_ROWS mode)
+hipError_t launch_consumer_rows(const PlanLayout& L, int32_t* ws, const uint16_t* y, const uint32_t* flags,
+                                uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks, hipStream_t s);
 hipError_t launch_scale(const PlanLayout& L, const int32_t* ws, const uint16_t* recv_self,
                         const float* topk_w, uint16_t* out, hipStream_t s);
 

@@ -10,6 +10,8 @@
   layout row; repeated overlapped epochs without a flag reset, with y
   poisoned by NaN before each call, copy exactly their own y and give the
   same y again; serial and overlapped y agree within the tolerance.
+* Per-row copy (the §4.3 alternative to the layout, as an ablation): the
+  remote rows copied one per wavefront give the segment copy's bits.
 * Gathered rows: the gate/up GEMM reading the layout's rows from x_recv
   through src_index instead of a materialized X gives the same bits.
 * Scale (§2.2 step 5): sampled tokens of the rank's own output against the
@@ -92,6 +94,30 @@ def test_combine_writes_exactly_the_plan(name):
         exp[dst] = Y[src]
         got = host_bits(share.recv[o][: exp.shape[0]])
         assert np.array_equal(got, exp), f"owner {o}"
+
+
+@pytest.mark.parametrize("name", ["tiny_unit", "mixtral", "qwen3", "decode_tb32", "dsv3_skew"])
+def test_per_row_copy_equals_the_segment_copy(name):
+    """The per-row ablation of the copy (the notes' alternative to the
+    owner-aligned layout, §4.3: every row routed on its own at transfer
+    time): with the remote owners' buffers refilled, copying the remote rows
+    one per wavefront leaves every buffer bit for bit as the plan applied to
+    y -- the same result as the segment consumer."""
+    import moe_expert_tile_amd as m
+    c, share, _, _ = planned(name, m.MODE_OVERLAP)
+    cfg, pl = c["cfg"], c["plan"]
+    for o in range(cfg.W):
+        if o != cfg.rank:
+            share.recv[o].copy_(dev_bf16(synth.foreign_rows(cfg, o)))
+    share.combine(None, None, mode=m.MODE_COPY_ROWS, epoch=share.epoch)
+    assert share.status() == m.MOE_OK
+    Y = host_bits(share.y[:pl.M])
+    written = OC.written_rows(pl)
+    for o in range(cfg.W):
+        exp = synth.foreign_rows(cfg, o)
+        dst, src = written[o]
+        exp[dst] = Y[src]
+        assert np.array_equal(host_bits(share.recv[o][: exp.shape[0]]), exp), f"owner {o}"
 
 
 @pytest.mark.parametrize("name", ["tiny_unit", "mixtral", "qwen3", "decode_tb32", "dsv3_skew"])
