@@ -91,6 +91,15 @@ def test_bad_pointers_are_rejected_before_any_hip_call():
         m.moe_expert_combine(s, good, good, good, good, good, good, good, 1, [good] * 4,
                              consumer_cus=16, consumer_blocks=17, stream=0)
     assert ei.value.status == m.MOE_EINVAL                        # more consumer workgroups than CUs
+    for bad_mode in (-1, 4):
+        with pytest.raises(m.MoEError) as ei:
+            m.moe_expert_combine(s, good, good, good, good, good, good, good, 1, [good] * 4,
+                                 mode=bad_mode, stream=0)
+        assert ei.value.status == m.MOE_EINVAL                    # no such mode
+    with pytest.raises(m.MoEError) as ei:
+        m.moe_expert_combine(s, good, None, None, None, None, None, good, 1, [good] * 4,
+                             mode=m.MODE_COPY_ROWS, stream=0)
+    assert ei.value.status == m.MOE_EINVAL                        # per-row copy without y
     with pytest.raises(m.MoEError) as ei:
         m.moe_expert_combine(s, good, good, good, good, good, good, good, 1, [good, 0, good, good],
                              stream=0)
