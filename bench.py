@@ -1,18 +1,21 @@
 """Benchmark: one expert-parallel rank's share of an MoE layer on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input:
-moe_plan (owner-aligned layout, remote-first schedule, combine plan) ->
-moe_expert_combine (gate/up GEMM + SwiGLU, down GEMM with tile flags in
+moe_plan (owner-aligned layout, remote-first schedule, combine plan, layout
+X) -> moe_expert_combine (gate/up GEMM + SwiGLU, down GEMM with tile flags in
 parallel with the consumer copy on reserved CUs) -> moe_scale.  Inputs are
 resident in HBM before the timed region.  The default workload is the
-Mixtral-8x7B-like layer (W=4 ranks, 8 experts, 4096 tokens per owner,
-d=4096, f=14336, top-2, tb_M=128), rank 0's share.
+largest one, the DeepSeek-V3-like skewed layer (W=8 ranks, 256 experts with
+32 local, owner token counts 1638x4 + 410x4, d=7168, f=2048, top-8 with
+Zipf(1.2) expert popularity, tb_M=256), rank 0's share: rank 0 hosts the
+32 hottest experts, so it is the busiest rank.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--mode overlap|serial]
                     [--consumer-cus C] [--mgb B] [--no-cpu-baseline]
 
-Prints one JSON line.  value = tokens/s = (tokens per owner) / (time per
-step): the per-GPU rate if every rank took as long as rank 0.
+Prints one JSON line.  value = tokens/s = (N / W) / (time per step), with N
+the layer's tokens over all W owners: the per-GPU rate of the layer if every
+rank took as long as rank 0.  routed rows/s = R / (time per step).
 """
 from __future__ import annotations
 
@@ -37,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--workload", default="dsv3_skew")
     ap.add_argument("--mode", default="overlap", choices=["overlap", "serial"])
     ap.add_argument("--consumer-cus", type=int, default=16)
     ap.add_argument("--mgb", type=int, default=None,
@@ -52,7 +55,10 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemm_mixtral_traffic.txt")
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"gateup_gemm_{workload}_traffic.txt")
+
+
 GEMM_SOURCES = [os.path.join(ROOT, "moe_expert_tile_amd", "csrc", n)
                 for n in ("gemm.hip", "consume.h", "moe_internal.h")]
 
@@ -77,10 +83,11 @@ def measured_traffic(workload):
     """HBM bytes per gate/up GEMM launch from the committed counter summary,
     or None when there is none for this workload or the kernel source has
     changed since the counters were taken."""
-    if workload != "mixtral" or not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -109,46 +116,79 @@ def algorithmic(cfg, R, M, n_seg_rows):
     }
 
 
+def host_info():
+    """Threads the oracle's BLAS may use on this host (the CPU share: the
+    affinity mask, capped by OMP_NUM_THREADS when that is set), the BLAS
+    library numpy calls, and the CPU model."""
+    affinity = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    threads = min(affinity, int(cap)) if cap and cap.isdigit() and int(cap) > 0 else affinity
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            blas = "%s %s (%s)" % (libs[0].get("internal_api"), libs[0].get("version"),
+                                   os.path.basename(libs[0].get("filepath", "")))
+    except Exception:  # pragma: no cover
+        pass
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    return {"threads": threads, "affinity_cpus": affinity, "blas": blas, "cpu_model": model}
+
+
 def cpu_baseline(cfg, ids, w, x_recv, wgu, wd, budget_s):
     """The oracle as it stands on the host, on a bounded sample: the full plan,
     the FFN on a sample of layout rows (extrapolated to all M rows), the
-    combine and the scale of the rank's tokens."""
+    combine and the scale of the rank's tokens.  Same unit as the GPU line:
+    (N / W) tokens per step over the summed stage times."""
     from oracle import combine as OC, ffn as OF, plan as OP, scale as OS
+    info = host_info()
+    import contextlib
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=info["threads"], user_api="blas")
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    pl = OP.build_plan(ids, cfg.tokens, cfg.rank, cfg.E_l, cfg.tb_m, cfg.mgb)
-    X = OC.layout_x(pl, x_recv)
-    t_plan = time.perf_counter() - t0
-    rng = np.random.default_rng(0)
-    n = 64
-    t_ffn_rows, rows_done = 0.0, 0
-    while t_ffn_rows < budget_s * 0.6 and rows_done < pl.M:
-        n = min(n, pl.M - rows_done)
-        rows = rng.integers(0, pl.M, n)
-        t1 = time.perf_counter()
-        OF.layout_rows(pl, X, wgu, wd, rows)
-        t_ffn_rows += time.perf_counter() - t1
-        rows_done += n
-        n = min(2 * n, 1024)
-    t_ffn = t_ffn_rows / max(rows_done, 1) * pl.M
-    Y = np.zeros((pl.M, cfg.d), np.uint16)
-    recv = [np.zeros((t * cfg.k, cfg.d), np.uint16) for t in cfg.tokens]
-    t2 = time.perf_counter()
-    recv = OC.apply(pl, Y, recv)
-    t_comb = time.perf_counter() - t2
-    t3 = time.perf_counter()
-    OS.scale(recv[cfg.rank], w[: cfg.tokens[cfg.rank]], pl.pos)
-    t_scale = time.perf_counter() - t3
+        limiter = contextlib.nullcontext()
+    with limiter:
+        t0 = time.perf_counter()
+        pl = OP.build_plan(ids, cfg.tokens, cfg.rank, cfg.E_l, cfg.tb_m, cfg.mgb)
+        X = OC.layout_x(pl, x_recv)
+        t_plan = time.perf_counter() - t0
+        rng = np.random.default_rng(0)
+        n = 64
+        t_ffn_rows, rows_done = 0.0, 0
+        while t_ffn_rows < budget_s * 0.6 and rows_done < pl.M:
+            n = min(n, pl.M - rows_done)
+            rows = rng.integers(0, pl.M, n)
+            t1 = time.perf_counter()
+            OF.layout_rows(pl, X, wgu, wd, rows)
+            t_ffn_rows += time.perf_counter() - t1
+            rows_done += n
+            n = min(2 * n, 1024)
+        t_ffn = t_ffn_rows / max(rows_done, 1) * pl.M
+        Y = np.zeros((pl.M, cfg.d), np.uint16)
+        recv = [np.zeros((t * cfg.k, cfg.d), np.uint16) for t in cfg.tokens]
+        t2 = time.perf_counter()
+        recv = OC.apply(pl, Y, recv)
+        t_comb = time.perf_counter() - t2
+        t3 = time.perf_counter()
+        OS.scale(recv[cfg.rank], w[: cfg.tokens[cfg.rank]], pl.pos)
+        t_scale = time.perf_counter() - t3
     total = t_plan + t_ffn + t_comb + t_scale
     return {
-        "value": cfg.tokens[cfg.rank] / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "value": round((cfg.N / cfg.W) / total, 3), "unit": "tokens/s", "cores": int(info["threads"]),
+        "kind": "oracle",
         "sample": f"full plan+layout ({t_plan:.2f}s), FFN on {rows_done} random of {pl.M} layout rows "
                   f"({t_ffn_rows:.2f}s, extrapolated to {t_ffn:.1f}s), full combine ({t_comb:.2f}s) "
-                  f"and scale ({t_scale:.2f}s); float64 NumPy",
+                  f"and scale ({t_scale:.2f}s); float64 NumPy; one step = {total:.1f}s",
+        "affinity_cpus": info["affinity_cpus"], "blas": info["blas"], "cpu_model": info["cpu_model"],
     }
 
 
@@ -281,6 +321,7 @@ def main():
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e-3
 
+    t_plan_cold = amortized_cold(lambda: share.plan(ids_d, xr_d))
     t_scale_cold = amortized_cold(lambda: share.scale(w_r))
     t_copy_cold = amortized_cold(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch))
     t_rows_cold = amortized_cold(lambda: share.combine(None, None, mode=m.MODE_COPY_ROWS, epoch=share.epoch))
@@ -351,9 +392,10 @@ def main():
             raise SystemExit(f"device status after gathered-row steps: {m.status_string(st)}")
 
     gu_tflops = work["gateup_flop"] / t_gu
+    tokens_per_rank = cfg.N / cfg.W   # N / W: the layer's tokens per rank
     result = {
         "metric": METRIC,
-        "value": round(T_r / (ms * 1e-3), 1),
+        "value": round(tokens_per_rank / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -368,7 +410,7 @@ def main():
             "workload": f"{args.workload}: rank {cfg.rank} share of W={cfg.W} ranks, E={cfg.E} experts "
                         f"({cfg.E_l} local), {cfg.tokens[0]} tokens per owner, d={cfg.d}, f={cfg.f} SwiGLU, "
                         f"top-{cfg.k}, tb_M={cfg.tb_m}, mgb={cfg.mgb}",
-            "mode": args.mode, "consumer_cus": args.consumer_cus, "R": R, "M": M,
+            "mode": args.mode, "consumer_cus": args.consumer_cus, "N": cfg.N, "W": cfg.W, "R": R, "M": M,
             "padding_pct": round(100.0 * (M - R) / max(M, 1), 2),
         },
         "roofline": {
@@ -388,25 +430,31 @@ def main():
             "consumer_per_row_cold_cache": round(t_rows_cold * 1e6, 2),
             "device_copy_same_bytes_cold_cache": round(t_dev_copy_cold * 1e6, 2) if t_dev_copy_cold else None,
             "scale_cold_cache": round(t_scale_cold * 1e6, 2),
+            "plan_cold_cache": round(t_plan_cold * 1e6, 2),
         },
         "rates": {
+            # primary bandwidth figures: each launch alone after a 1 GiB read
+            # (a cold Infinity Cache), so the bytes come from HBM
+            "plan_frac_hbm_cold": round(work["plan_bytes"] / t_plan_cold / PEAK_HBM, 4),
+            "combine_frac_hbm_cold": round(work["combine_bytes"] / t_copy_cold / PEAK_HBM, 4),
+            "scale_frac_hbm_cold": round(work["scale_bytes"] / t_scale_cold / PEAK_HBM, 4),
             "gateup_TFLOPs": round(gu_tflops / 1e12, 2),
             "down_TFLOPs": round(work["down_flop"] / t_dn / 1e12, 2),
-            "plan_GBs": round(work["plan_bytes"] / t_plan_k / 1e9, 1),
-            "combine_standalone_GBs": round(work["combine_bytes"] / t_copy / 1e9, 1),
-            "scale_GBs": round(work["scale_bytes"] / t_scale_k / 1e9, 1),
-            "plan_frac_hbm": round(work["plan_bytes"] / t_plan_k / PEAK_HBM, 4),
-            "combine_frac_hbm": round(work["combine_bytes"] / t_copy / PEAK_HBM, 4),
-            "scale_frac_hbm": round(work["scale_bytes"] / t_scale_k / PEAK_HBM, 4),
+            "down_frac_mfma": round(work["down_flop"] / t_dn / PEAK_BF16, 4),
+            "plan_GBs_cold": round(work["plan_bytes"] / t_plan_cold / 1e9, 1),
+            "combine_GBs_cold": round(work["combine_bytes"] / t_copy_cold / 1e9, 1),
+            "scale_GBs_cold": round(work["scale_bytes"] / t_scale_cold / 1e9, 1),
+            # the same kernels back to back (their working set partly in the
+            # 256 MB Infinity Cache)
+            "plan_frac_hbm_warm": round(work["plan_bytes"] / t_plan_k / PEAK_HBM, 4),
+            "combine_frac_hbm_warm": round(work["combine_bytes"] / t_copy / PEAK_HBM, 4),
+            "scale_frac_hbm_warm": round(work["scale_bytes"] / t_scale_k / PEAK_HBM, 4),
             "combine_at_budget_GBs": round(work["combine_bytes"] / t_copy_budget / 1e9, 1),
-            "combine_frac_hbm_cold": round(work["combine_bytes"] / t_copy_cold / PEAK_HBM, 4) if t_copy_cold else None,
             "combine_per_row_frac_hbm": round(work["combine_bytes"] / t_rows / PEAK_HBM, 4) if t_rows else None,
             "combine_per_row_frac_hbm_cold": (round(work["combine_bytes"] / t_rows_cold / PEAK_HBM, 4)
                                               if t_rows_cold else None),
             "device_copy_frac_hbm_cold": (round(work["combine_bytes"] / t_dev_copy_cold / PEAK_HBM, 4)
                                           if t_dev_copy_cold else None),
-            "scale_frac_hbm_cold": round(work["scale_bytes"] / t_scale_cold / PEAK_HBM, 4) if t_scale_cold else None,
-            "down_frac_mfma": round(work["down_flop"] / t_dn / PEAK_BF16, 4),
             "routed_rows_per_s": round(R / (ms * 1e-3), 1),
         },
         "overlap": {
@@ -417,7 +465,7 @@ def main():
         },
         "gathered_rows": None if ms_gathered is None else {
             "ms_per_step": round(ms_gathered, 4),
-            "tokens_per_s": round(T_r / (ms_gathered * 1e-3), 1),
+            "tokens_per_s": round(tokens_per_rank / (ms_gathered * 1e-3), 1),
             "plan_metadata_back_to_back_us": round(t_plan_meta * 1e6, 2),
         },
         "work": {k: v for k, v in work.items()},

@@ -52,7 +52,7 @@ typedef enum moe_status {
 typedef struct moe_shape {
   int32_t world;            /* W: ranks, also the token owners; 1..64 */
   int32_t rank;             /* r: the rank whose share is computed; 0..W-1 */
-  int32_t experts_per_rank; /* E_l; rank q hosts global experts [q*E_l, (q+1)*E_l); W*E_l <= 4096 */
+  int32_t experts_per_rank; /* E_l; rank q hosts global experts [q*E_l, (q+1)*E_l); W*E_l <= 1024 */
   int32_t top_k;            /* k; 1..min(32, W*E_l) */
   int32_t hidden;           /* d; multiple of 256 */
   int32_t ffn;              /* f; multiple of 128 */
@@ -103,6 +103,9 @@ typedef struct moe_plan_view {
    * (present when tb_M divides 256; first band and band count per tile) */
   size_t gu_tile_row, gu_tile_expert;                              /* [hdr[10]] */
   size_t dn_tile_row, dn_tile_expert, dn_tile_band, dn_tile_nbands; /* [hdr[11]] */
+  /* uint64 [sk_counters_count]: epoch-tagged tile counters of the GEMMs'
+   * K-split tails; zero them (with the flags) before an epoch is reused */
+  size_t sk_counters, sk_counters_count;
 } moe_plan_view;
 
 /* moe_expert_combine modes */
@@ -190,6 +193,9 @@ int moe_plan(const moe_shape* shape, const int32_t* topk_ids, const uint16_t* x_
  *   h, y       device bf16 [rows_cap, f] and [rows_cap, d]; scratch written here.
  *   flags      device uint32 [flags_count]; zero them once at allocation, then
  *              pass a new epoch (never 0, increasing) on every call: no reset.
+ *              An epoch value may be used again only after the flags and the
+ *              plan's sk_counters (moe_plan_view) are zeroed, e.g. when the
+ *              32-bit epoch wraps around.
  *   recv       HOST array of W device pointers; recv[o] is bf16 [T_o*k, d].
  *   opts       may be NULL (OVERLAP, defaults).
  * Every mode runs on `stream` alone.  OVERLAP launches the down GEMM with

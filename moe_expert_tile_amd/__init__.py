@@ -46,7 +46,8 @@ _VIEW_FIELDS = ["hdr", "c", "grp_off", "m_e", "row_off", "rb", "order", "base",
                 "band_expert", "band_dst", "band_src_row", "band_dst_off", "band_valid",
                 "seg_first", "seg_nbands", "seg_dst", "seg_dst_off", "seg_src_row", "seg_rows",
                 "seg_unit", "src_index", "pos",
-                "gu_tile_row", "gu_tile_expert", "dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands"]
+                "gu_tile_row", "gu_tile_expert", "dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands",
+                "sk_counters", "sk_counters_count"]
 
 
 class moe_plan_view(ctypes.Structure):
@@ -68,7 +69,7 @@ class MoEError(RuntimeError):
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m moe_expert_tile_amd.build` "
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python moe_expert_tile_amd/build.py` "
                           "(there is no fallback implementation)")
     lib = ctypes.CDLL(_LIB_PATH)
     P, I, V = ctypes.POINTER, ctypes.c_int, ctypes.c_void_p
@@ -233,11 +234,27 @@ class RankShare:
         """x_recv given: gathered rows (the gate/up GEMM reads x_recv through
         src_index instead of the layout X)."""
         if epoch is None:
-            self.epoch += 1
-            epoch = self.epoch
+            epoch = self._next_epoch()
+        elif mode in (MODE_OVERLAP, MODE_SERIAL):
+            # a compute mode needs a fresh epoch: with one the flags already
+            # hold, the consumer could copy rows before they are written
+            if not 0 < epoch <= 0xFFFFFFFF or epoch <= self.epoch:
+                raise ValueError(f"epoch {epoch} is not above the last one ({self.epoch})")
+            self.epoch = epoch
         moe_expert_combine(self.shape, self.plan_ws, self.x_layout if x_recv is None else None, w_gate_up,
                            w_down, self.h, self.y, self.flags, epoch, self.recv, mode, consumer_cus,
                            consumer_blocks, spin_timeout_ns, events, stream, x_recv=x_recv)
+
+    def _next_epoch(self) -> int:
+        """The next epoch; after 2^32 - 1 the flags and the K-split counters
+        are zeroed (on the current stream) and the epochs start again at 1."""
+        if self.epoch >= 0xFFFFFFFF:
+            self.flags.zero_()
+            o = self.offsets["sk_counters"] // 4
+            self.plan_ws[o:o + 2 * self.offsets["sk_counters_count"]].zero_()
+            self.epoch = 0
+        self.epoch += 1
+        return self.epoch
 
     def scale(self, topk_w_self, stream=None):
         moe_scale(self.shape, self.plan_ws, self.recv[self.shape.c.rank], topk_w_self, self.out, stream)

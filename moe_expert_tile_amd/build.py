@@ -1,6 +1,6 @@
 """Build libmoe.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
 
-    python -m moe_expert_tile_amd.build [--verbose]
+    python moe_expert_tile_amd/build.py [--verbose]
 
 Every call recompiles.  Device code is built with packed-fp32 instructions
 disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass

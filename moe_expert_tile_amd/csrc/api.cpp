@@ -114,10 +114,22 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->o_gumt_row = take(L->gu_mt_cap);
   L->o_gumt_exp = take(L->gu_mt_cap);
   L->o_dnt_row = take(B); L->o_dnt_exp = take(B); L->o_dnt_band = take(B); L->o_dnt_nb = take(B);
-  // stream-K: only when a GEMM can have more tiles than the smallest grid
+  // stream-K partial-sum slots: as many as the larger GEMM can split.  A
+  // split happens only for K >= kMinSkKTOneRound steps (kMinSkKT behind full
+  // rounds); its tiles are at most 3/4 of a round (half a round when only
+  // the one-round rule applies), and their K steps are cut into at most
+  // min(G, steps / kMinSkSteps) pieces, two slots each (a piece may close
+  // one tile and open the next).
   const int64_t gu_tiles_max = (int64_t)L->gu_mt_cap * L->gu_ntn;
   const int64_t dn_tiles_max = B * L->dn_sub * L->dn_ntn;
-  L->sk_slots = (std::max(gu_tiles_max, dn_tiles_max) > 8) ? 2 * kMaxProducers : 0;
+  auto sk_need = [](int64_t tiles_max, int KT) -> int64_t {
+    if (KT < kMinSkKTOneRound || tiles_max <= 0) return 0;
+    const int64_t split_max = KT >= kMinSkKT ? 3 * kMaxProducers / 4 : kMaxProducers / 2;
+    const int64_t tiles = std::min(tiles_max, split_max);
+    return 2 * std::min<int64_t>(kMaxProducers, tiles * KT / kMinSkSteps);
+  };
+  const int dn_bk = L->dn_bm == 256 ? kDnBK : (L->dn_bm == 64 ? kDn64BK : kDn32BK);
+  L->sk_slots = (int)std::max(sk_need(gu_tiles_max, d / kGuBK), sk_need(dn_tiles_max, f / dn_bk));
   L->o_skc = take(2 * kMaxProducers * 2);
   L->o_skp = take((int64_t)L->sk_slots * 256 * 256);
   L->total_words = off;
@@ -244,6 +256,7 @@ int moe_plan_offsets(const moe_shape* s, moe_plan_view* v) {
   v->gu_tile_row = L.o_gumt_row * 4; v->gu_tile_expert = L.o_gumt_exp * 4;
   v->dn_tile_row = L.o_dnt_row * 4; v->dn_tile_expert = L.o_dnt_exp * 4;
   v->dn_tile_band = L.o_dnt_band * 4; v->dn_tile_nbands = L.o_dnt_nb * 4;
+  v->sk_counters = L.o_skc * 4; v->sk_counters_count = 2 * kMaxProducers;
   return MOE_OK;
 }
 

@@ -11,12 +11,14 @@
 // are not copied here: their rows never leave the rank, and the down GEMM's
 // epilogue writes them straight into the rank's own receive buffer.
 //
-// Memory ordering: the producer stores a tile, releases at agent scope and
-// sets flags[tile] = epoch with an agent-scope store.  Here wave 0 polls the
-// flags with agent-scope loads; every later read of the tile also uses
-// agent-scope (sc1) loads, 16 bytes per lane, which bypass the non-coherent
-// caches of this XCD, so no cache-wide invalidation is issued and the
-// producer's L2 contents on the same XCD survive.
+// Memory ordering: the producer stores a tile's rows at device scope (sc1,
+// written through its XCD's L2), waits until every store is acknowledged and
+// only then sets flags[tile] = epoch with a relaxed agent-scope store (no
+// release fence).  Here wave 0 polls the flags with relaxed agent-scope
+// loads; the tile's rows are read only after the flags were seen, with
+// agent-scope (sc1) loads, 16 bytes per lane, which do not return lines this
+// XCD cached earlier, so no acquire fence or cache-wide invalidation is
+// issued and the producer's L2 contents on the same XCD survive.
 //
 // Work split: each segment is cut into units of kCopyChunk bytes, numbered
 // in schedule order.  The standalone consumer kernel gives unit u to

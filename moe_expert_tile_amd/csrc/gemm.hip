@@ -348,13 +348,17 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   // runs the tile's epilogue.
   int full = total, sk_tiles = 0, G_sk = 0;
   int64_t W_sk = 0;
-  if (L.sk_slots >= 2 * G && total > 0 && (KT >= kMinSkKT || (2 * total <= G && KT >= kMinSkKTOneRound))) {
+  if (total > 0 && (KT >= kMinSkKT || (2 * total <= G && KT >= kMinSkKTOneRound))) {
     const int rem = total % G;
-    if (rem != 0 && 4 * rem <= 3 * G) {
+    const int64_t w = (int64_t)rem * KT;
+    const int g_sk = (int)min((int64_t)G, w / kMinSkSteps);
+    // slot 2 * s + piece of the partial sums for s < g_sk: the workspace
+    // holds as many as the host sized it for
+    if (rem != 0 && 4 * rem <= 3 * G && 2 * g_sk <= L.sk_slots) {
       full = total - rem;
       sk_tiles = rem;
-      W_sk = (int64_t)sk_tiles * KT;
-      G_sk = (int)min((int64_t)G, W_sk / kMinSkSteps);
+      W_sk = w;
+      G_sk = g_sk;
     }
   }
   auto sk_lo = [&](int w) { return (int64_t)w * W_sk / G_sk; };
@@ -788,12 +792,15 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       // side, the point where all XCDs' agent-scope loads meet; the same
       // instruction form as a relaxed agent-scope atomic store), and each
       // wave waits until its stores are acknowledged; after the barrier one
-      // lane sets the flags with agent-scope stores.  So the data is visible
-      // to every XCD before any flag is, without the L2 write-back an
+      // lane sets the flags with relaxed agent-scope stores.  So the data is
+      // visible to every XCD before any flag is, without the L2 write-back an
       // agent-scope release fence would add: that write-back (buffer_wbl2)
       // only matters for ordinary write-back stores, and walking the L2 once
-      // per tile cost 7-10% of the short-K down GEMMs.  The consumer's side
-      // is an agent-scope acquire (L2 invalidate) and sc1 loads.
+      // per tile cost 7-10% of the short-K down GEMMs.  The consumer polls
+      // the flags with relaxed agent-scope loads and reads the rows only
+      // after it has seen them (a control dependency), with agent-scope (sc1)
+      // loads that do not return lines this XCD cached earlier; it issues no
+      // acquire fence and no L2 invalidate.
       static_assert((MOE_STORE_AUX & kDeviceScope) != 0, "flag publication needs device-scope (sc1) output stores");
       wait_vm0();
       if constexpr (FLAGS) {
@@ -838,10 +845,17 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
 
 
 using GuCfg = Cfg<256, 256, MOE_GU_WAVES_M, MOE_GU_WAVES_N, MOE_GU_BK, MOE_GU_SA, MOE_GU_SB>;
+static_assert(GuCfg::BK == kGuBK, "the host sizes the stream-K scratch with this K step");
 using Dn256 = Cfg<256, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_DN_BK, MOE_DN_SA, MOE_DN_SB>;
-using Dn128 = Cfg<128, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_DN_BK, MOE_DN_SA, MOE_DN_SB>;
-using Dn64 = Cfg<64, 256, 1, 4, 32, 3, 3>;
-using Dn32 = Cfg<32, 256, 1, 4, 64, 3, 3>;
+static_assert(Dn256::BK == kDnBK, "the host sizes the stream-K scratch with this K step");
+// Down tiles of 64 and 32 rows, for band heights that do not divide 256 (a
+// band is cut into tb_M / 64 or tb_M / 32 row tiles).  The 64-row tile's
+// ~61 KB of LDS lets two workgroups
+// share a CU, so in the overlapped launch a consumer workgroup may share its
+// CU with a producer; the whole grid is resident at once either way, so no
+// workgroup waits for a slot held by one that waits for it.
+using Dn64 = Cfg<64, 256, 1, 4, kDn64BK, 3, 3>;
+using Dn32 = Cfg<32, 256, 1, 4, kDn32BK, 3, 3>;
 
 }  // namespace
 
@@ -862,15 +876,15 @@ hipError_t launch_down(const PlanLayout& L, int32_t* ws, const uint16_t* h, cons
     case 256:
       hipLaunchKernelGGL((grouped_gemm_kernel<Dn256, false, true>), dim3(grid), dim3(Dn256::NT), 0, s, L, a, recv);
       break;
-    case 128:
-      hipLaunchKernelGGL((grouped_gemm_kernel<Dn128, false, true>), dim3(grid), dim3(Dn128::NT), 0, s, L, a, recv);
-      break;
     case 64:
       hipLaunchKernelGGL((grouped_gemm_kernel<Dn64, false, true>), dim3(grid), dim3(Dn64::NT), 0, s, L, a, recv);
       break;
-    default:
+    case 32:
       hipLaunchKernelGGL((grouped_gemm_kernel<Dn32, false, true>), dim3(grid), dim3(Dn32::NT), 0, s, L, a, recv);
       break;
+    default:
+      // make_layout never picks another height: 128 divides 256 and takes the 256-row path
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

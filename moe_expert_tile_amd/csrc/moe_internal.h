@@ -15,6 +15,12 @@ constexpr int kCopyChunk = 32768;      // bytes per consumer copy unit
 constexpr int kGuBM = 256;             // gate/up GEMM tile rows
 constexpr int kGuBN = 256;             // gate/up GEMM tile cols (128 gate + 128 up)
 constexpr int kDnBN = 256;             // down GEMM tile cols
+// K steps of the GEMM configurations (gemm.hip asserts them); the host sizes
+// the stream-K scratch with them
+constexpr int kGuBK = 64;              // gate/up
+constexpr int kDnBK = 64;              // down, 256-row tiles
+constexpr int kDn64BK = 32;            // down, 64-row tiles (tb_M a multiple of 64, not dividing 256)
+constexpr int kDn32BK = 64;            // down, 32-row tiles
 constexpr int kMaxProducers = 256;     // persistent GEMM workgroups at most (one per CU on MI355X)
 constexpr int kMinSkSteps = 16;        // shortest K range of a stream-K piece
 // stream-K for a tail round only with tiles of at least this many K steps.

@@ -143,5 +143,21 @@ def oracle_ffn_rows(name, pl, x_layout_bits, rows):
     return OF.layout_rows(pl, x_layout_bits, wgu, wd, rows)
 
 
+@functools.lru_cache(maxsize=None)
+def oracle_sample(name: str):
+    """(rows, h_ref, y_ref): the oracle's h and y of every layout row (small
+    workloads) or of the sampled rows, for the workload's own plan."""
+    c = case(name)
+    pl = c["plan"]
+    rows = np.arange(pl.M) if pl.M <= 4096 else sample_rows(pl)
+    X = OC.layout_x(pl, c["x_recv"])
+    h_ref, y_ref = oracle_ffn_rows(name, pl, X, rows)
+    return rows, h_ref, y_ref
+
+
+def rows_of(t: torch.Tensor, rows: np.ndarray) -> np.ndarray:
+    return host_bits(t.index_select(0, torch.from_numpy(rows).cuda()))
+
+
 def layout_x(pl, x_recv):
     return OC.layout_x(pl, x_recv)

@@ -51,7 +51,7 @@ def test_sizes_follow_the_padding_bound():
         assert z["recv_rows_self"] == 64 * 2
         assert z["plan_bytes"] % 256 == 0
         off = m.moe_plan_offsets(s)
-        vals = sorted(off.values())
+        vals = sorted(v for k, v in off.items() if not k.endswith("_count"))
         assert all(v % 256 == 0 for v in vals)
         assert len(set(vals)) == len(vals)
         assert max(vals) < z["plan_bytes"]
@@ -127,3 +127,40 @@ def test_status_strings():
     for code in range(7):
         assert m.status_string(code)
     assert m.status_string(99) == "unknown status"
+
+
+def test_stream_k_scratch_only_where_a_gemm_can_split():
+    """The plan workspace holds stream-K partial sums only when one of the
+    GEMMs is long enough in K to be split (32 K steps of 64 at least): none
+    for d = 512, f = 1024 (8 and 16 steps), 512 slots of 256 KB for d = 4096."""
+    import moe_expert_tile_amd as m
+    small = m.moe_query_sizes(_shape())
+    assert small["plan_bytes"] < (1 << 20)
+    big = m.moe_query_sizes(_shape(hidden=4096, ffn=14336))
+    assert big["plan_bytes"] >= 512 * 256 * 256 * 4
+    off = m.moe_plan_offsets(_shape())
+    assert off["sk_counters_count"] == 512 and off["sk_counters"] % 256 == 0
+
+
+def test_epochs_of_the_binding():
+    """RankShare.combine refuses, before any library call, an explicit epoch
+    that is not above the last one in a compute mode (its flags would already
+    read as ready), and the automatic epoch skips 0 on wrap-around after
+    zeroing the flags and the K-split counters."""
+    import torch
+    import moe_expert_tile_amd as m
+    sh = m.RankShare(_shape(), device="cpu")
+    sh.epoch = 7
+    for e in (7, 3, 0, 1 << 32):
+        with pytest.raises(ValueError):
+            sh.combine(None, None, mode=m.MODE_OVERLAP, epoch=e)
+        with pytest.raises(ValueError):
+            sh.combine(None, None, mode=m.MODE_SERIAL, epoch=e)
+    assert sh.epoch == 7
+    sh.epoch = 0xFFFFFFFF
+    sh.flags.fill_(5)
+    o = sh.offsets["sk_counters"] // 4
+    sh.plan_ws[o:o + 1024].fill_(9)
+    assert sh._next_epoch() == 1
+    assert int(sh.flags.abs().sum()) == 0 and int(sh.plan_ws[o:o + 1024].abs().sum()) == 0
+    assert sh._next_epoch() == 2

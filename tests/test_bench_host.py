@@ -45,9 +45,16 @@ def test_traffic_is_void_when_the_digest_differs(tmp_path, monkeypatch):
     traffic.write_text(
         "gemm_code_sha256: %s\ncopy_bytes: 1024\ncopy_fetch_kib: 0.5\ncopy_write_kib: 1.0\n"
         "gateup_fetch_kib: 2.0\ngateup_write_kib: 3.0\n" % bench.gemm_code_digest())
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(traffic))
+    monkeypatch.setattr(bench, "traffic_file",
+                        lambda w: str(traffic) if w == "dsv3_skew" else str(tmp_path / "none.txt"))
     # reads scaled by 1024 / (1024 * 0.5) = 2, writes by 1
-    assert bench.measured_traffic("mixtral") == 1024.0 * (2.0 * 2 + 3.0 * 1)
+    assert bench.measured_traffic("dsv3_skew") == 1024.0 * (2.0 * 2 + 3.0 * 1)
     assert bench.measured_traffic("qwen3") is None
     open(paths[0], "a").write("\nstatic int changed;\n")
-    assert bench.measured_traffic("mixtral") is None
+    assert bench.measured_traffic("dsv3_skew") is None
+
+
+def test_host_info_names_the_cpu_share():
+    info = bench.host_info()
+    assert 1 <= info["threads"] <= info["affinity_cpus"]
+    assert info["cpu_model"] and info["blas"]

@@ -82,6 +82,7 @@ def test_full_layer_equals_definition(name, mode):
 
 
 def _custom(W, E_l, k, tokens, d=256, f=256, tb=32, mgb=1, seed=0, hot=None, rank=0):
+    assert tb % 32 == 0 and 32 <= tb <= 256 and d % 256 == 0 and f % 128 == 0
     cfg = synth.MoEConfig("custom", W, W * E_l, tuple(tokens), d, f, k, tb, seed=seed, mgb=mgb, rank=rank)
     rng = np.random.default_rng(seed)
     ids = synth.random_routing_case(rng, W, E_l, k, list(tokens), hot=hot)
@@ -97,6 +98,12 @@ EDGE_CASES = {
     "k_equals_E": dict(W=2, E_l=2, k=4, tokens=[33, 70], rank=1),
     "tb96": dict(W=3, E_l=2, k=2, tokens=[120, 80, 100], tb=96, mgb=2),
     "tb256_wide": dict(W=5, E_l=1, k=1, tokens=[300, 10, 260, 0, 513], tb=256, d=512, f=384),
+    # band heights that do not divide 256: the down GEMM cuts each band into
+    # 32-row tiles (160: five, 224: seven) or 64-row tiles (192: three, with
+    # K = 1024 long enough to split the single round of tiles along K)
+    "tb160": dict(W=3, E_l=2, k=2, tokens=[460, 190, 530], tb=160, mgb=2, rank=1),
+    "tb192": dict(W=3, E_l=2, k=2, tokens=[600, 400, 500], tb=192, f=1024, mgb=2),
+    "tb224": dict(W=4, E_l=1, k=2, tokens=[500, 350, 0, 610], tb=224, mgb=3, rank=3),
 }
 
 

@@ -22,8 +22,8 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import (ATOL, RTOL, case, dev_bf16, host_bits, layout_x, oracle_ffn_rows, owner_slice,
-                         sample_rows, say, shape_of, tol_ratio, weights)
+from gpu_helpers import (ATOL, RTOL, case, dev_bf16, host_bits, layout_x, oracle_ffn_rows, oracle_sample,
+                         owner_slice, rows_of, sample_rows, say, shape_of, tol_ratio, weights)
 from oracle import combine as OC
 from oracle import scale as OS
 from oracle import bf16 as OB
@@ -61,12 +61,9 @@ def test_ffn_rows_match_oracle(name):
     import moe_expert_tile_amd as m
     c, share, _, _ = planned(name, m.MODE_SERIAL)
     pl = c["plan"]
-    rows = np.arange(pl.M) if pl.M <= 4096 else sample_rows(pl)
-    X = layout_x(pl, c["x_recv"])
-    h_ref, y_ref = oracle_ffn_rows(name, pl, X, rows)
-    idx = torch.from_numpy(rows).cuda()
-    h = host_bits(share.h.index_select(0, idx))
-    y = host_bits(share.y.index_select(0, idx))
+    rows, h_ref, y_ref = oracle_sample(name)
+    h = rows_of(share.h, rows)
+    y = rows_of(share.y, rows)
     scale_aware = name == "tiny"
     rh = tol_ratio(h, h_ref, scale_aware)
     ry = tol_ratio(y, y_ref, scale_aware)
@@ -151,6 +148,11 @@ def test_overlapped_combine_over_epochs(name):
             y_first = Y
         else:
             assert np.array_equal(Y, y_first), it
+    # the overlapped y straight against the oracle, and against the serial y
+    rows, _, y_ref = oracle_sample(name)
+    ratio = tol_ratio(y_first[rows], y_ref)
+    say(f"[overlap] {name} rows={rows.size} worst y {ratio:.3f} against the oracle")
+    assert ratio <= 1.0
     assert tol_ratio(y_first, y_serial, name == "tiny") <= 1.0
     if name in ("tiny_unit", "decode_tb32"):
         assert np.array_equal(y_first, y_serial)
@@ -207,6 +209,7 @@ def test_gathered_rows_equal_the_layout_path(name):
     g.x_layout.fill_(float("nan"))
     xr = dev_bf16(c["x_recv"])
     g.plan(torch.from_numpy(c["ids"]).cuda(), xr, materialize=False)
+    rows, h_ref, y_ref = oracle_sample(name)
     for mode in (m.MODE_SERIAL, m.MODE_OVERLAP):
         for o in range(cfg.W):
             g.recv[o].copy_(dev_bf16(synth.foreign_rows(cfg, o)))
@@ -214,6 +217,12 @@ def test_gathered_rows_equal_the_layout_path(name):
         g.y.fill_(float("nan"))
         g.combine(wgu_d, wd_d, mode=mode, x_recv=xr)
         assert g.status() == m.MOE_OK
+        # gathered h and y straight against the oracle ...
+        rh = tol_ratio(rows_of(g.h, rows), h_ref)
+        ry = tol_ratio(rows_of(g.y, rows), y_ref)
+        say(f"[gathered] {name} mode={mode} worst h {rh:.3f} y {ry:.3f} against the oracle")
+        assert rh <= 1.0 and ry <= 1.0
+        # ... and bit for bit against the materialized layout's
         assert np.array_equal(host_bits(g.h[:pl.M]), H), mode
         y = host_bits(g.y[:pl.M])
         if mode == m.MODE_SERIAL:
