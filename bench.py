@@ -102,13 +102,19 @@ def dev_bf16(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def algorithmic(cfg, R, M, n_seg_rows):
-    """Work per call (the rank-0 share) in the units the rooflines use."""
+def algorithmic(cfg, R, M, n_seg_rows, gu_rows, dn_rows):
+    """Work per call (the rank-0 share) in the units the rooflines use.  The
+    GEMMs' algorithmic flops count the R real rows only: padding rows carry
+    no data (the gate/up GEMM never computes them; the down GEMM writes zeros
+    for them).  The rows the kernels run through their MFMAs, ragged tile
+    tails and padding included, are reported beside as executed flops."""
     d, f, k, T_r = cfg.d, cfg.f, cfg.k, cfg.tokens[cfg.rank]
     N = cfg.N
     return {
-        "gateup_flop": 4.0 * d * f * M,          # executed rows, padding included
-        "down_flop": 2.0 * d * f * M,
+        "gateup_flop": 4.0 * d * f * R,
+        "down_flop": 2.0 * d * f * R,
+        "gateup_flop_executed": 4.0 * d * f * gu_rows,
+        "down_flop_executed": 2.0 * d * f * dn_rows,
         "useful_flop": 6.0 * d * f * R,
         "plan_bytes": 4.0 * N * k + 2.0 * d * R + 2.0 * d * M + 4.0 * M + 4.0 * T_r * k,
         "combine_bytes": 4.0 * d * n_seg_rows,   # valid rows read + written
@@ -277,7 +283,12 @@ def main():
     # down GEMM's epilogue)
     nrs = hdr["remote_segments"]
     seg_rows = int(share.array("seg_rows", nrs).sum()) if nrs else 0
-    work = algorithmic(cfg, R, M, seg_rows)
+    # rows the GEMMs run through their MFMAs: the gate/up GEMM's 256-row
+    # tiles over every expert's real rows; the down GEMM's tiles over the
+    # layout rows of every band (padding included)
+    gu_rows = 256 * hdr["gateup_row_tiles"]
+    dn_rows = M
+    work = algorithmic(cfg, R, M, seg_rows, gu_rows, dn_rows)
 
     # Short kernels: 20 back-to-back launches between two events on the
     # stream they run on, so the per-launch event overhead does not count.
@@ -415,6 +426,7 @@ def main():
         },
         "roofline": {
             "kernel": "gate/up grouped GEMM + SwiGLU (grouped_gemm_kernel, gate/up instance)",
+            "algorithmic": "4*d*f*R flops per launch (R real rows; no padding row is computed)",
             "bound": "mfma", "achieved": round(gu_tflops / 1e12, 2), "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16, 4), "traffic": measured_traffic(args.workload),
         },
@@ -441,6 +453,8 @@ def main():
             "gateup_TFLOPs": round(gu_tflops / 1e12, 2),
             "down_TFLOPs": round(work["down_flop"] / t_dn / 1e12, 2),
             "down_frac_mfma": round(work["down_flop"] / t_dn / PEAK_BF16, 4),
+            "gateup_frac_mfma_executed": round(work["gateup_flop_executed"] / t_gu / PEAK_BF16, 4),
+            "down_frac_mfma_executed": round(work["down_flop_executed"] / t_dn / PEAK_BF16, 4),
             "plan_GBs_cold": round(work["plan_bytes"] / t_plan_cold / 1e9, 1),
             "combine_GBs_cold": round(work["combine_bytes"] / t_copy_cold / 1e9, 1),
             "scale_GBs_cold": round(work["scale_bytes"] / t_scale_cold / 1e9, 1),

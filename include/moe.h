@@ -106,6 +106,15 @@ typedef struct moe_plan_view {
   /* uint64 [sk_counters_count]: epoch-tagged tile counters of the GEMMs'
    * K-split tails; zero them (with the flags) before an epoch is reused */
   size_t sk_counters, sk_counters_count;
+  /* Compacted rows: the layout's R real rows without its padding, in layout
+   * order (experts ascending, inside X_e the groups in layout order).  The
+   * gate/up GEMM runs over them, so it computes no padding row, and h holds
+   * them in this order.  crow_off [E_l + 1]: first compacted row of X_e;
+   * grp_crow [E_l][W]: offset of group (e, o) inside X_e's compacted rows;
+   * band_crow [B]: first compacted row of every band (schedule order);
+   * cmp_row [R]: layout row of every compacted row; cmp_src [R]: its
+   * received row (index into x_recv). */
+  size_t crow_off, grp_crow, band_crow, cmp_row, cmp_src;
 } moe_plan_view;
 
 /* moe_expert_combine modes */

@@ -76,6 +76,8 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->dn_merge = (256 % tb_m == 0) ? 256 / tb_m : 0;
   if (L->dn_merge > 0) bm = 256;
   L->dn_bm = bm;
+  L->tb_log2 = 0;
+  while ((1 << L->tb_log2) < tb_m) ++L->tb_log2;
   L->dn_sub = L->dn_merge > 0 ? 1 : tb_m / bm;
   L->dn_ntn = d / kDnBN;
   L->dn_tpb = L->dn_sub * L->dn_ntn;
@@ -114,6 +116,11 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->o_gumt_row = take(L->gu_mt_cap);
   L->o_gumt_exp = take(L->gu_mt_cap);
   L->o_dnt_row = take(B); L->o_dnt_exp = take(B); L->o_dnt_band = take(B); L->o_dnt_nb = take(B);
+  L->o_crowoff = take(E_l + 1);
+  L->o_ccum = take(EW);
+  L->o_bcrow = take(B);
+  L->o_cmprow = take(R);
+  L->o_cmpsrc = take(R);
   // stream-K partial-sum slots: as many as the larger GEMM can split.  A
   // split happens only for K >= kMinSkKTOneRound steps (kMinSkKT behind full
   // rounds); its tiles are at most 3/4 of a round (half a round when only
@@ -257,6 +264,8 @@ int moe_plan_offsets(const moe_shape* s, moe_plan_view* v) {
   v->dn_tile_row = L.o_dnt_row * 4; v->dn_tile_expert = L.o_dnt_exp * 4;
   v->dn_tile_band = L.o_dnt_band * 4; v->dn_tile_nbands = L.o_dnt_nb * 4;
   v->sk_counters = L.o_skc * 4; v->sk_counters_count = 2 * kMaxProducers;
+  v->crow_off = L.o_crowoff * 4; v->grp_crow = L.o_ccum * 4; v->band_crow = L.o_bcrow * 4;
+  v->cmp_row = L.o_cmprow * 4; v->cmp_src = L.o_cmpsrc * 4;
   return MOE_OK;
 }
 

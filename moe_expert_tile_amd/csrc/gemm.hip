@@ -144,7 +144,10 @@ struct GemmArgs {
   int half;               // SWIGLU: f (offset of the up rows); else 0
   int n_prod;             // producer workgroups (the rest of the grid consumes)
   int64_t timeout;        // consumer wait bound, 100 MHz ticks
-  const int32_t* gather;  // gathered A rows: row m of the layout is a[gather[m]] (< 0: zeros); else null
+  // gate/up: the table of A rows of the compacted rows (cmp_src into x_recv
+  // when `gathered`, else cmp_row into the layout X); null for the down GEMM
+  const int32_t* rows;
+  int gathered;
   int64_t a_bytes;        // gathered: bytes of `a` (< 2^31)
 };
 
@@ -419,9 +422,10 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     // the first band and the number of bands whose flags it sets
     int e, row0, lim, band0 = 0, nbt = 1;
     if constexpr (SWIGLU) {
+      // gate/up tiles run over compacted rows (the layout without padding)
       row0 = g.ws[L.o_gumt_row + mt];
       e = g.ws[L.o_gumt_exp + mt];
-      lim = rowoff[e + 1];
+      lim = g.ws[L.o_crowoff + e + 1];
     } else if (L.dn_merge > 0) {
       // up to dn_merge row-contiguous bands of one expert
       row0 = g.ws[L.o_dnt_row + mt];
@@ -456,36 +460,72 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     // a sub-tile of a partial (local tail) band can start past the expert's
     // last row: nothing to compute or store, only its flag to publish
     const bool empty = row0 >= row_end;
-    // wave-uniform base row (clamped into the expert) + 32-bit lane byte
-    // offsets, never negative (rows < 2^16 apart, K < 2^16)
-    const int rbase = min(row0, row_end - 1);
-    // buffer descriptors: A from the clamped base row to the expert's last
-    // row, B over the expert's weight matrix (loads never leave them)
-    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(g.w + (int64_t)e * g.w_rows * g.K, (int64_t)g.w_rows * g.K * 2);
+    // A operand.  Every load is bounded by a buffer descriptor, and a lane
+    // whose row holds no data gets an offset past the bound (2^31 > the
+    // descriptor's extent), where buffer loads return zeros.
+    //  * gate/up: row r of the tile is compacted row row0 + r; the table
+    //    gives its row of x_recv (gathered) or of the layout X.  Rows of one
+    //    tile lie within one X_e, so their layout rows span at most
+    //    256 + (W-1)(tb_M-1) rows: 32-bit offsets from the first suffice.
+    //  * down: A is h in compacted order.  The tile's real rows are the
+    //    first `valid` rows of each of its bands, and those are consecutive
+    //    compacted rows from band_crow of its first band; padding rows read
+    //    zeros, so their y rows come out exactly zero.
     __amdgpu_buffer_rsrc_t a_rsrc;
     uint32_t a_off[C::A_LOADS];
     uint32_t b_off[C::B_LOADS];
-    if (SWIGLU && g.gather != nullptr) {
-      // gathered rows: each lane's row comes from the received rows through
-      // src_index; padding rows and rows past the expert point past the
-      // buffer's bound (2^31 > a_bytes) and read as zeros
-      a_rsrc = make_rsrc(g.a, g.a_bytes);
+    if constexpr (SWIGLU) {
+      int base = 0;
+      if (g.gathered) {
+        a_rsrc = make_rsrc(g.a, g.a_bytes);
+      } else if (empty) {
+        a_rsrc = make_rsrc(g.a, 0);
+      } else {
+        base = __builtin_amdgcn_readfirstlane(g.rows[row0]);
+        const int last = __builtin_amdgcn_readfirstlane(g.rows[min(row0 + C::BM, row_end) - 1]);
+        a_rsrc = make_rsrc(g.a + (int64_t)base * g.K, (int64_t)(last - base + 1) * g.K * 2);
+      }
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i) {
         const int r = (wave + i * C::NW) * C::RPB + ld_row;
-        const int src = (row0 + r < row_end) ? g.gather[row0 + r] : -1;
+        const int src = (row0 + r < row_end) ? g.rows[row0 + r] - base : -1;
         a_off[i] = src >= 0 ? 2u * ((uint32_t)src * (uint32_t)g.K + (uint32_t)(C::swz(r, ld_phys) * 8))
                             : 0x80000000u;
       }
     } else {
-      a_rsrc = make_rsrc(g.a + (int64_t)rbase * g.K, (int64_t)(row_end - rbase) * g.K * 2);
+      const int32_t* bcrow = g.ws + L.o_bcrow;
+      const int32_t* bval = g.ws + L.o_bval;
+      int crow0, nvalid, sub = 0, band = 0;
+      if (L.dn_merge > 0) {
+        crow0 = bcrow[band0];
+        nvalid = bcrow[band0 + nbt - 1] + bval[band0 + nbt - 1] - crow0;
+      } else {
+        band = mt / L.dn_sub;
+        sub = (mt - band * L.dn_sub) * C::BM;
+        crow0 = bcrow[band] + sub;
+        nvalid = max(0, min(C::BM, bval[band] - sub));
+      }
+      crow0 = __builtin_amdgcn_readfirstlane(crow0);
+      nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+      a_rsrc = make_rsrc(g.a + (int64_t)crow0 * g.K, (int64_t)nvalid * g.K * 2);
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i) {
-        const int r = (wave + i * C::NW) * C::RPB + ld_row;
-        const int rr = min(row0 + r, row_end - 1) - rbase;
-        a_off[i] = 2u * ((uint32_t)rr * (uint32_t)g.K + (uint32_t)(C::swz(r, ld_phys) * 8));
+        int r = (wave + i * C::NW) * C::RPB + ld_row;
+        // recomputed per tile: kept live across the K loop instead, the
+        // per-lane band index and offset spill to scratch
+        asm volatile("" : "+v"(r));
+        int src = -1;
+        if (L.dn_merge > 0) {
+          const int bi = r >> L.tb_log2, j = r & (L.tb_m - 1);
+          if (bi < nbt && j < bval[band0 + bi]) src = bcrow[band0 + bi] + j - crow0;
+        } else if (sub + r < bval[band]) {
+          src = r;
+        }
+        a_off[i] = src >= 0 ? 2u * ((uint32_t)src * (uint32_t)g.K + (uint32_t)(C::swz(r, ld_phys) * 8))
+                            : 0x80000000u;
       }
     }
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(g.w + (int64_t)e * g.w_rows * g.K, (int64_t)g.w_rows * g.K * 2);
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
       const int r = (wave + i * C::NW) * C::RPB + ld_row;
@@ -862,7 +902,7 @@ using Dn32 = Cfg<32, 256, 1, 4, kDn32BK, 3, 3>;
 hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const uint16_t* x, bool gathered, const uint16_t* wgu,
                          uint16_t* h, uint32_t epoch, int grid, hipStream_t s) {
   GemmArgs a{ws, x, wgu, h, nullptr, epoch, L.d, L.f, 2 * L.f, L.f, grid, 0,
-             gathered ? ws + L.o_src : nullptr, gathered ? (int64_t)L.R * L.d * 2 : 0};
+             ws + (gathered ? L.o_cmpsrc : L.o_cmprow), gathered ? 1 : 0, gathered ? (int64_t)L.R * L.d * 2 : 0};
   RecvPtrs none{};
   hipLaunchKernelGGL((grouped_gemm_kernel<GuCfg, true, false>), dim3(grid), dim3(GuCfg::NT), 0, s, L, a, none);
   return hipGetLastError();
@@ -871,7 +911,7 @@ hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const uint16_t* x, bo
 hipError_t launch_down(const PlanLayout& L, int32_t* ws, const uint16_t* h, const uint16_t* wd, uint16_t* y,
                        uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks, int n_prod,
                        int grid, hipStream_t s) {
-  GemmArgs a{ws, h, wd, y, flags, epoch, L.f, L.d, L.d, 0, n_prod, timeout_ticks, nullptr, 0};
+  GemmArgs a{ws, h, wd, y, flags, epoch, L.f, L.d, L.d, 0, n_prod, timeout_ticks, nullptr, 0, 0};
   switch (L.dn_bm) {
     case 256:
       hipLaunchKernelGGL((grouped_gemm_kernel<Dn256, false, true>), dim3(grid), dim3(Dn256::NT), 0, s, L, a, recv);

@@ -60,6 +60,7 @@ struct PlanLayout {
   int R, rows_cap, bands_cap, T_r, NB, NB_r, gu_mt_cap;
   int dn_bm, dn_sub, dn_ntn, dn_tpb;   // down GEMM: tile rows, tiles per band row, n tiles, tiles per band
   int dn_merge;                        // > 0: down m-tiles of up to dn_merge row-contiguous bands (table)
+  int tb_log2;                         // log2(tb_m) when dn_merge > 0 (tb_m then divides 256)
   int gu_ntn;                          // gate/up GEMM n tiles (f / 128)
   int build_stage;                     // plan_build copies the block histograms into LDS
   int band_table;                      // plan_build's band -> group table in LDS (bands_cap, or 0)
@@ -72,6 +73,11 @@ struct PlanLayout {
   int64_t o_gumt_row, o_gumt_exp;
   int64_t o_pad;                       // [2][E_l*W]: first padding row and padding rows of every remote group
   int64_t o_dnt_row, o_dnt_exp, o_dnt_band, o_dnt_nb;
+  // compacted rows (the layout without its padding rows, in layout order):
+  // start of every expert, offset of every group inside its expert, first
+  // compacted row of every band, and per compacted row its layout row and
+  // its received row
+  int64_t o_crowoff, o_ccum, o_bcrow, o_cmprow, o_cmpsrc;
   int64_t o_skc;                       // uint64 [2][kMaxProducers] stream-K tile counters (gate/up, down)
   int64_t o_skp;                       // float [sk_slots][256*256] stream-K partial sums
   int64_t total_words;
@@ -89,7 +95,7 @@ struct RecvPtrs {
 // per-block histograms are copied in too.  The host sizes the launch's
 // dynamic LDS with the same function the kernel carves it with.
 struct BuildLds {
-  int c, grp, base, gstart, low, me, rowoff, rb, order, baser, gupre, dnpre, sh, misc;
+  int c, grp, base, gstart, low, me, rowoff, rb, order, baser, gupre, dnpre, sh, misc, ccum, ce, crowoff;
   int band_g, stage_bh, stage_bhr, total;
 };
 #if defined(__HIPCC__)
@@ -113,6 +119,9 @@ inline BuildLds build_lds(int W, int E_l, int E, int NB, int NB_r, int band_tabl
   s.dnpre = o; o += 2 * E_l + 1;
   s.sh = o; o += 16;
   s.misc = o; o += 8;
+  s.ccum = o; o += EW;
+  s.ce = o; o += E_l;
+  s.crowoff = o; o += E_l + 1;
   s.band_g = o; o += band_table;              // group of every band (0: not kept)
   o = (o + 3) & ~3;                           // 16-byte aligned staging
   s.stage_bh = o; if (stage) o += (NB * (E_l + 2) + 3) & ~3;

@@ -191,6 +191,9 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   int* dnpre = smem + S.dnpre;     // [2 E_l + 1] down row tiles before each run
   int* sh = smem + S.sh;           // scan scratch
   int* misc = smem + S.misc;       // [0] remote segments
+  int* ccum = smem + S.ccum;       // [E_l][W] group offsets inside X_e's compacted rows
+  int* ce = smem + S.ce;           // [E_l] real rows of X_e
+  int* crowoff = smem + S.crowoff; // [E_l + 1] first compacted row of X_e
   const int32_t* bh = ws + L.o_bh;
   int32_t* bp = ws + L.o_bp;
   int32_t* brecv = ws + L.o_brecv;
@@ -286,14 +289,17 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   // (d) layout: padded group offsets inside X_e, remote owners ascending then
   //     r; receive-buffer bases: owner o's pairs below global expert r*E_l + e
   for (int e = tid; e < E_l; e += nt) {
-    int run = 0;
+    int run = 0, crun = 0;
     for (int q = 0; q < W; ++q) {
       const int o = (q < W - 1) ? (q < r ? q : q + 1) : r;
       grp[e * W + o] = run;
+      ccum[e * W + o] = crun;
       const int n = c[e * W + o];
       run += (o == r) ? n : ((n + tb - 1) / tb) * tb;
+      crun += n;
     }
     me[e] = run;
+    ce[e] = crun;
   }
   for (int o = tid; o < W; o += nt) {
     int run = low[o];
@@ -307,8 +313,14 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     rb[e] = n;
   }
   __syncthreads();
-  const int M = scan_items(
-      E_l, [&](int e) { return me[e]; }, [&](int e, int pre) { rowoff[e] = pre; }, sh);
+  const int2 mtot = scan_items2(
+      E_l, [&](int e) { return make_int2(me[e], ce[e]); },
+      [&](int e, int2 pre) {
+        rowoff[e] = pre.x;
+        crowoff[e] = pre.y;
+      },
+      sh);
+  const int M = mtot.x;
   // rule (ii) order: more remote bands first, ties to the lower id
   for (int e = tid; e < E_l; e += nt) {
     int rank = 0;
@@ -319,7 +331,10 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     }
     order[rank] = e;
   }
-  if (tid == 0) rowoff[E_l] = M;
+  if (tid == 0) {
+    rowoff[E_l] = M;
+    crowoff[E_l] = mtot.y;   // = rcount
+  }
   __syncthreads();
 
   // (e) groups in schedule order: remote groups of experts in rule (ii) order
@@ -358,6 +373,7 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   int32_t* bsrc = ws + L.o_bsrc;
   int32_t* bdoff = ws + L.o_bdoff;
   int32_t* bval = ws + L.o_bval;
+  int32_t* bcrow = ws + L.o_bcrow;
   int* band_g = L.band_table > 0 ? smem + S.band_g : nullptr;
   int32_t* pad_st = ws + L.o_pad;         // read by plan_place, which writes the padding entries
   int32_t* pad_ct = pad_st + EW;
@@ -369,8 +385,10 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     const int gs = gstart[gi];
     const int rowb = rowoff[e] + grp[e * W + o];
     const int dstb = base[o * E_l + e];
+    const int crowb = crowoff[e] + ccum[e * W + o];
     for (int q = 0; q < nb; ++q) {
       if (band_g) band_g[gs + q] = gi;
+      bcrow[gs + q] = crowb + q * tb;
       bexp[gs + q] = e;
       bdst[gs + q] = o;
       bsrc[gs + q] = rowb + q * tb;
@@ -454,17 +472,18 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   const int n_rsegs = misc[0] >= 0 ? misc[0] : NS;
   if (tid == 0) sunit[NS] = U;
 
-  // (i) gate/up m-tiles: every X_e cut into kGuBM-row tiles, experts in
-  //     rule (ii) order; one thread per tile
+  // (i) gate/up m-tiles: the compacted rows of every X_e (its real rows,
+  //     padding left out) cut into kGuBM-row tiles, experts in rule (ii)
+  //     order; one thread per tile.  The GEMM computes no padding row.
   int32_t* mt_row = ws + L.o_gumt_row;
   int32_t* mt_exp = ws + L.o_gumt_exp;
   const int NMT = scan_items(
-      E_l, [&](int q) { return (me[order[q]] + kGuBM - 1) / kGuBM; },
+      E_l, [&](int q) { return (ce[order[q]] + kGuBM - 1) / kGuBM; },
       [&](int q, int pre) { gupre[q] = pre; }, sh);
   for (int t = tid; t < NMT; t += nt) {
     const int q = upper_index(gupre, E_l, t);
     const int e = order[q];
-    mt_row[t] = rowoff[e] + (t - gupre[q]) * kGuBM;
+    mt_row[t] = crowoff[e] + (t - gupre[q]) * kGuBM;
     mt_exp[t] = e;
   }
 
@@ -520,7 +539,9 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     ws[L.o_c + i] = c[i];
     ws[L.o_grp + i] = grp[i];
     ws[L.o_base + i] = base[i];
+    ws[L.o_ccum + i] = ccum[i];
   }
+  for (int i = tid; i <= E_l; i += nt) ws[L.o_crowoff + i] = crowoff[i];
   for (int i = tid; i < W; i += nt) ws[L.o_low + i] = low[i];
   for (int i = tid; i < E_l; i += nt) {
     ws[L.o_me + i] = me[i];
@@ -597,6 +618,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_place_kernel(PlanLayout L, 
   __syncthreads();
   const int32_t* rowoff = ws + L.o_rowoff;
   const int32_t* grp = ws + L.o_grp;
+  const int32_t* crowoff = ws + L.o_crowoff;
+  const int32_t* ccum = ws + L.o_ccum;
+  int32_t* cmp_row = ws + L.o_cmprow;
+  int32_t* cmp_src = ws + L.o_cmpsrc;
   const int32_t* bp = ws + L.o_bp + (int64_t)b * (E_l + 1);
   const int recv_base = ws[L.o_brecv + b];
   int32_t* src = ws + L.o_src;
@@ -629,8 +654,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_place_kernel(PlanLayout L, 
       int rank_e = run[e] + re, rank_l = run[E_l] + rl;
       for (int x = 0; x < w; ++x) { rank_e += wc[x * NX + e]; rank_l += wc[x * NX + E_l]; }
       const int dest = rowoff[e] + grp[e * W + o] + bp[e] + rank_e;
+      const int cdest = crowoff[e] + ccum[e * W + o] + bp[e] + rank_e;
       const int i = recv_base + rank_l;
       if (dest < L.rows_cap && i < L.R) src[dest] = i;
+      if (cdest < L.R && i < L.R) {
+        cmp_row[cdest] = dest;
+        cmp_src[cdest] = i;
+      }
     }
     if (own && g >= 0 && g < E) {
       int rank_g = run_g[g] + rg;

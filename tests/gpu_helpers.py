@@ -156,7 +156,41 @@ def oracle_sample(name: str):
 
 
 def rows_of(t: torch.Tensor, rows: np.ndarray) -> np.ndarray:
-    return host_bits(t.index_select(0, torch.from_numpy(rows).cuda()))
+    return host_bits(t.index_select(0, torch.from_numpy(np.asarray(rows, dtype=np.int64)).cuda()))
+
+
+def compact_index(pl) -> np.ndarray:
+    """Compacted row of every layout row (-1 for padding): the GPU's h holds
+    the layout's real rows without its padding, in layout order, so a real
+    row's index there is the number of real rows before it."""
+    real = pl.src_index >= 0
+    idx = np.cumsum(real) - 1
+    return np.where(real, idx, -1).astype(np.int64)
+
+
+def h_rows(share, pl, rows, h_ref):
+    """GPU h and the oracle's h of the real rows among `rows` (padding rows
+    have no h row on the GPU; the oracle's h of a padding row is zero)."""
+    ci = compact_index(pl)[rows]
+    keep = ci >= 0
+    return rows_of(share.h, ci[keep]), h_ref[keep]
+
+
+def expected_compacted(pl):
+    """The compacted-row tables implied by the oracle plan: first compacted
+    row of every X_e, offset of every group inside its X_e, first compacted
+    row of every band, and layout row / received row of every compacted row."""
+    ci = compact_index(pl)
+    crow_off = np.array([int(np.count_nonzero(pl.src_index[:pl.row_off[e]] >= 0)) for e in range(pl.E_l + 1)])
+    grp = np.zeros((pl.E_l, pl.W), np.int64)
+    for e in range(pl.E_l):
+        for o in range(pl.W):
+            a = int(pl.row_off[e] + pl.grp_off[e, o])
+            grp[e, o] = int(np.count_nonzero(pl.src_index[pl.row_off[e]:a] >= 0))
+    band_crow = ci[pl.bands["src_row"]]
+    real = np.nonzero(pl.src_index >= 0)[0]
+    return {"crow_off": crow_off, "grp_crow": grp, "band_crow": band_crow,
+            "cmp_row": real, "cmp_src": pl.src_index[real]}
 
 
 def layout_x(pl, x_recv):

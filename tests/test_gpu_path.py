@@ -22,8 +22,8 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import (ATOL, RTOL, case, dev_bf16, host_bits, layout_x, oracle_ffn_rows, oracle_sample,
-                         owner_slice, rows_of, sample_rows, say, shape_of, tol_ratio, weights)
+from gpu_helpers import (ATOL, RTOL, case, dev_bf16, h_rows, host_bits, layout_x, oracle_ffn_rows,
+                         oracle_sample, owner_slice, rows_of, sample_rows, say, shape_of, tol_ratio, weights)
 from oracle import combine as OC
 from oracle import scale as OS
 from oracle import bf16 as OB
@@ -62,7 +62,7 @@ def test_ffn_rows_match_oracle(name):
     c, share, _, _ = planned(name, m.MODE_SERIAL)
     pl = c["plan"]
     rows, h_ref, y_ref = oracle_sample(name)
-    h = rows_of(share.h, rows)
+    h, h_ref = h_rows(share, pl, rows, h_ref)
     y = rows_of(share.y, rows)
     scale_aware = name == "tiny"
     rh = tol_ratio(h, h_ref, scale_aware)
@@ -202,7 +202,7 @@ def test_gathered_rows_equal_the_layout_path(name):
     import moe_expert_tile_amd as m
     c, share, wgu_d, wd_d = planned(name, m.MODE_SERIAL)
     cfg, pl = c["cfg"], c["plan"]
-    H, Y = host_bits(share.h[:pl.M]), host_bits(share.y[:pl.M])
+    H, Y = host_bits(share.h[:pl.R]), host_bits(share.y[:pl.M])
     recv_ref = [host_bits(r) for r in share.recv]
     written = OC.written_rows(pl)
     g = m.RankShare(shape_of(cfg, pl.R))
@@ -218,12 +218,12 @@ def test_gathered_rows_equal_the_layout_path(name):
         g.combine(wgu_d, wd_d, mode=mode, x_recv=xr)
         assert g.status() == m.MOE_OK
         # gathered h and y straight against the oracle ...
-        rh = tol_ratio(rows_of(g.h, rows), h_ref)
+        rh = tol_ratio(*h_rows(g, pl, rows, h_ref))
         ry = tol_ratio(rows_of(g.y, rows), y_ref)
         say(f"[gathered] {name} mode={mode} worst h {rh:.3f} y {ry:.3f} against the oracle")
         assert rh <= 1.0 and ry <= 1.0
         # ... and bit for bit against the materialized layout's
-        assert np.array_equal(host_bits(g.h[:pl.M]), H), mode
+        assert np.array_equal(host_bits(g.h[:pl.R]), H), mode
         y = host_bits(g.y[:pl.M])
         if mode == m.MODE_SERIAL:
             assert np.array_equal(y, Y)

@@ -6,7 +6,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import case, dev_bf16, expected_plan, host_bits, layout_x, plan_arrays, say, shape_of
+from gpu_helpers import (case, dev_bf16, expected_compacted, expected_plan, host_bits, layout_x, plan_arrays, say,
+                         shape_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +44,13 @@ def test_plan_metadata_bit_exact(name, mgb):
     exp = expected_plan(pl)
     for k, v in exp.items():
         assert np.array_equal(np.asarray(got[k]).astype(np.int64), np.asarray(v).astype(np.int64)), k
+    # the compacted-row tables the GEMMs run on (the layout without padding)
+    cx = expected_compacted(pl)
+    sizes = {"crow_off": pl.E_l + 1, "grp_crow": pl.E_l * pl.W, "band_crow": pl.n_bands,
+             "cmp_row": pl.R, "cmp_src": pl.R}
+    for k, v in cx.items():
+        g = share.array(k, sizes[k]).astype(np.int64)
+        assert np.array_equal(g, np.asarray(v, dtype=np.int64).reshape(-1)), k
 
 
 @pytest.mark.parametrize("name", WORKLOADS)
@@ -70,14 +78,17 @@ def test_replanning_reuses_the_workspace():
 
 
 def expected_tiles(pl):
-    """GEMM row tiles implied by the oracle plan: gate/up tiles cut every X_e
-    (experts in rule (ii) order) into 256-row pieces; down tiles cut each
-    maximal run of bands in S order with one expert and one side (remote or
-    local) into pieces of at most 256 / tb_M bands."""
+    """GEMM row tiles implied by the oracle plan: gate/up tiles cut the real
+    rows of every X_e (its compacted rows, experts in rule (ii) order) into
+    256-row pieces; down tiles cut each maximal run of bands in S order with
+    one expert and one side (remote or local) into pieces of at most
+    256 / tb_M bands."""
     gu_row, gu_exp = [], []
+    crow_off = expected_compacted(pl)["crow_off"]
     for e in pl.expert_order:
-        for i in range(-(-int(pl.m_e[e]) // 256)):
-            gu_row.append(int(pl.row_off[e]) + 256 * i)
+        n = int(crow_off[e + 1] - crow_off[e])
+        for i in range(-(-n // 256)):
+            gu_row.append(int(crow_off[e]) + 256 * i)
             gu_exp.append(int(e))
     P = 256 // pl.tb_m
     b = pl.bands
