@@ -221,6 +221,31 @@ int moe_expert_combine(const moe_shape* shape, const void* plan_ws, const uint16
                        uint16_t* const* recv, const moe_combine_opts* opts, void* stream);
 
 /*
+ * moe_expert_combine_noalloc — moe_expert_combine for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, modes, results and
+ * errors as moe_expert_combine, and it allocates nothing: the scratch of its
+ * kernels (the fp32 partial sums of the GEMMs' K-split tails, their tile
+ * counters, the copy-claim counters of the overlapped launch) is a static
+ * device array of 64 MiB + 8 KiB that every GPU the library runs on holds
+ * until the process ends; its device address is looked up once per device.
+ * So the plan workspace only needs the first moe_plan_view.sk_counters
+ * bytes of plan_bytes (the K-split part at its end is not used).
+ * Limit: at most 256 partial-sum slots of 256 KiB.  No input is refused
+ * for it: a K-split tail that would need more pieces than the slots allow
+ * is cut into fewer, longer pieces, or not split at all, which changes only
+ * the fp32 summation order of those tiles.
+ * The counters are cleared at the start of every call (a small fill kernel
+ * on `stream`).  Every call on one GPU shares that GPU's array: calls that
+ * overlap on the device (other streams, or concurrent host threads) race and
+ * give wrong results; calls on one stream never overlap.
+ */
+int moe_expert_combine_noalloc(const moe_shape* shape, const void* plan_ws, const uint16_t* x_layout,
+                               const uint16_t* w_gate_up, const uint16_t* w_down,
+                               uint16_t* h, uint16_t* y, uint32_t* flags, uint32_t epoch,
+                               uint16_t* const* recv, const moe_combine_opts* opts, void* stream);
+
+/*
  * moe_scale — step 5 of the distributed MoE forward (tile-signal notes §2.2;
  * §2.1: the output is the gate-weighted sum of the selected experts' outputs):
  *   out[t] = bf16( sum_{j<k} topk_w[t][j] * recv_self[pos[t][j]] ), fp32 in j order.

@@ -81,6 +81,8 @@ def _load():
         "moe_plan": (I, [P(moe_shape), V, V, V, V, V]),
         "moe_expert_combine": (I, [P(moe_shape), V, V, V, V, V, V, V, ctypes.c_uint32,
                                    P(ctypes.c_void_p), P(moe_combine_opts), V]),
+        "moe_expert_combine_noalloc": (I, [P(moe_shape), V, V, V, V, V, V, V, ctypes.c_uint32,
+                                           P(ctypes.c_void_p), P(moe_combine_opts), V]),
         "moe_scale": (I, [P(moe_shape), V, V, V, V, V]),
         "moe_device_status": (I, [V, V]),
         "moe_device_cus": (I, []),
@@ -94,7 +96,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ["moe_status_string", "moe_query_sizes", "moe_plan_offsets", "moe_plan",
-            "moe_expert_combine", "moe_scale", "moe_device_status", "moe_device_cus"]
+            "moe_expert_combine", "moe_expert_combine_noalloc", "moe_scale", "moe_device_status",
+            "moe_device_cus"]
 
 
 def library_path() -> str:
@@ -162,9 +165,14 @@ def moe_plan(shape: Shape, topk_ids, x_recv, plan_ws, x_layout, stream=None) -> 
 def moe_expert_combine(shape: Shape, plan_ws, x_layout, w_gate_up, w_down, h, y, flags, epoch: int,
                        recv: List, mode: int = MODE_OVERLAP, consumer_cus: int = 0,
                        consumer_blocks: int = 0, spin_timeout_ns: int = 0,
-                       events: Optional[Sequence] = None, stream=None, x_recv=None) -> None:
+                       events: Optional[Sequence] = None, stream=None, x_recv=None,
+                       noalloc: bool = False) -> None:
     """x_layout=None with x_recv given: the gate/up GEMM gathers its rows from
-    x_recv through the plan's src_index (the layout is never materialized)."""
+    x_recv through the plan's src_index (the layout is never materialized).
+    noalloc=True calls moe_expert_combine_noalloc (kernel scratch in the
+    library's static device array instead of the plan workspace)."""
+    fn = _lib.moe_expert_combine_noalloc if noalloc else _lib.moe_expert_combine
+    name = "moe_expert_combine_noalloc" if noalloc else "moe_expert_combine"
     arr = (ctypes.c_void_p * max(1, len(recv)))(*[_ptr(r) for r in recv])
     opts = moe_combine_opts()
     opts.mode = mode
@@ -175,10 +183,9 @@ def moe_expert_combine(shape: Shape, plan_ws, x_layout, w_gate_up, w_down, h, y,
     if events is not None:
         for i, ev in enumerate(events):
             opts.events[i] = None if ev is None else int(ev.cuda_event)
-    _check(_lib.moe_expert_combine(shape.ptr, _ptr(plan_ws), _ptr(x_layout), _ptr(w_gate_up),
-                                   _ptr(w_down), _ptr(h), _ptr(y), _ptr(flags), int(epoch),
-                                   ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)),
-                                   ctypes.byref(opts), _stream(stream)), "moe_expert_combine")
+    _check(fn(shape.ptr, _ptr(plan_ws), _ptr(x_layout), _ptr(w_gate_up), _ptr(w_down), _ptr(h), _ptr(y),
+              _ptr(flags), int(epoch), ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)),
+              ctypes.byref(opts), _stream(stream)), name)
 
 
 def moe_scale(shape: Shape, plan_ws, recv_self, topk_w, out, stream=None) -> None:

@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["plan.hip", "gemm.hip", "combine.hip", "scale.hip", "api.cpp"]
+SOURCES = ["plan.hip", "gemm.hip", "combine.hip", "scale.hip", "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -296,9 +296,17 @@ int moe_plan(const moe_shape* s, const int32_t* topk_ids, const uint16_t* x_recv
   return hip_rc(launch_plan(L, topk_ids, x_recv, (int32_t*)plan_ws, x_layout, (hipStream_t)stream));
 }
 
-int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* x_layout, const uint16_t* w_gate_up,
-                       const uint16_t* w_down, uint16_t* h, uint16_t* y, uint32_t* flags, uint32_t epoch,
-                       uint16_t* const* recv, const moe_combine_opts* opts, void* stream) {
+}  // extern "C"
+
+namespace moe {
+
+// moe_expert_combine with its kernels' scratch either in the plan workspace
+// (get_scratch == nullptr) or where get_scratch(device, &sc) puts it; then
+// the counters are cleared first, since that scratch outlives the call.
+int combine_impl(const moe_shape* s, const void* plan_ws, const uint16_t* x_layout, const uint16_t* w_gate_up,
+                 const uint16_t* w_down, uint16_t* h, uint16_t* y, uint32_t* flags, uint32_t epoch,
+                 uint16_t* const* recv, const moe_combine_opts* opts, void* stream,
+                 int (*get_scratch)(int dev, Scratch* out)) {
   int rc = valid_shape(s);
   if (rc) return rc;
   moe_combine_opts o;
@@ -353,6 +361,16 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   int full_grid = std::min(cus, kMaxProducers);
   full_grid -= full_grid % 8;
   if (full_grid < 8) full_grid = 8;
+  Scratch sc;
+  if (get_scratch) {
+    rc = get_scratch(dev, &sc);
+    if (rc) return rc;
+  } else {
+    sc.sk_part = (float*)(ws_rw + L.o_skp);
+    sc.sk_ctr = (uint64_t*)(ws_rw + L.o_skc);
+    sc.claim = ws_rw + L.o_hdr + H_CLAIM;
+    sc.sk_slots = L.sk_slots;
+  }
 
   if (o.mode == MOE_MODE_COPY_ROWS) {
     record(o.events[4], st);
@@ -367,13 +385,17 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
     record(o.events[5], st);
     return rc;
   }
+  if (get_scratch) {
+    rc = hip_rc(launch_clear_counters(sc, st));
+    if (rc) return rc;
+  }
   record(o.events[0], st);
-  rc = hip_rc(launch_gateup(L, ws_rw, a_rows, gathered, w_gate_up, h, epoch, full_grid, st));
+  rc = hip_rc(launch_gateup(L, ws_rw, sc, a_rows, gathered, w_gate_up, h, epoch, full_grid, st));
   record(o.events[1], st);
   if (rc) return rc;
   if (o.mode == MOE_MODE_SERIAL) {
     record(o.events[2], st);
-    rc = hip_rc(launch_down(L, ws_rw, h, w_down, y, flags, epoch, rp, timeout, full_grid, full_grid, st));
+    rc = hip_rc(launch_down(L, ws_rw, sc, h, w_down, y, flags, epoch, rp, timeout, full_grid, full_grid, st));
     record(o.events[3], st);
     if (rc) return rc;
     record(o.events[4], st);
@@ -391,10 +413,20 @@ int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* 
   const int n_cons = o.consumer_blocks ? o.consumer_blocks : o.consumer_cus;
   record(o.events[2], st);
   record(o.events[4], st);
-  rc = hip_rc(launch_down(L, ws_rw, h, w_down, y, flags, epoch, rp, timeout, n_prod, n_prod + n_cons, st));
+  rc = hip_rc(launch_down(L, ws_rw, sc, h, w_down, y, flags, epoch, rp, timeout, n_prod, n_prod + n_cons, st));
   record(o.events[3], st);
   record(o.events[5], st);
   return rc;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_expert_combine(const moe_shape* s, const void* plan_ws, const uint16_t* x_layout, const uint16_t* w_gate_up,
+                       const uint16_t* w_down, uint16_t* h, uint16_t* y, uint32_t* flags, uint32_t epoch,
+                       uint16_t* const* recv, const moe_combine_opts* opts, void* stream) {
+  return combine_impl(s, plan_ws, x_layout, w_gate_up, w_down, h, y, flags, epoch, recv, opts, stream, nullptr);
 }
 
 int moe_scale(const moe_shape* s, const void* plan_ws, const uint16_t* recv_self, const float* topk_w, uint16_t* out,

@@ -176,7 +176,7 @@ __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_
 
 // Consumer with claimed work, for the overlapped down-GEMM launch: the
 // remote copy units are handed out kClaimUnits at a time, in schedule order,
-// from the counter hdr[H_CLAIM] (zeroed by the gate/up launch before it).
+// from the counter claim[0] (zeroed by the gate/up launch before it).
 // The launch's consumer workgroups run it from the start; producers that
 // have run out of tiles join them, so the dedicated consumer can be small
 // and the copies left when the last tiles finish are shared by every CU.
@@ -190,7 +190,7 @@ __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_
 constexpr int kClaimUnitsMax = 8;
 
 template <int NT>
-__device__ void consume_claimed(const PlanLayout& L, int32_t* ws, const uint16_t* __restrict__ y,
+__device__ void consume_claimed(const PlanLayout& L, int32_t* ws, int32_t* claim, const uint16_t* __restrict__ y,
                                 const uint32_t* __restrict__ flags, uint32_t epoch, const RecvPtrs& recv,
                                 int64_t timeout, int* s_word) {
   int32_t* hdr = ws + L.o_hdr;
@@ -207,14 +207,14 @@ __device__ void consume_claimed(const PlanLayout& L, int32_t* ws, const uint16_t
   const int cu = max(1, min(kClaimUnitsMax, U / (2 * (int)gridDim.x)));   // units per claim
   const int n_claims = (U + cu - 1) / cu;
   const int tid = threadIdx.x;
-  if (tid == 0) s_word[1] = __hip_atomic_fetch_add(hdr + H_CLAIM, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) s_word[1] = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   int k = s_word[1];
   __syncthreads();
   int seg = 0, ready = -1;
   while (k < n_claims) {
     // the next claim is in flight while this one is copied
-    if (tid == 0) s_word[1] = __hip_atomic_fetch_add(hdr + H_CLAIM, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) s_word[1] = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int j = 0; j < cu; ++j) {
       const int u = k * cu + j;
       if (u < U) {

@@ -149,6 +149,7 @@ struct GemmArgs {
   const int32_t* rows;
   int gathered;
   int64_t a_bytes;        // gathered: bytes of `a` (< 2^31)
+  Scratch sc;             // stream-K partials and counters, copy-claim counters
 };
 
 __device__ __forceinline__ void stamp_max(int32_t* hdr, int word) {
@@ -296,8 +297,8 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     // the overlapped down GEMM that follows on this stream claims its copy
     // units from these counters
     if (blockIdx.x == 0 && tid == 0) {
-      hdr[H_CLAIM] = 0;
-      hdr[H_STARTED] = 0;
+      g.sc.claim[0] = 0;
+      g.sc.claim[1] = 0;
     }
   }
   const bool overlapped = FLAGS && (int)gridDim.x > g.n_prod;
@@ -307,14 +308,14 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     // hold the GEMM's LDS footprint, so each has a CU of its own; producers
     // never wait for them.
     if ((int)blockIdx.x >= g.n_prod) {
-      consume_claimed<C::NT>(L, g.ws, g.out, g.flags, g.epoch, recv, g.timeout, (int*)lds);
+      consume_claimed<C::NT>(L, g.ws, g.sc.claim, g.out, g.flags, g.epoch, recv, g.timeout, (int*)lds);
       if (tid == 0) stamp_max(hdr, H_T_CONS_END);
       return;
     }
   }
   if (hdr[H_ERROR] != 0) return;
   if (overlapped && tid == 0)
-    __hip_atomic_fetch_add(hdr + H_STARTED, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(g.sc.claim + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Row tiles are taken in two regions, each in grouped order: for the down
   // GEMM the remote bands' tiles [0, n_mt_r) before the local bands' (so the
@@ -354,10 +355,12 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
   if (total > 0 && (KT >= kMinSkKT || (2 * total <= G && KT >= kMinSkKTOneRound))) {
     const int rem = total % G;
     const int64_t w = (int64_t)rem * KT;
-    const int g_sk = (int)min((int64_t)G, w / kMinSkSteps);
-    // slot 2 * s + piece of the partial sums for s < g_sk: the workspace
-    // holds as many as the host sized it for
-    if (rem != 0 && 4 * rem <= 3 * G && 2 * g_sk <= L.sk_slots) {
+    // pieces: at most one per workgroup, at least kMinSkSteps long, and as
+    // many as the scratch has slot pairs for (slot 2 * s + piece for
+    // s < G_sk); at least one per tile, so that a piece spans at most two
+    // tiles
+    const int g_sk = (int)min((int64_t)min(G, g.sc.sk_slots / 2), w / kMinSkSteps);
+    if (rem != 0 && 4 * rem <= 3 * G && g_sk >= rem) {
       full = total - rem;
       sk_tiles = rem;
       W_sk = w;
@@ -370,8 +373,8 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     sk_cur = sk_lo(slot);
     sk_hi = sk_lo(slot + 1);
   }
-  float* sk_part = (float*)(g.ws + L.o_skp);
-  uint64_t* sk_ctr = (uint64_t*)(g.ws + L.o_skc) + (SWIGLU ? 0 : kMaxProducers);
+  float* sk_part = g.sc.sk_part;
+  uint64_t* sk_ctr = g.sc.sk_ctr + (SWIGLU ? 0 : kMaxProducers);
 
   // load-side lane constants: lane l fills row RPB q + l / CPR, physical chunk
   // l % CPR, so it must fetch the logical chunk swz(row, l % CPR)
@@ -871,12 +874,12 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       // layer: 5 us slower down GEMM).
       __syncthreads();   // every wave is done with the LDS ring
       int* s_word = (int*)lds;
-      if (tid == 0) s_word[0] = __hip_atomic_load(hdr + H_STARTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) s_word[0] = __hip_atomic_load(g.sc.claim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       const bool all_started = s_word[0] == g.n_prod;
       __syncthreads();
       if (all_started) {
-        consume_claimed<C::NT>(L, g.ws, g.out, g.flags, g.epoch, recv, g.timeout, s_word);
+        consume_claimed<C::NT>(L, g.ws, g.sc.claim, g.out, g.flags, g.epoch, recv, g.timeout, s_word);
         if (tid == 0) stamp_max(hdr, H_T_CONS_END);
       }
     }
@@ -897,21 +900,31 @@ static_assert(Dn256::BK == kDnBK, "the host sizes the stream-K scratch with this
 using Dn64 = Cfg<64, 256, 1, 4, kDn64BK, 3, 3>;
 using Dn32 = Cfg<32, 256, 1, 4, kDn32BK, 3, 3>;
 
+__global__ __launch_bounds__(256) void clear_counters_kernel(uint64_t* ctr, int n, int32_t* claim) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) ctr[i] = 0;
+  if (threadIdx.x < 2) claim[threadIdx.x] = 0;
+}
+
 }  // namespace
 
-hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const uint16_t* x, bool gathered, const uint16_t* wgu,
-                         uint16_t* h, uint32_t epoch, int grid, hipStream_t s) {
+hipError_t launch_clear_counters(const Scratch& sc, hipStream_t s) {
+  hipLaunchKernelGGL(clear_counters_kernel, dim3(1), dim3(256), 0, s, sc.sk_ctr, 2 * kMaxProducers, sc.claim);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const Scratch& sc, const uint16_t* x, bool gathered,
+                         const uint16_t* wgu, uint16_t* h, uint32_t epoch, int grid, hipStream_t s) {
   GemmArgs a{ws, x, wgu, h, nullptr, epoch, L.d, L.f, 2 * L.f, L.f, grid, 0,
-             ws + (gathered ? L.o_cmpsrc : L.o_cmprow), gathered ? 1 : 0, gathered ? (int64_t)L.R * L.d * 2 : 0};
+             ws + (gathered ? L.o_cmpsrc : L.o_cmprow), gathered ? 1 : 0, gathered ? (int64_t)L.R * L.d * 2 : 0, sc};
   RecvPtrs none{};
   hipLaunchKernelGGL((grouped_gemm_kernel<GuCfg, true, false>), dim3(grid), dim3(GuCfg::NT), 0, s, L, a, none);
   return hipGetLastError();
 }
 
-hipError_t launch_down(const PlanLayout& L, int32_t* ws, const uint16_t* h, const uint16_t* wd, uint16_t* y,
-                       uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks, int n_prod,
-                       int grid, hipStream_t s) {
-  GemmArgs a{ws, h, wd, y, flags, epoch, L.f, L.d, L.d, 0, n_prod, timeout_ticks, nullptr, 0, 0};
+hipError_t launch_down(const PlanLayout& L, int32_t* ws, const Scratch& sc, const uint16_t* h, const uint16_t* wd,
+                       uint16_t* y, uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks,
+                       int n_prod, int grid, hipStream_t s) {
+  GemmArgs a{ws, h, wd, y, flags, epoch, L.f, L.d, L.d, 0, n_prod, timeout_ticks, nullptr, 0, 0, sc};
   switch (L.dn_bm) {
     case 256:
       hipLaunchKernelGGL((grouped_gemm_kernel<Dn256, false, true>), dim3(grid), dim3(Dn256::NT), 0, s, L, a, recv);

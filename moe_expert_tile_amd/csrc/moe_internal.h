@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe.h"
+
 namespace moe {
 
 constexpr int kMaxWorld = 64;
@@ -47,8 +49,8 @@ enum Hdr {
   H_T_PROD_END = 12, H_T_CONS_END = 14,
   H_DN_MT_R = 16,   // down row tiles of remote bands (they come first)
   // overlapped down-GEMM launch: copy-unit claims handed out so far, and
-  // producers that have started; both zeroed by the gate/up launch, which
-  // precedes every down GEMM on the same stream
+  // producers that have started (the default Scratch::claim); both zeroed by
+  // the gate/up launch, which precedes every down GEMM on the same stream
   H_CLAIM = 18, H_STARTED = 19,
   H_WORDS = 64
 };
@@ -88,6 +90,18 @@ struct PlanLayout {
 
 struct RecvPtrs {
   uint16_t* p[kMaxWorld];
+};
+
+// Scratch of moe_expert_combine's kernels: the stream-K partial sums and
+// their epoch-tagged tile counters, and the two copy-claim counters of the
+// overlapped down-GEMM launch (claims handed out, producers started).  By
+// default they live in the plan workspace; the allocation-free entry point
+// points them into a static device array instead.
+struct Scratch {
+  float* sk_part;       // [sk_slots][256*256] fp32
+  uint64_t* sk_ctr;     // [2][kMaxProducers]: gate/up, down
+  int32_t* claim;       // [2]: claims handed out, producers started
+  int sk_slots;
 };
 
 // LDS carve-out of plan_build_kernel, in int words: the expert x owner tables
@@ -135,20 +149,30 @@ constexpr int kBandTableMax = 8192;          // plan_build keeps a band -> group
 // host-side helpers (api.cpp)
 bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb,
                  const int32_t* tokens, int64_t R, PlanLayout* L);
+// moe_expert_combine; get_scratch == nullptr: the kernels' scratch is in the
+// plan workspace, else get_scratch(device, &sc) supplies it (the counters are
+// then cleared at the start of the call)
+int combine_impl(const moe_shape* s, const void* plan_ws, const uint16_t* x_layout, const uint16_t* w_gate_up,
+                 const uint16_t* w_down, uint16_t* h, uint16_t* y, uint32_t* flags, uint32_t epoch,
+                 uint16_t* const* recv, const moe_combine_opts* opts, void* stream,
+                 int (*get_scratch)(int dev, Scratch* out));
 
 // launchers (defined next to their kernels); all asynchronous on `s`
 hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t* x_recv,
                        int32_t* ws, uint16_t* x_layout, hipStream_t s);
 // gate/up GEMM: A rows from the layout `x` [rows_cap, d], or (gathered) from
 // x_recv [R, d] through the plan's src_index
-hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const uint16_t* x, bool gathered, const uint16_t* wgu,
-                         uint16_t* h, uint32_t epoch, int grid, hipStream_t s);
+hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const Scratch& sc, const uint16_t* x, bool gathered,
+                         const uint16_t* wgu, uint16_t* h, uint32_t epoch, int grid, hipStream_t s);
 // down GEMM: `n_prod` persistent producer workgroups; the grid's remaining
 // workgroups (if any) are consumers (consume.h).  Local bands are also
 // written to recv.p[L.r].
-hipError_t launch_down(const PlanLayout& L, int32_t* ws, const uint16_t* h, const uint16_t* wd, uint16_t* y,
-                       uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks, int n_prod,
-                       int grid, hipStream_t s);
+hipError_t launch_down(const PlanLayout& L, int32_t* ws, const Scratch& sc, const uint16_t* h, const uint16_t* wd,
+                       uint16_t* y, uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks,
+                       int n_prod, int grid, hipStream_t s);
+// zeroes the counters of `sc` (its tile counters and claim words) with a fill
+// kernel: the static scratch keeps the previous call's contents
+hipError_t launch_clear_counters(const Scratch& sc, hipStream_t s);
 hipError_t launch_consumer(const PlanLayout& L, int32_t* ws, const uint16_t* y,
                            const uint32_t* flags, uint32_t epoch, const RecvPtrs& recv,
                            int64_t timeout_ticks, int grid, hipStream_t s);
