@@ -582,10 +582,15 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     // its own fragments; the next stages' global->LDS loads go out after the
     // first substep's reads.  Steady-state steps issue both rings, the last
     // S_DEEP-1 steps fewer, so each step body is one branch-free scheduling
-    // region.
-    auto k_step = [&](int kt, auto issue_sh_tag, auto issue_dp_tag, int in_flight) __attribute__((always_inline)) {
+    // region.  FE (<= FM) is the number of this wave's 32-row blocks that
+    // take part: blocks past it hold padding rows only, and their
+    // accumulators stay zero.
+    auto k_step = [&](int kt, auto issue_sh_tag, auto issue_dp_tag, int in_flight, auto fe_tag)
+                      __attribute__((always_inline)) {
       constexpr bool ISSUE_SH = decltype(issue_sh_tag)::value;
       constexpr bool ISSUE_DP = decltype(issue_dp_tag)::value;
+      constexpr int FE = decltype(fe_tag)::value;
+      constexpr int FNE = FE > 0 ? C::FN : 0;
       stage_barrier<C>(in_flight);
       const uint16_t* sa = lds + (kt % C::SA) * C::A_ELEMS;
       const uint16_t* sb = lds + C::SA * C::A_ELEMS + (kt % C::SB) * C::B_ELEMS;
@@ -593,10 +598,10 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       auto read_frags = [&](int kk, int slot) __attribute__((always_inline)) {
         const int phys = ((2 * kk + lhalf) ^ rsw) * 8;
 #pragma unroll
-        for (int i = 0; i < C::FN; ++i)
+        for (int i = 0; i < FNE; ++i)
           pw[slot][i] = *(const bf16x8*)(sb + (prow[i] + lrow) * C::BK + phys);
 #pragma unroll
-        for (int j = 0; j < C::FM; ++j)
+        for (int j = 0; j < FE; ++j)
           px[slot][j] = *(const bf16x8*)(sa + (wave_m * C::WM + 32 * j + lrow) * C::BK + phys);
       };
       read_frags(0, 0);
@@ -610,31 +615,67 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       for (int kk = 0; kk < C::KK; ++kk) {
         if (kk + 1 < C::KK) read_frags(kk + 1, (kk + 1) & 1);
 #pragma unroll
-        for (int i = 0; i < C::FN; ++i)
+        for (int i = 0; i < FNE; ++i)
 #pragma unroll
-          for (int j = 0; j < C::FM; ++j)
+          for (int j = 0; j < FE; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pw[kk & 1][i], px[kk & 1][j], acc[i][j], 0, 0, 0);
       }
       if constexpr (SWIGLU) __builtin_amdgcn_s_setprio(0);
       constexpr int NVMEM = (ISSUE_SH ? (C::SA <= C::SB ? C::A_LOADS : C::B_LOADS) : 0) +
                             (ISSUE_DP ? (C::SA <= C::SB ? C::B_LOADS : C::A_LOADS) : 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::FN + C::FM, 0);
+      if constexpr (FE > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, FNE + FE, 0);
       if constexpr (NVMEM > 0) __builtin_amdgcn_sched_group_barrier(kSchedVmem, NVMEM, 0);
+      if constexpr (FE > 0) {
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
-        if (kk + 1 < C::KK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::FN + C::FM, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, C::FN * C::FM, 0);
+        for (int kk = 0; kk < C::KK; ++kk) {
+          if (kk + 1 < C::KK) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, FNE + FE, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, FNE * FE, 0);
+        }
       }
     };
     using T_ = std::integral_constant<bool, true>;
     using F_ = std::integral_constant<bool, false>;
     // one loop per step body (a branch between bodies inside one loop makes
     // the register allocator spill)
-    int kt = 0;
-    for (; kt + C::S_DEEP - 1 < KTt; ++kt) k_step(kt, T_{}, T_{}, C::DEEP_LOADS);
-    if constexpr (C::S_DEEP > C::S_SHALLOW)
-      for (; kt + C::S_SHALLOW - 1 < KTt; ++kt) k_step(kt, T_{}, F_{}, (kt + 1 < KTt) ? C::DEEP_LOADS : 0);
-    for (; kt < KTt; ++kt) k_step(kt, F_{}, F_{}, (kt + 1 < KTt) ? C::DEEP_LOADS : 0);
+    auto run_k = [&](auto fe_tag) __attribute__((always_inline)) {
+      int kt = 0;
+      for (; kt + C::S_DEEP - 1 < KTt; ++kt) k_step(kt, T_{}, T_{}, C::DEEP_LOADS, fe_tag);
+      if constexpr (C::S_DEEP > C::S_SHALLOW)
+        for (; kt + C::S_SHALLOW - 1 < KTt; ++kt) k_step(kt, T_{}, F_{}, (kt + 1 < KTt) ? C::DEEP_LOADS : 0, fe_tag);
+      for (; kt < KTt; ++kt) k_step(kt, F_{}, F_{}, (kt + 1 < KTt) ? C::DEEP_LOADS : 0, fe_tag);
+    };
+    if constexpr (!SWIGLU && C::BM == 256 && C::FM == 4) {
+      // Down tiles of 256 rows hold up to 256 / tb_M bands, each of whose
+      // rows past `valid` are padding.  This wave's blocks are rows
+      // [wave_m WM + 32 j, +32), j < FM; it multiplies blocks 0 .. fe - 1,
+      // fe - 1 being its last block with a real row, and every wave still
+      // joins every load and barrier.  The waves of one SIMD hold the two
+      // row halves of the same columns, so the SIMD's MFMA time follows the
+      // tile's real rows (DeepSeek-like layer: 45% of the layout rows are
+      // padding).
+      int fe = 0;
+      if (L.dn_merge > 0) {
+        const int32_t* bval = g.ws + L.o_bval;
+#pragma unroll
+        for (int j = C::FM - 1; j >= 0 && fe == 0; --j) {
+          const int r = wave_m * C::WM + 32 * j;      // first row of the block
+          const int bi = r >> L.tb_log2, q = r & (L.tb_m - 1);
+          if (bi < nbt && q < bval[band0 + bi]) fe = j + 1;
+        }
+      } else {
+        fe = C::FM;
+      }
+      fe = __builtin_amdgcn_readfirstlane(fe);
+      switch (fe) {
+        case 4: run_k(std::integral_constant<int, 4>{}); break;
+        case 3: run_k(std::integral_constant<int, 3>{}); break;
+        case 2: run_k(std::integral_constant<int, 2>{}); break;
+        case 1: run_k(std::integral_constant<int, 1>{}); break;
+        default: run_k(std::integral_constant<int, 0>{}); break;
+      }
+    } else {
+      run_k(std::integral_constant<int, C::FM>{});
+    }
 
     if (sk_j >= 0) {
       // stream-K piece: store the partial sums in register order (slot
