@@ -283,11 +283,11 @@ def main():
     # down GEMM's epilogue)
     nrs = hdr["remote_segments"]
     seg_rows = int(share.array("seg_rows", nrs).sum()) if nrs else 0
-    # rows the GEMMs run through their MFMAs: the gate/up GEMM's 256-row
-    # tiles over every expert's real rows; the down GEMM's tiles over the
-    # layout rows of every band (padding included)
+    # rows the GEMMs' tiles hold: 256-row tiles over every expert's real
+    # rows (gate/up) and over the real rows of whole bands (down); their
+    # unused rows are not multiplied in the down GEMM, but counted here
     gu_rows = 256 * hdr["gateup_row_tiles"]
-    dn_rows = M
+    dn_rows = 256 * hdr["down_row_tiles"]
     work = algorithmic(cfg, R, M, seg_rows, gu_rows, dn_rows)
 
     # Short kernels: 20 back-to-back launches between two events on the

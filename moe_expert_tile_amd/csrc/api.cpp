@@ -67,20 +67,10 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->tok_off[W] = tok;
   L->NB = blk;
   L->NB_r = L->blk_off[r + 1] - L->blk_off[r];
-  // down GEMM m-tiles: when tb_M divides 256, 256-row tiles of up to
-  // 256 / tb_M row-contiguous bands (a table the planner builds); otherwise
-  // every band is cut into tb_M / bm sub-tiles of the largest power of two
-  // bm dividing tb_M
-  int bm = 256;
-  while (tb_m % bm != 0) bm >>= 1;
-  L->dn_merge = (256 % tb_m == 0) ? 256 / tb_m : 0;
-  if (L->dn_merge > 0) bm = 256;
-  L->dn_bm = bm;
-  L->tb_log2 = 0;
-  while ((1 << L->tb_log2) < tb_m) ++L->tb_log2;
-  L->dn_sub = L->dn_merge > 0 ? 1 : tb_m / bm;
+  // down GEMM: 256-row tiles of whole bands (their real rows packed), one
+  // flag per band and column tile
   L->dn_ntn = d / kDnBN;
-  L->dn_tpb = L->dn_sub * L->dn_ntn;
+  L->dn_tpb = L->dn_ntn;
   L->gu_ntn = f / (kGuBN / 2);
   L->gu_mt_cap = (int)(rows_cap / kGuBM + E_l + 1);
   L->build_stage = 0;  // decided at launch, against the device's LDS limit
@@ -128,15 +118,14 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   // min(G, steps / kMinSkSteps) pieces, two slots each (a piece may close
   // one tile and open the next).
   const int64_t gu_tiles_max = (int64_t)L->gu_mt_cap * L->gu_ntn;
-  const int64_t dn_tiles_max = B * L->dn_sub * L->dn_ntn;
+  const int64_t dn_tiles_max = B * L->dn_ntn;
   auto sk_need = [](int64_t tiles_max, int KT) -> int64_t {
     if (KT < kMinSkKTOneRound || tiles_max <= 0) return 0;
     const int64_t split_max = KT >= kMinSkKT ? 3 * kMaxProducers / 4 : kMaxProducers / 2;
     const int64_t tiles = std::min(tiles_max, split_max);
     return 2 * std::min<int64_t>(kMaxProducers, tiles * KT / kMinSkSteps);
   };
-  const int dn_bk = L->dn_bm == 256 ? kDnBK : (L->dn_bm == 64 ? kDn64BK : kDn32BK);
-  L->sk_slots = (int)std::max(sk_need(gu_tiles_max, d / kGuBK), sk_need(dn_tiles_max, f / dn_bk));
+  L->sk_slots = (int)std::max(sk_need(gu_tiles_max, d / kGuBK), sk_need(dn_tiles_max, f / kDnBK));
   L->o_skc = take(2 * kMaxProducers * 2);
   L->o_skp = take((int64_t)L->sk_slots * 256 * 256);
   L->total_words = off;

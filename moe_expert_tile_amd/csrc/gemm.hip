@@ -288,7 +288,11 @@ __device__ __forceinline__ void issue_operand(lds_void_t* dst, __amdgpu_buffer_r
 template <class C, bool SWIGLU, bool FLAGS>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
 void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
+  // one LDS object: the operand rings, and for the down GEMM two small
+  // epilogue tables past them (a second object made the compiler wait for
+  // every outstanding load at each K step)
+  constexpr int kExtraElems = SWIGLU ? 0 : 2 * (kDnMaxBands + 1 + C::BM);
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS + kExtraElems];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int WAVES_N = C::BN / C::WN;
   const int wave_m = wave / WAVES_N, wave_n = wave % WAVES_N;
@@ -421,27 +425,24 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       decode_tile(t - n_mt_r * n_nt, n_mt - n_mt_r, n_nt, blk_r, blk_c, mt, nt);
       mt += n_mt_r;
     }
-    // row tile: its expert, first row and row limit; for the down GEMM also
-    // the first band and the number of bands whose flags it sets
-    int e, row0, lim, band0 = 0, nbt = 1;
+    // row tile.  gate/up: 256 compacted rows of one expert (row0 their
+    // first, row_end the expert's end).  down: nbt whole bands of one run
+    // from band0 on, whose nrows real rows are consecutive compacted rows of
+    // h from crow0 on; row0 is the layout row of the first band (the run's
+    // bands follow one another in the layout, tb_M rows apart)
+    int e, row0, lim, band0 = 0, nbt = 1, crow0 = 0, nrows = 0;
     if constexpr (SWIGLU) {
-      // gate/up tiles run over compacted rows (the layout without padding)
       row0 = g.ws[L.o_gumt_row + mt];
       e = g.ws[L.o_gumt_exp + mt];
       lim = g.ws[L.o_crowoff + e + 1];
-    } else if (L.dn_merge > 0) {
-      // up to dn_merge row-contiguous bands of one expert
+    } else {
       row0 = g.ws[L.o_dnt_row + mt];
       e = g.ws[L.o_dnt_exp + mt];
       band0 = g.ws[L.o_dnt_band + mt];
       nbt = g.ws[L.o_dnt_nb + mt];
-      lim = min(rowoff[e + 1], row0 + nbt * L.tb_m);
-    } else {
-      // sub-tile mt % dn_sub of band mt / dn_sub
-      const int band = mt / L.dn_sub;
-      e = g.ws[L.o_bexp + band];
-      row0 = g.ws[L.o_bsrc + band] + (mt - band * L.dn_sub) * C::BM;
-      lim = rowoff[e + 1];
+      crow0 = g.ws[L.o_bcrow + band0];
+      nrows = g.ws[L.o_bcrow + band0 + nbt - 1] + g.ws[L.o_bval + band0 + nbt - 1] - crow0;
+      lim = row0 + nrows;
     }
     // per-tile values are wave-uniform; say so, so that the buffer
     // descriptors built from them live in scalar registers
@@ -449,19 +450,19 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     row0 = __builtin_amdgcn_readfirstlane(row0);
     band0 = __builtin_amdgcn_readfirstlane(band0);
     nbt = __builtin_amdgcn_readfirstlane(nbt);
+    crow0 = __builtin_amdgcn_readfirstlane(crow0);
+    nrows = __builtin_amdgcn_readfirstlane(nrows);
     const int row_end = __builtin_amdgcn_readfirstlane(lim);
     // local bands (destination r) never leave the rank: the epilogue also
     // writes their rows into r's own receive buffer at the combine plan's
-    // destination rows, so the consumer moves only remote segments
+    // destination rows, so the consumer moves only remote segments.  A run,
+    // so a tile, is all remote or all local; a local run's bands are
+    // consecutive rows of the unpadded local group, at both ends.
     int ldst0 = -1;
     if constexpr (FLAGS) {
-      const int bfirst = L.dn_merge > 0 ? band0 : mt / L.dn_sub;
-      if (g.ws[L.o_bdst + bfirst] == L.r)
-        ldst0 = g.ws[L.o_bdoff + bfirst] + (L.dn_merge > 0 ? 0 : (mt - bfirst * L.dn_sub) * C::BM);
+      if (g.ws[L.o_bdst + band0] == L.r) ldst0 = g.ws[L.o_bdoff + band0];
       ldst0 = __builtin_amdgcn_readfirstlane(ldst0);
     }
-    // a sub-tile of a partial (local tail) band can start past the expert's
-    // last row: nothing to compute or store, only its flag to publish
     const bool empty = row0 >= row_end;
     // A operand.  Every load is bounded by a buffer descriptor, and a lane
     // whose row holds no data gets an offset past the bound (2^31 > the
@@ -470,10 +471,8 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     //    gives its row of x_recv (gathered) or of the layout X.  Rows of one
     //    tile lie within one X_e, so their layout rows span at most
     //    256 + (W-1)(tb_M-1) rows: 32-bit offsets from the first suffice.
-    //  * down: A is h in compacted order.  The tile's real rows are the
-    //    first `valid` rows of each of its bands, and those are consecutive
-    //    compacted rows from band_crow of its first band; padding rows read
-    //    zeros, so their y rows come out exactly zero.
+    //  * down: A is h in compacted order: the tile's nrows real rows packed
+    //    from crow0 on; its rows past them read zeros.
     __amdgpu_buffer_rsrc_t a_rsrc;
     uint32_t a_off[C::A_LOADS];
     uint32_t b_off[C::B_LOADS];
@@ -496,36 +495,12 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
                             : 0x80000000u;
       }
     } else {
-      const int32_t* bcrow = g.ws + L.o_bcrow;
-      const int32_t* bval = g.ws + L.o_bval;
-      int crow0, nvalid, sub = 0, band = 0;
-      if (L.dn_merge > 0) {
-        crow0 = bcrow[band0];
-        nvalid = bcrow[band0 + nbt - 1] + bval[band0 + nbt - 1] - crow0;
-      } else {
-        band = mt / L.dn_sub;
-        sub = (mt - band * L.dn_sub) * C::BM;
-        crow0 = bcrow[band] + sub;
-        nvalid = max(0, min(C::BM, bval[band] - sub));
-      }
-      crow0 = __builtin_amdgcn_readfirstlane(crow0);
-      nvalid = __builtin_amdgcn_readfirstlane(nvalid);
-      a_rsrc = make_rsrc(g.a + (int64_t)crow0 * g.K, (int64_t)nvalid * g.K * 2);
+      a_rsrc = make_rsrc(g.a + (int64_t)crow0 * g.K, (int64_t)nrows * g.K * 2);
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i) {
-        int r = (wave + i * C::NW) * C::RPB + ld_row;
-        // recomputed per tile: kept live across the K loop instead, the
-        // per-lane band index and offset spill to scratch
-        asm volatile("" : "+v"(r));
-        int src = -1;
-        if (L.dn_merge > 0) {
-          const int bi = r >> L.tb_log2, j = r & (L.tb_m - 1);
-          if (bi < nbt && j < bval[band0 + bi]) src = bcrow[band0 + bi] + j - crow0;
-        } else if (sub + r < bval[band]) {
-          src = r;
-        }
-        a_off[i] = src >= 0 ? 2u * ((uint32_t)src * (uint32_t)g.K + (uint32_t)(C::swz(r, ld_phys) * 8))
-                            : 0x80000000u;
+        const int r = (wave + i * C::NW) * C::RPB + ld_row;
+        a_off[i] = r < nrows ? 2u * ((uint32_t)r * (uint32_t)g.K + (uint32_t)(C::swz(r, ld_phys) * 8))
+                             : 0x80000000u;
       }
     }
     const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(g.w + (int64_t)e * g.w_rows * g.K, (int64_t)g.w_rows * g.K * 2);
@@ -644,28 +619,16 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
         for (; kt + C::S_SHALLOW - 1 < KTt; ++kt) k_step(kt, T_{}, F_{}, (kt + 1 < KTt) ? C::DEEP_LOADS : 0, fe_tag);
       for (; kt < KTt; ++kt) k_step(kt, F_{}, F_{}, (kt + 1 < KTt) ? C::DEEP_LOADS : 0, fe_tag);
     };
-    if constexpr (!SWIGLU && C::BM == 256 && C::FM == 4) {
-      // Down tiles of 256 rows hold up to 256 / tb_M bands, each of whose
-      // rows past `valid` are padding.  This wave's blocks are rows
-      // [wave_m WM + 32 j, +32), j < FM; it multiplies blocks 0 .. fe - 1,
-      // fe - 1 being its last block with a real row, and every wave still
-      // joins every load and barrier.  The waves of one SIMD hold the two
-      // row halves of the same columns, so the SIMD's MFMA time follows the
-      // tile's real rows (DeepSeek-like layer: 45% of the layout rows are
-      // padding).
-      int fe = 0;
-      if (L.dn_merge > 0) {
-        const int32_t* bval = g.ws + L.o_bval;
-#pragma unroll
-        for (int j = C::FM - 1; j >= 0 && fe == 0; --j) {
-          const int r = wave_m * C::WM + 32 * j;      // first row of the block
-          const int bi = r >> L.tb_log2, q = r & (L.tb_m - 1);
-          if (bi < nbt && q < bval[band0 + bi]) fe = j + 1;
-        }
-      } else {
-        fe = C::FM;
-      }
-      fe = __builtin_amdgcn_readfirstlane(fe);
+    if constexpr (!SWIGLU) {
+      // The tile's nrows real rows are packed at its top.  This wave's
+      // blocks are rows [wave_m WM + 32 j, +32), j < FM; it multiplies
+      // blocks 0 .. fe - 1, the last of them holding a real row, and every
+      // wave still joins every load and barrier.  The waves of one SIMD hold
+      // the two row halves of the same columns, so the SIMD's MFMA time
+      // follows the tile's real rows.
+      int fe = (nrows + 31) / 32 - wave_m * C::FM;
+      fe = __builtin_amdgcn_readfirstlane(max(0, min(C::FM, fe)));
+      static_assert(C::FM == 4, "one K-loop body per block count");
       switch (fe) {
         case 4: run_k(std::integral_constant<int, 4>{}); break;
         case 3: run_k(std::integral_constant<int, 3>{}); break;
@@ -820,7 +783,30 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       constexpr int NCH = OUT_TC / 8;   // 16-byte chunks per output row
       static_assert(C::BM * OUT_TC <= C::LDS_ELEMS, "output tile fits the LDS ring");
       static_assert((NCH & (NCH - 1)) == 0 && NCH >= 16, "power-of-two chunk count");
-      __syncthreads();   // every wave is done with the ring
+      // Row map: row m < nrows of the tile is row j of its band bi, which is
+      // layout row row0 + bi * tb_M + j in a remote run (whose bands follow
+      // one another tb_M rows apart) and row0 + m in a local one (its bands
+      // are consecutive rows of the unpadded local group).  boff[bi] is the
+      // first packed row of band bi; both tables sit past the LDS ring.
+      int* boff = (int*)(lds + C::LDS_ELEMS);   // [kDnMaxBands + 1]
+      int* rowmap = boff + kDnMaxBands + 1;     // [BM]
+      if (tid <= nbt) boff[tid] = (tid < nbt ? g.ws[L.o_bcrow + band0 + tid] : crow0 + nrows) - crow0;
+      __syncthreads();   // every wave is done with the ring; boff is complete
+      const bool remote_tile = ldst0 < 0;
+      if (tid < C::BM) {
+        const int m = tid;
+        int dst = -1;
+        if (m < nrows) {
+          if (remote_tile) {
+            int bi = 0;
+            while (boff[bi + 1] <= m) ++bi;
+            dst = bi * L.tb_m + (m - boff[bi]);
+          } else {
+            dst = m;
+          }
+        }
+        rowmap[m] = dst;
+      }
       char* tl = (char*)lds;
 #pragma unroll
       for (int j = 0; j < C::FM; ++j) {
@@ -837,14 +823,16 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
           }
       }
       __syncthreads();
-      // rows [row0, row_end) of this tile exist; the store descriptors end
-      // at row_end, so the rows past it are dropped by the buffer bounds
+      // the stores: the tile's real rows to their layout rows (and, in a
+      // local run, to the rank's own receive buffer), then zeros into the
+      // padding rows of every remote band; the descriptors end past the
+      // last row written
       const int64_t out_row_bytes = (int64_t)g.out_cols * 2;
       const int col0 = nt * OUT_TC;
-      const int nrows = row_end - row0;   // > 0 unless the tile is empty
+      const int span = remote_tile ? nbt * L.tb_m : nrows;   // layout rows from row0
       if (nrows > 0) {
         const __amdgpu_buffer_rsrc_t o_rsrc =
-            make_rsrc(g.out + (int64_t)row0 * g.out_cols + col0, (int64_t)nrows * out_row_bytes);
+            make_rsrc(g.out + (int64_t)row0 * g.out_cols + col0, (int64_t)span * out_row_bytes);
         __amdgpu_buffer_rsrc_t l_rsrc = o_rsrc;
         if (ldst0 >= 0)
           l_rsrc = make_rsrc(recv.p[L.r] + (int64_t)ldst0 * g.out_cols + col0, (int64_t)nrows * out_row_bytes);
@@ -857,17 +845,35 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
         for (int p0 = 0; p0 < PASSES; p0 += UNR) {
           if ((p0 * RPP) >= nrows) break;
           v4u32 v[UNR];
+          int dst[UNR];
 #pragma unroll
           for (int u = 0; u < UNR; ++u) {
             const int m = (p0 + u) * RPP + r_in;
             v[u] = *(const v4u32*)(tl + m * (OUT_TC * 2) + 16 * (ch ^ (m & (NCH - 1))));
+            dst[u] = rowmap[m];
           }
 #pragma unroll
           for (int u = 0; u < UNR; ++u) {
             const int m = (p0 + u) * RPP + r_in;
-            const uint32_t off = (uint32_t)((int64_t)m * out_row_bytes + ch * 16);
+            const uint32_t off = dst[u] >= 0 ? (uint32_t)((int64_t)dst[u] * out_row_bytes + ch * 16) : 0xFFFFFFF0u;
             __builtin_amdgcn_raw_buffer_store_b128(v[u], o_rsrc, off, 0, MOE_STORE_AUX);
-            if (ldst0 >= 0) __builtin_amdgcn_raw_buffer_store_b128(v[u], l_rsrc, off, 0, MOE_STORE_AUX);
+            if (ldst0 >= 0) {
+              const uint32_t loff = m < nrows ? (uint32_t)((int64_t)m * out_row_bytes + ch * 16) : 0xFFFFFFF0u;
+              __builtin_amdgcn_raw_buffer_store_b128(v[u], l_rsrc, loff, 0, MOE_STORE_AUX);
+            }
+          }
+        }
+        if (remote_tile) {
+          // padding rows of the tile's bands: [valid, tb_M) of each
+          const v4u32 z = {0u, 0u, 0u, 0u};
+          for (int bi = 0; bi < nbt; ++bi) {
+            const int v = boff[bi + 1] - boff[bi];
+            const int npad = L.tb_m - v;
+            for (int idx = tid; idx < npad * NCH; idx += C::NT) {
+              const int row = bi * L.tb_m + v + idx / NCH;
+              __builtin_amdgcn_raw_buffer_store_b128(z, o_rsrc, (uint32_t)((int64_t)row * out_row_bytes + (idx % NCH) * 16),
+                                                     0, MOE_STORE_AUX);
+            }
           }
         }
       }
@@ -889,17 +895,11 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       wait_vm0();
       if constexpr (FLAGS) {
         __syncthreads();
-        if (tid == 0) {
-          if (L.dn_merge > 0) {
-            // one flag per covered band (a band has n_nt flags, one per column tile)
-            for (int b = 0; b < nbt; ++b)
-              __hip_atomic_store(g.flags + (int64_t)(band0 + b) * n_nt + nt, g.epoch, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-          } else {
-            __hip_atomic_store(g.flags + (int64_t)mt * n_nt + nt, g.epoch, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
+        // one flag per band of the tile (a band has n_nt flags, one per
+        // column tile)
+        if (tid < nbt)
+          __hip_atomic_store(g.flags + (int64_t)(band0 + tid) * n_nt + nt, g.epoch, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -932,14 +932,7 @@ using GuCfg = Cfg<256, 256, MOE_GU_WAVES_M, MOE_GU_WAVES_N, MOE_GU_BK, MOE_GU_SA
 static_assert(GuCfg::BK == kGuBK, "the host sizes the stream-K scratch with this K step");
 using Dn256 = Cfg<256, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_DN_BK, MOE_DN_SA, MOE_DN_SB>;
 static_assert(Dn256::BK == kDnBK, "the host sizes the stream-K scratch with this K step");
-// Down tiles of 64 and 32 rows, for band heights that do not divide 256 (a
-// band is cut into tb_M / 64 or tb_M / 32 row tiles).  The 64-row tile's
-// ~61 KB of LDS lets two workgroups
-// share a CU, so in the overlapped launch a consumer workgroup may share its
-// CU with a producer; the whole grid is resident at once either way, so no
-// workgroup waits for a slot held by one that waits for it.
-using Dn64 = Cfg<64, 256, 1, 4, kDn64BK, 3, 3>;
-using Dn32 = Cfg<32, 256, 1, 4, kDn32BK, 3, 3>;
+static_assert(Dn256::BM == kDnBM, "the planner packs bands into tiles of this height");
 
 __global__ __launch_bounds__(256) void clear_counters_kernel(uint64_t* ctr, int n, int32_t* claim) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) ctr[i] = 0;
@@ -966,20 +959,7 @@ hipError_t launch_down(const PlanLayout& L, int32_t* ws, const Scratch& sc, cons
                        uint16_t* y, uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks,
                        int n_prod, int grid, hipStream_t s) {
   GemmArgs a{ws, h, wd, y, flags, epoch, L.f, L.d, L.d, 0, n_prod, timeout_ticks, nullptr, 0, 0, sc};
-  switch (L.dn_bm) {
-    case 256:
-      hipLaunchKernelGGL((grouped_gemm_kernel<Dn256, false, true>), dim3(grid), dim3(Dn256::NT), 0, s, L, a, recv);
-      break;
-    case 64:
-      hipLaunchKernelGGL((grouped_gemm_kernel<Dn64, false, true>), dim3(grid), dim3(Dn64::NT), 0, s, L, a, recv);
-      break;
-    case 32:
-      hipLaunchKernelGGL((grouped_gemm_kernel<Dn32, false, true>), dim3(grid), dim3(Dn32::NT), 0, s, L, a, recv);
-      break;
-    default:
-      // make_layout never picks another height: 128 divides 256 and takes the 256-row path
-      return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL((grouped_gemm_kernel<Dn256, false, true>), dim3(grid), dim3(Dn256::NT), 0, s, L, a, recv);
   return hipGetLastError();
 }
 

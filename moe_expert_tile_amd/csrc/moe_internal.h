@@ -17,20 +17,22 @@ constexpr int kCopyChunk = 32768;      // bytes per consumer copy unit
 constexpr int kGuBM = 256;             // gate/up GEMM tile rows
 constexpr int kGuBN = 256;             // gate/up GEMM tile cols (128 gate + 128 up)
 constexpr int kDnBN = 256;             // down GEMM tile cols
+constexpr int kDnBM = 256;             // down GEMM tile rows: whole bands of one run, their real rows packed
+constexpr int kDnMaxBands = 64;        // bands packed into one down tile at most
 // K steps of the GEMM configurations (gemm.hip asserts them); the host sizes
 // the stream-K scratch with them
 constexpr int kGuBK = 64;              // gate/up
-constexpr int kDnBK = 64;              // down, 256-row tiles
-constexpr int kDn64BK = 32;            // down, 64-row tiles (tb_M a multiple of 64, not dividing 256)
-constexpr int kDn32BK = 64;            // down, 32-row tiles
+constexpr int kDnBK = 64;              // down
 constexpr int kMaxProducers = 256;     // persistent GEMM workgroups at most (one per CU on MI355X)
 constexpr int kMinSkSteps = 16;        // shortest K range of a stream-K piece
 // stream-K for a tail round only with tiles of at least this many K steps.
-// Measured: with 24-112 steps behind full rounds (the Qwen3- and
-// DeepSeek-like GEMMs) the partials' round trip through memory, limited by
-// each CU's ~35 GB/s load pipeline like the tiles themselves, costs as much
-// as the tail round it removes or more (Qwen3-like gate/up +1-2%, down +8%).
-constexpr int kMinSkKT = 128;
+// Measured with the gate/up GEMM over compacted rows (same box, serial mode,
+// threshold 128 -> 64): DeepSeek-like gate/up (112 steps, a tail round 19%
+// full) 2485 -> 2392 us, Qwen3-like gate/up (64 steps, 33% full) 450 ->
+// 432 us, Mixtral-like unchanged.  The short-K down GEMMs (24 and 32 steps)
+// stay below it: there the partials' round trip costs as much as the tail
+// round it removes.
+constexpr int kMinSkKT = 64;
 // ... but a GEMM whose tiles fill at most half of one round is split along
 // K from 2 * kMinSkSteps steps on, so that each tile gets pieces of at most
 // half its steps (decode's 120 gate/up tiles of 32 steps on 256 CUs:
@@ -60,9 +62,7 @@ enum Hdr {
 struct PlanLayout {
   int W, r, E_l, E, k, d, f, tb_m, mgb;
   int R, rows_cap, bands_cap, T_r, NB, NB_r, gu_mt_cap;
-  int dn_bm, dn_sub, dn_ntn, dn_tpb;   // down GEMM: tile rows, tiles per band row, n tiles, tiles per band
-  int dn_merge;                        // > 0: down m-tiles of up to dn_merge row-contiguous bands (table)
-  int tb_log2;                         // log2(tb_m) when dn_merge > 0 (tb_m then divides 256)
+  int dn_ntn, dn_tpb;                  // down GEMM: column tiles, flags per band (= column tiles)
   int gu_ntn;                          // gate/up GEMM n tiles (f / 128)
   int build_stage;                     // plan_build copies the block histograms into LDS
   int band_table;                      // plan_build's band -> group table in LDS (bands_cap, or 0)

@@ -487,52 +487,72 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     mt_exp[t] = e;
   }
 
-  // (j) down m-tiles, when tb_M divides 256: the runs of row-contiguous
-  //     bands in S order -- the remote bands of each expert (its remote
-  //     groups follow one another at the start of X_e), then the local bands
-  //     of each expert -- cut into tiles of at most dn_merge bands; one
-  //     thread per tile
-  int NDT = B * L.dn_sub;
-  int ndt_r = n_remote * L.dn_sub;
-  if (L.dn_merge > 0) {
-    const int P = L.dn_merge;
-    int32_t* dt_row = ws + L.o_dnt_row;
-    int32_t* dt_exp = ws + L.o_dnt_exp;
-    int32_t* dt_band = ws + L.o_dnt_band;
-    int32_t* dt_nb = ws + L.o_dnt_nb;
-    auto run_of = [&](int q, int& e, int& first, int& nb, int& row0) {
-      if (q < E_l) {
-        e = order[q];
-        first = gstart[q * (W - 1)];   // with W == 1 there are no remote bands
-        nb = rb[e];
-        row0 = rowoff[e];
+  // (j) down tiles: the runs of row-contiguous bands in S order -- the
+  //     remote bands of each expert in rule (ii) order (its remote groups
+  //     follow one another at the start of X_e), then the local bands of
+  //     each expert -- each cut greedily into tiles of whole bands whose
+  //     real rows add up to at most kDnBM (and at most kDnMaxBands bands).
+  //     The GEMM multiplies a tile's real rows only, packed, so a tile of
+  //     two half-empty bands costs one band's work.  One thread per run:
+  //     count, scan, then write.
+  int32_t* dt_row = ws + L.o_dnt_row;
+  int32_t* dt_exp = ws + L.o_dnt_exp;
+  int32_t* dt_band = ws + L.o_dnt_band;
+  int32_t* dt_nb = ws + L.o_dnt_nb;
+  // greedy packing of run q; with `at` >= 0 the tiles are written from
+  // index `at` on; returns the number of tiles
+  auto pack_run = [&](int q, int at) {
+    const bool remote_run = q < E_l;
+    const int e = remote_run ? order[q] : q - E_l;
+    int b = remote_run ? (W > 1 ? gstart[q * (W - 1)] : 0) : gstart[NGR + e];
+    int ntiles = 0, rows = 0, nbt = 0, tfirst = b, trow = 0;
+    for (int qq = 0; qq < W; ++qq) {
+      int o;
+      if (remote_run) {
+        if (qq >= W - 1) break;
+        o = qq < r ? qq : qq + 1;
       } else {
-        e = q - E_l;
-        first = gstart[NGR + e];
-        nb = (c[e * W + r] + tb - 1) / tb;
-        row0 = rowoff[e] + grp[e * W + r];
+        if (qq > 0) break;
+        o = r;
       }
-    };
-    NDT = scan_items(
-        2 * E_l,
-        [&](int q) {
-          int e, first, nb, row0;
-          run_of(q, e, first, nb, row0);
-          return (nb + P - 1) / P;
-        },
-        [&](int q, int pre) { dnpre[q] = pre; }, sh);
-    ndt_r = dnpre[E_l];   // the remote runs come first
-    for (int t = tid; t < NDT; t += nt) {
-      const int q = upper_index(dnpre, 2 * E_l, t);
-      int e, first, nb, row0;
-      run_of(q, e, first, nb, row0);
-      const int j = t - dnpre[q];
-      dt_row[t] = row0 + j * P * tb;
-      dt_exp[t] = e;
-      dt_band[t] = first + j * P;
-      dt_nb[t] = min(P, nb - j * P);
+      const int n = c[e * W + o];
+      const int row_g = rowoff[e] + grp[e * W + o];
+      for (int j = 0; j * tb < n; ++j, ++b) {
+        const int v = min(tb, n - j * tb);
+        if (nbt > 0 && (rows + v > kDnBM || nbt == kDnMaxBands)) {
+          if (at >= 0) {
+            dt_row[at + ntiles] = trow;
+            dt_exp[at + ntiles] = e;
+            dt_band[at + ntiles] = tfirst;
+            dt_nb[at + ntiles] = nbt;
+          }
+          ++ntiles;
+          rows = 0;
+          nbt = 0;
+        }
+        if (nbt == 0) {
+          tfirst = b;
+          trow = row_g + j * tb;
+        }
+        rows += v;
+        ++nbt;
+      }
     }
-  }
+    if (nbt > 0) {
+      if (at >= 0) {
+        dt_row[at + ntiles] = trow;
+        dt_exp[at + ntiles] = e;
+        dt_band[at + ntiles] = tfirst;
+        dt_nb[at + ntiles] = nbt;
+      }
+      ++ntiles;
+    }
+    return ntiles;
+  };
+  const int NDT = scan_items(
+      2 * E_l, [&](int q) { return pack_run(q, -1); }, [&](int q, int pre) { dnpre[q] = pre; }, sh);
+  const int ndt_r = dnpre[E_l];   // the remote runs come first
+  for (int q = tid; q < 2 * E_l; q += nt) (void)pack_run(q, dnpre[q]);
 
   // results used by later kernels and by inspection
   for (int i = tid; i < EW; i += nt) {
@@ -683,25 +703,56 @@ __global__ __launch_bounds__(kPlanThreads) void plan_place_kernel(PlanLayout L, 
   }
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end read
+// zero, stores past it are dropped (gfx9-family word 3: 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef unsigned int gv4u32 __attribute__((ext_vector_type(4)));
+
+#ifndef MOE_GATHER_STORE_AUX
+#define MOE_GATHER_STORE_AUX 0   // cache-policy bits of the layout stores
+#endif
+
+// One wavefront per layout row: a real row is copied from x_recv with
+// kGatherBatch 16-byte loads per lane in flight before their stores; a
+// padding row is written as zeros.  Both ends are bounded by per-row buffer
+// descriptors, so a row length that is not a multiple of the batch needs
+// no branch.
+constexpr int kGatherBatch = 8;
+
 __global__ __launch_bounds__(256) void plan_gather_kernel(PlanLayout L, const int32_t* __restrict__ ws,
-                                                         const uint4* __restrict__ x_recv,
-                                                         uint4* __restrict__ x_layout) {
+                                                         const uint16_t* __restrict__ x_recv,
+                                                         uint16_t* __restrict__ x_layout) {
   const int32_t* hdr = ws + L.o_hdr;
   if (hdr[H_ERROR] != 0) return;
   const int M = hdr[H_M];
   const int32_t* src = ws + L.o_src;
   const int lane = threadIdx.x & 63;
   const int wpb = blockDim.x >> 6;
-  const int64_t vec = L.d / 8;  // 16-byte vectors per row
+  const int64_t row_bytes = (int64_t)L.d * 2;
   for (int row = blockIdx.x * wpb + (threadIdx.x >> 6); row < M; row += gridDim.x * wpb) {
     const int s = src[row];
-    uint4* dst = x_layout + (int64_t)row * vec;
+    const __amdgpu_buffer_rsrc_t dst = row_rsrc(x_layout + (int64_t)row * L.d, row_bytes);
     if (s >= 0) {
-      const uint4* sp = x_recv + (int64_t)s * vec;
-      for (int64_t v = lane; v < vec; v += 64) dst[v] = sp[v];
+      const __amdgpu_buffer_rsrc_t sp = row_rsrc(x_recv + (int64_t)s * L.d, row_bytes);
+      for (int b0 = 0; b0 < row_bytes; b0 += kGatherBatch * 64 * 16) {
+        gv4u32 v[kGatherBatch];
+#pragma unroll
+        for (int u = 0; u < kGatherBatch; ++u)
+          v[u] = __builtin_amdgcn_raw_buffer_load_b128(sp, b0 + (u * 64 + lane) * 16, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kGatherBatch; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(v[u], dst, b0 + (u * 64 + lane) * 16, 0, MOE_GATHER_STORE_AUX);
+      }
     } else {
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      for (int64_t v = lane; v < vec; v += 64) dst[v] = z;
+      const gv4u32 z = {0u, 0u, 0u, 0u};
+      for (int b0 = 0; b0 < row_bytes; b0 += kGatherBatch * 64 * 16) {
+#pragma unroll
+        for (int u = 0; u < kGatherBatch; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(z, dst, b0 + (u * 64 + lane) * 16, 0, MOE_GATHER_STORE_AUX);
+      }
     }
   }
 }
@@ -726,8 +777,7 @@ hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t*
   int grid = (L.rows_cap + rows_per_block - 1) / rows_per_block;
   if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(plan_gather_kernel, dim3(grid), dim3(256), 0, s, L, (const int32_t*)ws,
-                     (const uint4*)x_recv, (uint4*)x_layout);
+  hipLaunchKernelGGL(plan_gather_kernel, dim3(grid), dim3(256), 0, s, L, (const int32_t*)ws, x_recv, x_layout);
   return hipGetLastError();
 }
 

@@ -81,8 +81,8 @@ def expected_tiles(pl):
     """GEMM row tiles implied by the oracle plan: gate/up tiles cut the real
     rows of every X_e (its compacted rows, experts in rule (ii) order) into
     256-row pieces; down tiles cut each maximal run of bands in S order with
-    one expert and one side (remote or local) into pieces of at most
-    256 / tb_M bands."""
+    one expert and one side (remote or local) greedily into tiles of whole
+    bands whose real rows add up to at most 256 (at most 64 bands)."""
     gu_row, gu_exp = [], []
     crow_off = expected_compacted(pl)["crow_off"]
     for e in pl.expert_order:
@@ -90,7 +90,6 @@ def expected_tiles(pl):
         for i in range(-(-n // 256)):
             gu_row.append(int(crow_off[e]) + 256 * i)
             gu_exp.append(int(e))
-    P = 256 // pl.tb_m
     b = pl.bands
     dn = []
     s0 = 0
@@ -99,8 +98,15 @@ def expected_tiles(pl):
         while (s1 + 1 < pl.n_bands and b["expert"][s1 + 1] == b["expert"][s0]
                and b["remote"][s1 + 1] == b["remote"][s0]):
             s1 += 1
-        for f0 in range(s0, s1 + 1, P):
-            dn.append((int(b["src_row"][f0]), int(b["expert"][f0]), f0, min(P, s1 + 1 - f0)))
+        # greedy: whole bands while their real rows fit 256 (at most 64 bands)
+        f0, rows = s0, 0
+        for s in range(s0, s1 + 1):
+            v = int(b["valid"][s])
+            if s > f0 and (rows + v > 256 or s - f0 == 64):
+                dn.append((int(b["src_row"][f0]), int(b["expert"][f0]), f0, s - f0))
+                f0, rows = s, 0
+            rows += v
+        dn.append((int(b["src_row"][f0]), int(b["expert"][f0]), f0, s1 + 1 - f0))
         s0 = s1 + 1
     return gu_row, gu_exp, dn
 
@@ -111,7 +117,6 @@ def test_gemm_tile_tables(name):
     implies, and every down tile's bands are consecutive rows of one expert."""
     c, share = run_plan(name, 1)
     pl = c["plan"]
-    assert 256 % pl.tb_m == 0
     hdr = share.header()
     gu_row, gu_exp, dn = expected_tiles(pl)
     assert hdr["gateup_row_tiles"] == len(gu_row)
