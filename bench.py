@@ -45,6 +45,11 @@ def parse():
     ap.add_argument("--consumer-cus", type=int, default=16)
     ap.add_argument("--mgb", type=int, default=None,
                     help="segment merge factor (bands per middle segment); default: the workload's (1)")
+    ap.add_argument("--link-gbps", type=float, default=0.0,
+                    help="emulated link per destination rank for the consumer's copies, GB/s (0: memory speed; "
+                         "one xGMI link is ~153)")
+    ap.add_argument("--signal", default="tile", choices=["tile", "group"],
+                    help="per-band tile flags, or one ready counter per (expert, destination) group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gathered", action="store_true",
                     help="skip the gathered-rows variant (profiling runs that count one kind of gate/up launch)")
@@ -225,6 +230,9 @@ def main():
     for o in range(cfg.W):
         share.recv[o].copy_(dev_bf16(synth.foreign_rows(cfg, o), torch))
     mode = m.MODE_OVERLAP if args.mode == "overlap" else m.MODE_SERIAL
+    link_mbps = int(round(args.link_gbps * 1000))
+    signal = m.SIGNAL_GROUP if args.signal == "group" else m.SIGNAL_TILE
+    cx = dict(link_mbps=link_mbps, signal=signal)   # how the consumer waits and copies
     stream = torch.cuda.current_stream()
 
     n_ev = args.steps
@@ -239,7 +247,7 @@ def main():
         if i is not None:
             ev_plan[i][1].record(stream)
         share.combine(wgu_d, wd_d, mode=mode, consumer_cus=args.consumer_cus,
-                      events=ev_comb[i] if i is not None else None)
+                      events=ev_comb[i] if i is not None else None, **cx)
         if i is not None:
             ev_scale[i][0].record(stream)
         share.scale(w_r)
@@ -296,7 +304,7 @@ def main():
     # queued all 20 launches before the first one starts: the interval is the
     # GPU's back-to-back time, not the host's launch rate.
     def amortized(fn, n=20):
-        share.combine(wgu_d, wd_d, mode=m.MODE_SERIAL)
+        share.combine(wgu_d, wd_d, mode=m.MODE_SERIAL, **cx)
         e0, e1 = m.timing_events(2)
         e0.record(stream)
         for _ in range(n):
@@ -308,13 +316,14 @@ def main():
     t_plan_k = amortized(lambda: share.plan(ids_d, xr_d))
     t_scale_k = amortized(lambda: share.scale(w_r))
     # standalone consumer: flags already equal the last epoch, all CUs
-    t_copy = amortized(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch))
+    t_copy = amortized(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch, **cx))
     # the per-row ablation of the copy (every remote row routed and copied
     # on its own, as without the owner-aligned layout), all CUs
-    t_rows = amortized(lambda: share.combine(None, None, mode=m.MODE_COPY_ROWS, epoch=share.epoch))
+    t_rows = amortized(lambda: share.combine(None, None, mode=m.MODE_COPY_ROWS, epoch=share.epoch)) \
+        if signal == m.SIGNAL_TILE else None
     # ... and with only the consumer's CU budget of workgroups
     t_copy_budget = amortized(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch,
-                                                    consumer_blocks=args.consumer_cus))
+                                                    consumer_blocks=args.consumer_cus, **cx))
 
     # The same kernels with a cold Infinity Cache: each launch follows a read
     # of a 1 GiB buffer (4x the 256 MB cache; a read leaves no dirty lines to
@@ -334,8 +343,9 @@ def main():
 
     t_plan_cold = amortized_cold(lambda: share.plan(ids_d, xr_d))
     t_scale_cold = amortized_cold(lambda: share.scale(w_r))
-    t_copy_cold = amortized_cold(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch))
-    t_rows_cold = amortized_cold(lambda: share.combine(None, None, mode=m.MODE_COPY_ROWS, epoch=share.epoch))
+    t_copy_cold = amortized_cold(lambda: share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch, **cx))
+    t_rows_cold = amortized_cold(lambda: share.combine(None, None, mode=m.MODE_COPY_ROWS, epoch=share.epoch)) \
+        if signal == m.SIGNAL_TILE else None
     # context for the copy: the runtime's own device-to-device copy of as
     # many bytes as the consumer reads (and writes), timed the same way
     half = int(work["combine_bytes"]) // 2
@@ -359,7 +369,7 @@ def main():
         tails = []
         for _ in range(5):
             share.plan(ids_d, xr_d)
-            share.combine(wgu_d, wd_d, mode=mode, consumer_cus=args.consumer_cus)
+            share.combine(wgu_d, wd_d, mode=mode, consumer_cus=args.consumer_cus, **cx)
             torch.cuda.synchronize()
             end_prod, end_cons = share.end_stamps()
             tails.append(max(0, end_cons - end_prod) * 1e-8)
@@ -367,13 +377,13 @@ def main():
     n_serial = 10
     for _ in range(3):
         share.plan(ids_d, xr_d)
-        share.combine(wgu_d, wd_d, mode=m.MODE_SERIAL)
+        share.combine(wgu_d, wd_d, mode=m.MODE_SERIAL, **cx)
         share.scale(w_r)
     torch.cuda.synchronize()
     t0s = time.perf_counter()
     for _ in range(n_serial):
         share.plan(ids_d, xr_d)
-        share.combine(wgu_d, wd_d, mode=m.MODE_SERIAL)
+        share.combine(wgu_d, wd_d, mode=m.MODE_SERIAL, **cx)
         share.scale(w_r)
     torch.cuda.synchronize()
     ms_serial = (time.perf_counter() - t0s) / n_serial * 1e3
@@ -383,7 +393,7 @@ def main():
     # so the layout X is never materialized (no gather kernel, no pad fill).
     def step_gathered():
         share.plan(ids_d, xr_d, materialize=False)
-        share.combine(wgu_d, wd_d, mode=mode, consumer_cus=args.consumer_cus, x_recv=xr_d)
+        share.combine(wgu_d, wd_d, mode=mode, consumer_cus=args.consumer_cus, x_recv=xr_d, **cx)
         share.scale(w_r)
 
     ms_gathered = t_plan_meta = None
@@ -421,7 +431,8 @@ def main():
             "workload": f"{args.workload}: rank {cfg.rank} share of W={cfg.W} ranks, E={cfg.E} experts "
                         f"({cfg.E_l} local), {cfg.tokens[0]} tokens per owner, d={cfg.d}, f={cfg.f} SwiGLU, "
                         f"top-{cfg.k}, tb_M={cfg.tb_m}, mgb={cfg.mgb}",
-            "mode": args.mode, "consumer_cus": args.consumer_cus, "N": cfg.N, "W": cfg.W, "R": R, "M": M,
+            "mode": args.mode, "consumer_cus": args.consumer_cus, "link_gbps": args.link_gbps or None,
+            "signal": args.signal, "N": cfg.N, "W": cfg.W, "R": R, "M": M,
             "padding_pct": round(100.0 * (M - R) / max(M, 1), 2),
         },
         "roofline": {
@@ -438,8 +449,8 @@ def main():
             "consumer_standalone_back_to_back": round(t_copy * 1e6, 2),
             "consumer_standalone_at_budget": round(t_copy_budget * 1e6, 2),
             "consumer_standalone_cold_cache": round(t_copy_cold * 1e6, 2),
-            "consumer_per_row_back_to_back": round(t_rows * 1e6, 2),
-            "consumer_per_row_cold_cache": round(t_rows_cold * 1e6, 2),
+            "consumer_per_row_back_to_back": round(t_rows * 1e6, 2) if t_rows else None,
+            "consumer_per_row_cold_cache": round(t_rows_cold * 1e6, 2) if t_rows_cold else None,
             "device_copy_same_bytes_cold_cache": round(t_dev_copy_cold * 1e6, 2) if t_dev_copy_cold else None,
             "scale_cold_cache": round(t_scale_cold * 1e6, 2),
             "plan_cold_cache": round(t_plan_cold * 1e6, 2),

@@ -134,7 +134,12 @@ typedef struct moe_combine_opts {
   int32_t consumer_blocks;  /* workgroups of the consumer; 0 = consumer_cus (OVERLAP: at most
                                consumer_cus, MOE_EINVAL above) or one per 32 KiB copy unit,
                                bounded on the host (SERIAL, COPY_ONLY) */
-  int32_t reserved;
+  int32_t link_mbps;        /* 0: the consumer copies at memory speed.  > 0 (1000 at least): an
+                               emulated link per destination rank in MB/s (an xGMI link is ~153000):
+                               each copy unit to owner o also occupies owner o's link for
+                               bytes / rate, reserved in order on the device clock, and the copying
+                               workgroup waits until that transfer would have ended (COPY_ROWS
+                               ignores it) */
   int64_t spin_timeout_ns;  /* bound on the consumer's wait for one segment's flags; 0 = 2 s */
   void* events[6];          /* optional hipEvent_t, recorded on `stream`: [0]/[1] around the gate/up GEMM,
                                [2]/[3] around the down GEMM, [4]/[5] around the consumer (in OVERLAP both
@@ -144,7 +149,18 @@ typedef struct moe_combine_opts {
                                moe_plan) and padding rows as zeros, so X is never materialized; requires
                                R*d*2 < 2^31 bytes; may be NULL when R = 0.  Ignored when x_layout is
                                given. */
+  int32_t signal;           /* how the down GEMM tells the consumer that rows are ready:
+                               MOE_SIGNAL_TILE (0): a flag per band and column tile, set to `epoch`
+                               by the tile that computed it (the consumer polls every flag of a
+                               segment); MOE_SIGNAL_GROUP (1): one ready counter per (expert,
+                               destination) group, raised by every tile by its bands of the group
+                               and tagged with `epoch` (the consumer polls one word per segment; a
+                               segment waits for its whole group).  COPY_ONLY must use the mode
+                               the compute call used; COPY_ROWS needs MOE_SIGNAL_TILE */
+  int32_t pad;              /* zero */
 } moe_combine_opts;
+
+enum { MOE_SIGNAL_TILE = 0, MOE_SIGNAL_GROUP = 1 };
 
 /* Text of a status code. */
 const char* moe_status_string(int status);
@@ -227,7 +243,7 @@ int moe_expert_combine(const moe_shape* shape, const void* plan_ws, const uint16
  * errors as moe_expert_combine, and it allocates nothing: the scratch of its
  * kernels (the fp32 partial sums of the GEMMs' K-split tails, their tile
  * counters, the copy-claim counters of the overlapped launch) is a static
- * device array of 64 MiB + 8 KiB that every GPU the library runs on holds
+ * device array of 64 MiB + 13 KiB that every GPU the library runs on holds
  * until the process ends; its device address is looked up once per device.
  * So the plan workspace only needs the first moe_plan_view.sk_counters
  * bytes of plan_bytes (the K-split part at its end is not used).

@@ -22,6 +22,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so"
 
 MOE_OK, MOE_EINVAL, MOE_ECAPACITY, MOE_EHIP, MOE_ETIMEOUT, MOE_EROUTING, MOE_EUNSUPPORTED = range(7)
 MODE_OVERLAP, MODE_SERIAL, MODE_COPY_ONLY, MODE_COPY_ROWS = 0, 1, 2, 3
+SIGNAL_TILE, SIGNAL_GROUP = 0, 1
 
 HDR_FIELDS = ["error", "M", "bands", "remote_bands", "segments", "remote_segments",
               "gateup_tiles", "down_tiles", "copy_units", "received_rows", "gateup_row_tiles",
@@ -57,9 +58,9 @@ class moe_plan_view(ctypes.Structure):
 
 class moe_combine_opts(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("consumer_cus", ctypes.c_int32),
-                ("consumer_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("consumer_blocks", ctypes.c_int32), ("link_mbps", ctypes.c_int32),
                 ("spin_timeout_ns", ctypes.c_int64), ("events", ctypes.c_void_p * 6),
-                ("x_recv", ctypes.c_void_p)]
+                ("x_recv", ctypes.c_void_p), ("signal", ctypes.c_int32), ("pad", ctypes.c_int32)]
 
 
 class MoEError(RuntimeError):
@@ -166,7 +167,7 @@ def moe_expert_combine(shape: Shape, plan_ws, x_layout, w_gate_up, w_down, h, y,
                        recv: List, mode: int = MODE_OVERLAP, consumer_cus: int = 0,
                        consumer_blocks: int = 0, spin_timeout_ns: int = 0,
                        events: Optional[Sequence] = None, stream=None, x_recv=None,
-                       noalloc: bool = False) -> None:
+                       noalloc: bool = False, link_mbps: int = 0, signal: int = SIGNAL_TILE) -> None:
     """x_layout=None with x_recv given: the gate/up GEMM gathers its rows from
     x_recv through the plan's src_index (the layout is never materialized).
     noalloc=True calls moe_expert_combine_noalloc (kernel scratch in the
@@ -180,6 +181,8 @@ def moe_expert_combine(shape: Shape, plan_ws, x_layout, w_gate_up, w_down, h, y,
     opts.consumer_blocks = consumer_blocks
     opts.spin_timeout_ns = spin_timeout_ns
     opts.x_recv = _ptr(x_recv)
+    opts.link_mbps = int(link_mbps)
+    opts.signal = int(signal)
     if events is not None:
         for i, ev in enumerate(events):
             opts.events[i] = None if ev is None else int(ev.cuda_event)
@@ -238,7 +241,8 @@ class RankShare:
         moe_plan(self.shape, topk_ids, x_recv, self.plan_ws, self.x_layout if materialize else None, stream)
 
     def combine(self, w_gate_up, w_down, mode=MODE_OVERLAP, consumer_cus=0, consumer_blocks=0,
-                spin_timeout_ns=0, events=None, stream=None, epoch=None, x_recv=None):
+                spin_timeout_ns=0, events=None, stream=None, epoch=None, x_recv=None, link_mbps=0,
+                signal=SIGNAL_TILE, noalloc=False):
         """x_recv given: gathered rows (the gate/up GEMM reads x_recv through
         src_index instead of the layout X)."""
         if epoch is None:
@@ -251,7 +255,8 @@ class RankShare:
             self.epoch = epoch
         moe_expert_combine(self.shape, self.plan_ws, self.x_layout if x_recv is None else None, w_gate_up,
                            w_down, self.h, self.y, self.flags, epoch, self.recv, mode, consumer_cus,
-                           consumer_blocks, spin_timeout_ns, events, stream, x_recv=x_recv)
+                           consumer_blocks, spin_timeout_ns, events, stream, x_recv=x_recv,
+                           noalloc=noalloc, link_mbps=link_mbps, signal=signal)
 
     def _next_epoch(self) -> int:
         """The next epoch; after 2^32 - 1 the flags and the K-split counters

@@ -126,6 +126,8 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
     return 2 * std::min<int64_t>(kMaxProducers, tiles * KT / kMinSkSteps);
   };
   L->sk_slots = (int)std::max(sk_need(gu_tiles_max, d / kGuBK), sk_need(dn_tiles_max, f / kDnBK));
+  L->o_link = take(2 * kMaxWorld);             // uint64 per destination
+  L->o_gready = take(2 * EW);                  // uint64 per (expert, destination) group
   L->o_skc = take(2 * kMaxProducers * 2);
   L->o_skp = take((int64_t)L->sk_slots * 256 * 256);
   L->total_words = off;
@@ -308,6 +310,9 @@ int combine_impl(const moe_shape* s, const void* plan_ws, const uint16_t* x_layo
   // OVERLAP: each consumer workgroup must have a reserved CU of its own
   if (o.mode == MOE_MODE_OVERLAP && o.consumer_blocks > o.consumer_cus) return MOE_EINVAL;
   if (o.spin_timeout_ns < 0) return MOE_EINVAL;
+  if (o.link_mbps < 0 || (o.link_mbps > 0 && o.link_mbps < 1000)) return MOE_EINVAL;
+  if (o.signal != MOE_SIGNAL_TILE && o.signal != MOE_SIGNAL_GROUP) return MOE_EINVAL;
+  if (o.signal == MOE_SIGNAL_GROUP && o.mode == MOE_MODE_COPY_ROWS) return MOE_EINVAL;
   if (epoch == 0) return MOE_EINVAL;
   if (!plan_ws || !aligned(plan_ws, 256)) return MOE_EINVAL;
   const bool compute = (o.mode != MOE_MODE_COPY_ONLY && o.mode != MOE_MODE_COPY_ROWS);
@@ -358,8 +363,16 @@ int combine_impl(const moe_shape* s, const void* plan_ws, const uint16_t* x_layo
     sc.sk_part = (float*)(ws_rw + L.o_skp);
     sc.sk_ctr = (uint64_t*)(ws_rw + L.o_skc);
     sc.claim = ws_rw + L.o_hdr + H_CLAIM;
+    sc.link_free = (uint64_t*)(ws_rw + L.o_link);
+    sc.gready = (uint64_t*)(ws_rw + L.o_gready);
     sc.sk_slots = L.sk_slots;
   }
+  CopyCtl cc;
+  cc.timeout = timeout;
+  cc.link_mbps = (uint32_t)o.link_mbps;
+  cc.signal = o.signal;
+  cc.link_free = sc.link_free;
+  cc.gready = sc.gready;
 
   if (o.mode == MOE_MODE_COPY_ROWS) {
     record(o.events[4], st);
@@ -369,7 +382,7 @@ int combine_impl(const moe_shape* s, const void* plan_ws, const uint16_t* x_layo
   }
   if (o.mode == MOE_MODE_COPY_ONLY) {
     record(o.events[4], st);
-    rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, timeout, o.consumer_blocks ? o.consumer_blocks : consumer_grid(L),
+    rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, cc, o.consumer_blocks ? o.consumer_blocks : consumer_grid(L),
                                 st));
     record(o.events[5], st);
     return rc;
@@ -384,11 +397,11 @@ int combine_impl(const moe_shape* s, const void* plan_ws, const uint16_t* x_layo
   if (rc) return rc;
   if (o.mode == MOE_MODE_SERIAL) {
     record(o.events[2], st);
-    rc = hip_rc(launch_down(L, ws_rw, sc, h, w_down, y, flags, epoch, rp, timeout, full_grid, full_grid, st));
+    rc = hip_rc(launch_down(L, ws_rw, sc, h, w_down, y, flags, epoch, rp, cc, full_grid, full_grid, st));
     record(o.events[3], st);
     if (rc) return rc;
     record(o.events[4], st);
-    rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, timeout, o.consumer_blocks ? o.consumer_blocks : consumer_grid(L),
+    rc = hip_rc(launch_consumer(L, ws_rw, y, flags, epoch, rp, cc, o.consumer_blocks ? o.consumer_blocks : consumer_grid(L),
                                 st));
     record(o.events[5], st);
     return rc;
@@ -402,7 +415,7 @@ int combine_impl(const moe_shape* s, const void* plan_ws, const uint16_t* x_layo
   const int n_cons = o.consumer_blocks ? o.consumer_blocks : o.consumer_cus;
   record(o.events[2], st);
   record(o.events[4], st);
-  rc = hip_rc(launch_down(L, ws_rw, sc, h, w_down, y, flags, epoch, rp, timeout, n_prod, n_prod + n_cons, st));
+  rc = hip_rc(launch_down(L, ws_rw, sc, h, w_down, y, flags, epoch, rp, cc, n_prod, n_prod + n_cons, st));
   record(o.events[3], st);
   record(o.events[5], st);
   return rc;

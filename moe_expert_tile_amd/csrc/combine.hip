@@ -13,9 +13,9 @@ constexpr int kConsumerThreads = 256;
 __global__ __launch_bounds__(kConsumerThreads) void consumer_kernel(PlanLayout L, int32_t* __restrict__ ws,
                                                                    const uint16_t* __restrict__ y,
                                                                    const uint32_t* __restrict__ flags, uint32_t epoch,
-                                                                   RecvPtrs recv, int64_t timeout) {
+                                                                   RecvPtrs recv, CopyCtl cc) {
   __shared__ int s_go;
-  consume_segments<kConsumerThreads>(L, ws, y, flags, epoch, recv, timeout, blockIdx.x, gridDim.x, &s_go);
+  consume_segments<kConsumerThreads>(L, ws, y, flags, epoch, recv, cc, blockIdx.x, gridDim.x, &s_go);
 }
 
 // Per-row ablation of the copy (the alternative the tile-signal notes weigh
@@ -92,9 +92,8 @@ hipError_t launch_consumer_rows(const PlanLayout& L, int32_t* ws, const uint16_t
 }
 
 hipError_t launch_consumer(const PlanLayout& L, int32_t* ws, const uint16_t* y, const uint32_t* flags,
-                           uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(consumer_kernel, dim3(grid), dim3(kConsumerThreads), 0, s, L, ws, y, flags, epoch, recv,
-                     timeout_ticks);
+                           uint32_t epoch, const RecvPtrs& recv, const CopyCtl& cc, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(consumer_kernel, dim3(grid), dim3(kConsumerThreads), 0, s, L, ws, y, flags, epoch, recv, cc);
   return hipGetLastError();
 }
 

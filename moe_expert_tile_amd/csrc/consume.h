@@ -75,17 +75,28 @@ __device__ __forceinline__ int segment_of_unit(const int32_t* sunit, int n_rs, i
   return lo;
 }
 
-// Wave 0 waits until every tile flag of segment `seg` equals `epoch`
-// (bounded by `timeout` ticks of the 100 MHz clock; on timeout the plan's
-// error word becomes MOE_ETIMEOUT); returns 0 if the workgroup must stop.
-// Every thread of the workgroup calls it.
+// Wave 0 waits until segment `seg` is ready: every tile flag of its bands
+// equals `epoch` (signal 0), or its group's ready counter reads (epoch,
+// bands of the group * column tiles) (signal 1).  Bounded by `timeout`
+// ticks of the 100 MHz clock; on timeout the plan's error word becomes
+// MOE_ETIMEOUT.  Returns 0 if the workgroup must stop.  Every thread of the
+// workgroup calls it.
 __device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, const int32_t* sfirst,
                                             const int32_t* snb, const uint32_t* __restrict__ flags, uint32_t epoch,
-                                            int64_t timeout, int seg, int* s_go) {
+                                            const CopyCtl& cc, const int32_t* ws, int seg, int* s_go) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int tpb = L.dn_tpb;
   if (tid < 64) {
     const int f0 = sfirst[seg] * tpb, f1 = (sfirst[seg] + snb[seg]) * tpb;
+    int gi = 0;
+    uint64_t want = 0;
+    if (cc.signal) {
+      // the segment's group: (expert of its first band, its destination)
+      const int e = ws[L.o_bexp + sfirst[seg]], o = ws[L.o_sdst + seg];
+      const int n = ws[L.o_c + e * L.W + o];
+      gi = e * L.W + o;
+      want = ((uint64_t)epoch << 32) | (uint32_t)(((n + L.tb_m - 1) / L.tb_m) * tpb);
+    }
     const uint64_t t0 = wall_clock64();
     int go = 1;
     // exponential back-off between polls (128 clocks doubling to ~4K), and
@@ -94,11 +105,15 @@ __device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, c
     int naps = 1;
     for (int poll = 1;; ++poll) {
       bool ok = true;
-      for (int i = f0 + lane; i < f1; i += 64)
-        ok &= (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch);
+      if (cc.signal) {
+        ok = __hip_atomic_load(cc.gready + gi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want;
+      } else {
+        for (int i = f0 + lane; i < f1; i += 64)
+          ok &= (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch);
+      }
       if (__ballot(!ok) == 0) break;
       if ((poll & 15) == 0) {
-        if ((int64_t)(wall_clock64() - t0) > timeout) {
+        if ((int64_t)(wall_clock64() - t0) > cc.timeout) {
           if (lane == 0)
             __hip_atomic_store(hdr + H_ERROR, 4 /* MOE_ETIMEOUT */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           go = 0;
@@ -120,12 +135,37 @@ __device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, c
   return go;
 }
 
+// Emulated link of destination `dst` (cc.link_mbps > 0): the unit's bytes
+// take bytes / rate on it, from when both the unit is copied and the link
+// is free (the reservation is a compare-and-swap on the link's busy-until
+// time, 1/1024 tick of the 100 MHz clock); the workgroup waits until the
+// transfer would have ended.  Every thread of the workgroup calls it.
+__device__ __forceinline__ void pace_unit(const CopyCtl& cc, int dst, int64_t bytes) {
+  if (cc.link_mbps == 0) return;
+  if (threadIdx.x == 0) {
+    const uint64_t dur = (uint64_t)bytes * 102400u / cc.link_mbps;   // 100 ticks per us, x1024
+    uint64_t* link = cc.link_free + dst;
+    uint64_t old = __hip_atomic_load(link, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t end;
+    for (;;) {
+      const uint64_t now = wall_clock64() << 10;
+      end = (old > now ? old : now) + dur;
+      if (__hip_atomic_compare_exchange_strong(link, &old, end, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        break;
+    }
+    while ((wall_clock64() << 10) < end) __builtin_amdgcn_s_sleep(1);
+  }
+  __syncthreads();
+}
+
 // Copy unit u of segment seg: bytes [lo, lo + kCopyChunk) of the segment,
 // clipped to its end by the buffer bounds, every load before the first store.
+// Returns the unit's bytes.
 template <int NT>
-__device__ __forceinline__ void copy_unit(const PlanLayout& L, const int32_t* ssrc, const int32_t* sdst,
-                                          const int32_t* sdoff, const int32_t* srows, const int32_t* sunit,
-                                          const uint16_t* __restrict__ y, const RecvPtrs& recv, int seg, int u) {
+__device__ __forceinline__ int64_t copy_unit(const PlanLayout& L, const int32_t* ssrc, const int32_t* sdst,
+                                             const int32_t* sdoff, const int32_t* srows, const int32_t* sunit,
+                                             const uint16_t* __restrict__ y, const RecvPtrs& recv, int seg, int u) {
   const int tid = threadIdx.x;
   const int64_t d = L.d;
   const int64_t bytes = (int64_t)srows[seg] * d * 2;
@@ -140,6 +180,7 @@ __device__ __forceinline__ void copy_unit(const PlanLayout& L, const int32_t* ss
   for (int k = 0; k < VPT; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b128(src, (k * NT + tid) * 16, 0, kAgentLoad);
 #pragma unroll
   for (int k = 0; k < VPT; ++k) __builtin_amdgcn_raw_buffer_store_b128(v[k], dst, (k * NT + tid) * 16, 0, kStreamStore);
+  return n;
 }
 
 // One consumer workgroup of NT threads; `cid` in [0, n_cons), units assigned
@@ -148,7 +189,7 @@ __device__ __forceinline__ void copy_unit(const PlanLayout& L, const int32_t* ss
 template <int NT>
 __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_t* __restrict__ y,
                                  const uint32_t* __restrict__ flags, uint32_t epoch, const RecvPtrs& recv,
-                                 int64_t timeout, int cid, int n_cons, int* s_go) {
+                                 const CopyCtl& cc, int cid, int n_cons, int* s_go) {
   int32_t* hdr = ws + L.o_hdr;
   if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
   const int32_t* sfirst = ws + L.o_sfirst;
@@ -167,10 +208,11 @@ __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_
   for (int u = cid; u < U; u += n_cons) {
     seg = segment_of_unit(sunit, n_rs, seg, u);
     if (seg != ready) {
-      if (!wait_segment(L, hdr, sfirst, snb, flags, epoch, timeout, seg, s_go)) return;
+      if (!wait_segment(L, hdr, sfirst, snb, flags, epoch, cc, ws, seg, s_go)) return;
       ready = seg;
     }
-    copy_unit<NT>(L, ssrc, sdst, sdoff, srows, sunit, y, recv, seg, u);
+    const int64_t n = copy_unit<NT>(L, ssrc, sdst, sdoff, srows, sunit, y, recv, seg, u);
+    pace_unit(cc, sdst[seg], n);
   }
 }
 
@@ -192,7 +234,7 @@ constexpr int kClaimUnitsMax = 8;
 template <int NT>
 __device__ void consume_claimed(const PlanLayout& L, int32_t* ws, int32_t* claim, const uint16_t* __restrict__ y,
                                 const uint32_t* __restrict__ flags, uint32_t epoch, const RecvPtrs& recv,
-                                int64_t timeout, int* s_word) {
+                                const CopyCtl& cc, int* s_word) {
   int32_t* hdr = ws + L.o_hdr;
   if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
   const int32_t* sfirst = ws + L.o_sfirst;
@@ -220,10 +262,11 @@ __device__ void consume_claimed(const PlanLayout& L, int32_t* ws, int32_t* claim
       if (u < U) {
         seg = segment_of_unit(sunit, n_rs, seg, u);
         if (seg != ready) {
-          if (!wait_segment(L, hdr, sfirst, snb, flags, epoch, timeout, seg, s_word)) return;
+          if (!wait_segment(L, hdr, sfirst, snb, flags, epoch, cc, ws, seg, s_word)) return;
           ready = seg;
         }
-        copy_unit<NT>(L, ssrc, sdst, sdoff, srows, sunit, y, recv, seg, u);
+        const int64_t n = copy_unit<NT>(L, ssrc, sdst, sdoff, srows, sunit, y, recv, seg, u);
+        pace_unit(cc, sdst[seg], n);
       }
     }
     __syncthreads();

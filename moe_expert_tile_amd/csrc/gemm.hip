@@ -143,7 +143,7 @@ struct GemmArgs {
   int w_rows;             // rows of one expert's weight matrix
   int half;               // SWIGLU: f (offset of the up rows); else 0
   int n_prod;             // producer workgroups (the rest of the grid consumes)
-  int64_t timeout;        // consumer wait bound, 100 MHz ticks
+  CopyCtl cc;             // consumer: wait bound, link pacing, signal mode
   // gate/up: the table of A rows of the compacted rows (cmp_src into x_recv
   // when `gathered`, else cmp_row into the layout X); null for the down GEMM
   const int32_t* rows;
@@ -312,7 +312,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     // hold the GEMM's LDS footprint, so each has a CU of its own; producers
     // never wait for them.
     if ((int)blockIdx.x >= g.n_prod) {
-      consume_claimed<C::NT>(L, g.ws, g.sc.claim, g.out, g.flags, g.epoch, recv, g.timeout, (int*)lds);
+      consume_claimed<C::NT>(L, g.ws, g.sc.claim, g.out, g.flags, g.epoch, recv, g.cc, (int*)lds);
       if (tid == 0) stamp_max(hdr, H_T_CONS_END);
       return;
     }
@@ -895,11 +895,34 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       wait_vm0();
       if constexpr (FLAGS) {
         __syncthreads();
-        // one flag per band of the tile (a band has n_nt flags, one per
-        // column tile)
-        if (tid < nbt)
-          __hip_atomic_store(g.flags + (int64_t)(band0 + tid) * n_nt + nt, g.epoch, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        if (g.cc.signal == 0) {
+          // one flag per band of the tile (a band has n_nt flags, one per
+          // column tile)
+          if (tid < nbt)
+            __hip_atomic_store(g.flags + (int64_t)(band0 + tid) * n_nt + nt, g.epoch, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        } else if (tid == 0) {
+          // group-batched: the tile's bands, run by run of one (expert,
+          // destination) group, are counted on the group's epoch-tagged
+          // ready word; the group is ready once every band of it has been
+          // counted for every column tile
+          uint64_t* gready = g.sc.gready;
+          int b = band0;
+          while (b < band0 + nbt) {
+            const int gi = g.ws[L.o_bexp + b] * L.W + g.ws[L.o_bdst + b];
+            int k = 1;
+            while (b + k < band0 + nbt && g.ws[L.o_bexp + b + k] * L.W + g.ws[L.o_bdst + b + k] == gi) ++k;
+            uint64_t old = __hip_atomic_load(gready + gi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (;;) {
+              const uint32_t cnt = ((uint32_t)(old >> 32) == g.epoch ? (uint32_t)old : 0u) + (uint32_t)k;
+              const uint64_t nv = ((uint64_t)g.epoch << 32) | cnt;
+              if (__hip_atomic_compare_exchange_strong(gready + gi, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT))
+                break;
+            }
+            b += k;
+          }
+        }
       }
     }
   }
@@ -920,7 +943,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       const bool all_started = s_word[0] == g.n_prod;
       __syncthreads();
       if (all_started) {
-        consume_claimed<C::NT>(L, g.ws, g.sc.claim, g.out, g.flags, g.epoch, recv, g.timeout, s_word);
+        consume_claimed<C::NT>(L, g.ws, g.sc.claim, g.out, g.flags, g.epoch, recv, g.cc, s_word);
         if (tid == 0) stamp_max(hdr, H_T_CONS_END);
       }
     }
@@ -934,21 +957,23 @@ using Dn256 = Cfg<256, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_DN_BK, MOE_DN_SA
 static_assert(Dn256::BK == kDnBK, "the host sizes the stream-K scratch with this K step");
 static_assert(Dn256::BM == kDnBM, "the planner packs bands into tiles of this height");
 
-__global__ __launch_bounds__(256) void clear_counters_kernel(uint64_t* ctr, int n, int32_t* claim) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) ctr[i] = 0;
-  if (threadIdx.x < 2) claim[threadIdx.x] = 0;
+__global__ __launch_bounds__(256) void clear_counters_kernel(Scratch sc) {
+  for (int i = threadIdx.x; i < 2 * kMaxProducers; i += blockDim.x) sc.sk_ctr[i] = 0;
+  for (int i = threadIdx.x; i < kMaxWorld; i += blockDim.x) sc.link_free[i] = 0;
+  for (int i = threadIdx.x; i < kMaxGroups; i += blockDim.x) sc.gready[i] = 0;
+  if (threadIdx.x < 2) sc.claim[threadIdx.x] = 0;
 }
 
 }  // namespace
 
 hipError_t launch_clear_counters(const Scratch& sc, hipStream_t s) {
-  hipLaunchKernelGGL(clear_counters_kernel, dim3(1), dim3(256), 0, s, sc.sk_ctr, 2 * kMaxProducers, sc.claim);
+  hipLaunchKernelGGL(clear_counters_kernel, dim3(1), dim3(256), 0, s, sc);
   return hipGetLastError();
 }
 
 hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const Scratch& sc, const uint16_t* x, bool gathered,
                          const uint16_t* wgu, uint16_t* h, uint32_t epoch, int grid, hipStream_t s) {
-  GemmArgs a{ws, x, wgu, h, nullptr, epoch, L.d, L.f, 2 * L.f, L.f, grid, 0,
+  GemmArgs a{ws, x, wgu, h, nullptr, epoch, L.d, L.f, 2 * L.f, L.f, grid, CopyCtl{},
              ws + (gathered ? L.o_cmpsrc : L.o_cmprow), gathered ? 1 : 0, gathered ? (int64_t)L.R * L.d * 2 : 0, sc};
   RecvPtrs none{};
   hipLaunchKernelGGL((grouped_gemm_kernel<GuCfg, true, false>), dim3(grid), dim3(GuCfg::NT), 0, s, L, a, none);
@@ -956,9 +981,9 @@ hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const Scratch& sc, co
 }
 
 hipError_t launch_down(const PlanLayout& L, int32_t* ws, const Scratch& sc, const uint16_t* h, const uint16_t* wd,
-                       uint16_t* y, uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks,
+                       uint16_t* y, uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, const CopyCtl& cc,
                        int n_prod, int grid, hipStream_t s) {
-  GemmArgs a{ws, h, wd, y, flags, epoch, L.f, L.d, L.d, 0, n_prod, timeout_ticks, nullptr, 0, 0, sc};
+  GemmArgs a{ws, h, wd, y, flags, epoch, L.f, L.d, L.d, 0, n_prod, cc, nullptr, 0, 0, sc};
   hipLaunchKernelGGL((grouped_gemm_kernel<Dn256, false, true>), dim3(grid), dim3(Dn256::NT), 0, s, L, a, recv);
   return hipGetLastError();
 }

@@ -80,6 +80,8 @@ struct PlanLayout {
   // compacted row of every band, and per compacted row its layout row and
   // its received row
   int64_t o_crowoff, o_ccum, o_bcrow, o_cmprow, o_cmpsrc;
+  int64_t o_link;                      // uint64 [kMaxWorld] emulated link busy-until times
+  int64_t o_gready;                    // uint64 [E_l * W] group-batched ready counters
   int64_t o_skc;                       // uint64 [2][kMaxProducers] stream-K tile counters (gate/up, down)
   int64_t o_skp;                       // float [sk_slots][256*256] stream-K partial sums
   int64_t total_words;
@@ -101,7 +103,27 @@ struct Scratch {
   float* sk_part;       // [sk_slots][256*256] fp32
   uint64_t* sk_ctr;     // [2][kMaxProducers]: gate/up, down
   int32_t* claim;       // [2]: claims handed out, producers started
+  uint64_t* link_free;  // [kMaxWorld]: emulated link of each destination busy until (1/1024 ticks, 100 MHz)
+  uint64_t* gready;     // [kMaxGroups]: group-batched ready counters, epoch-tagged
   int sk_slots;
+};
+constexpr int kMaxGroups = 1024;       // E_l * W at most
+
+// How the consumer waits and copies (moe_combine_opts):
+//   signal 0: per-band tile flags, equal to the call's epoch when ready;
+//   signal 1: one ready counter per (expert, destination) group, raised by
+//             each down tile by its bands of the group and ready when it
+//             reads (epoch, bands * column tiles);
+//   link_mbps > 0: every copy unit to owner o also takes bytes / rate on an
+//             emulated link of owner o (reserved in order on the device
+//             clock), and the copying workgroup waits until its transfer
+//             would have ended.
+struct CopyCtl {
+  int64_t timeout;      // 100 MHz ticks
+  uint32_t link_mbps;
+  int signal;
+  uint64_t* link_free;
+  const uint64_t* gready;
 };
 
 // LDS carve-out of plan_build_kernel, in int words: the expert x owner tables
@@ -168,14 +190,15 @@ hipError_t launch_gateup(const PlanLayout& L, int32_t* ws, const Scratch& sc, co
 // workgroups (if any) are consumers (consume.h).  Local bands are also
 // written to recv.p[L.r].
 hipError_t launch_down(const PlanLayout& L, int32_t* ws, const Scratch& sc, const uint16_t* h, const uint16_t* wd,
-                       uint16_t* y, uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks,
+                       uint16_t* y, uint32_t* flags, uint32_t epoch, const RecvPtrs& recv, const CopyCtl& cc,
                        int n_prod, int grid, hipStream_t s);
-// zeroes the counters of `sc` (its tile counters and claim words) with a fill
-// kernel: the static scratch keeps the previous call's contents
+// zeroes the counters of `sc` (tile counters, claim words, link times, group
+// counters) with a fill kernel: the static scratch keeps the previous call's
+// contents
 hipError_t launch_clear_counters(const Scratch& sc, hipStream_t s);
 hipError_t launch_consumer(const PlanLayout& L, int32_t* ws, const uint16_t* y,
                            const uint32_t* flags, uint32_t epoch, const RecvPtrs& recv,
-                           int64_t timeout_ticks, int grid, hipStream_t s);
+                           const CopyCtl& cc, int grid, hipStream_t s);
 // per-row ablation of the copy: one wavefront per remote row (COPY_ROWS mode)
 hipError_t launch_consumer_rows(const PlanLayout& L, int32_t* ws, const uint16_t* y, const uint32_t* flags,
                                 uint32_t epoch, const RecvPtrs& recv, int64_t timeout_ticks, hipStream_t s);

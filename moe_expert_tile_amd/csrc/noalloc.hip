@@ -12,9 +12,12 @@ namespace {
 
 constexpr int kStaticSkSlots = 256;                        // partial-sum slots of 256x256 fp32 (64 MiB)
 constexpr size_t kCtrBytes = 2 * kMaxProducers * 8;        // uint64 tile counters, gate/up and down
-constexpr size_t kClaimOff = kCtrBytes;                    // two int32 claim counters
-constexpr size_t kPartOff = kCtrBytes + 4096;              // partial sums, 4 KB past the claim words
+constexpr size_t kClaimOff = kCtrBytes;                    // two int32 claim counters (256 bytes kept)
+constexpr size_t kLinkOff = kClaimOff + 256;               // uint64 link busy-until time per destination
+constexpr size_t kGreadyOff = kLinkOff + kMaxWorld * 8;    // uint64 group ready counters
+constexpr size_t kPartOff = kGreadyOff + kMaxGroups * 8;   // partial sums
 constexpr size_t kScratchBytes = kPartOff + (size_t)kStaticSkSlots * 256 * 256 * 4;
+static_assert(kPartOff % 256 == 0, "aligned partial sums");
 
 // The array itself.  In host code its name is a host-side stand-in, not a
 // device address: only the address hipGetSymbolAddress returns for the
@@ -42,6 +45,8 @@ int static_scratch(int dev, Scratch* out) {
   char* base = (char*)p;
   out->sk_ctr = (uint64_t*)base;
   out->claim = (int32_t*)(base + kClaimOff);
+  out->link_free = (uint64_t*)(base + kLinkOff);
+  out->gready = (uint64_t*)(base + kGreadyOff);
   out->sk_part = (float*)(base + kPartOff);
   out->sk_slots = kStaticSkSlots;
   return MOE_OK;

@@ -116,6 +116,14 @@ def test_bad_pointers_are_rejected_before_any_hip_call():
         m.moe_expert_combine(big, good, None, good, good, good, good, good, 1, [good] * 4, stream=0,
                              x_recv=good)
     assert ei.value.status == m.MOE_EINVAL                        # R*d*2 = 2^31 bytes: too large to gather
+    for kw in (dict(link_mbps=999), dict(link_mbps=-1), dict(signal=2), dict(signal=-1),
+               dict(signal=m.SIGNAL_GROUP, mode=m.MODE_COPY_ROWS)):
+        for noalloc in (False, True):
+            with pytest.raises(m.MoEError) as ei:
+                m.moe_expert_combine(s, good, good, good, good, good, good, good, 1, [good] * 4, stream=0,
+                                     noalloc=noalloc, **kw)
+            assert ei.value.status == m.MOE_EINVAL, kw               # link too slow, no such signal,
+                                                                     # per-row copy without tile flags
     with pytest.raises(m.MoEError) as ei:
         m.moe_scale(s, good, good, good, good + 2, stream=0)
     assert ei.value.status == m.MOE_EINVAL

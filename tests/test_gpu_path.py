@@ -296,3 +296,72 @@ def test_scale_alone_within_rounding_bound(name):
     excess = float((np.abs(out - ref) / bound).max())
     say(f"[scale-bound] {name} worst {excess:.3f}, max ulps {int(OB.ulp_distance(host_bits(share.out[: cfg.tokens[r]]), ref_bits).max())}")
     assert excess <= 1.0
+
+
+@pytest.mark.parametrize("name,signal,link", [("tiny_unit", 1, 2000), ("qwen3", 1, 153000), ("mixtral", 1, 0),
+                                              ("decode_tb32", 0, 153000), ("dsv3_skew", 1, 153000),
+                                              ("decode_tb64", 1, 20000)])
+def test_paced_and_group_signalled_combine(name, signal, link):
+    """The consumer behind an emulated link per destination (link_mbps) and
+    with group-batched ready counters instead of per-band flags (signal 1;
+    the Perseus page's decoupled signalling, one signal per destination
+    group), in the overlapped and the serial mode, over two epochs with y
+    poisoned by NaN first: y is bit for bit the per-band, unpaced y of the
+    same mode, and the receive buffers are exactly the plan applied to it."""
+    import moe_expert_tile_amd as m
+    c = case(name)
+    cfg, pl = c["cfg"], c["plan"]
+    wgu, wd = weights(name)
+    wgu_d, wd_d = dev_bf16(wgu), dev_bf16(wd)
+    written = OC.written_rows(pl)
+    say(f"[signal] {name} signal={signal} link_mbps={link}")
+    for mode in (m.MODE_OVERLAP, m.MODE_SERIAL):
+        ref = m.RankShare(shape_of(cfg, pl.R))
+        ref.plan(torch.from_numpy(c["ids"]).cuda(), dev_bf16(c["x_recv"]))
+        ref.combine(wgu_d, wd_d, mode=mode)
+        assert ref.status() == m.MOE_OK
+        y_ref = host_bits(ref.y[:pl.M])
+        sh = m.RankShare(shape_of(cfg, pl.R))
+        sh.plan(torch.from_numpy(c["ids"]).cuda(), dev_bf16(c["x_recv"]))
+        for it in range(2):
+            sh.y.fill_(float("nan"))
+            for o in range(cfg.W):
+                sh.recv[o].copy_(dev_bf16(synth.foreign_rows(cfg, o)))
+            sh.combine(wgu_d, wd_d, mode=mode, signal=signal, link_mbps=link)
+            assert sh.status() == m.MOE_OK
+            Y = host_bits(sh.y[:pl.M])
+            assert np.array_equal(Y, y_ref), (mode, it)
+            for o in range(cfg.W):
+                exp = synth.foreign_rows(cfg, o)
+                dst, src = written[o]
+                exp[dst] = Y[src]
+                assert np.array_equal(host_bits(sh.recv[o][: exp.shape[0]]), exp), (mode, it, o)
+        del ref, sh
+
+
+def test_paced_copy_takes_at_least_the_link_time():
+    """With flags already set, the copy alone at 2000 MB/s per destination
+    lasts at least (bytes to the busiest destination) / rate: the emulated
+    links bound it, not the memory."""
+    import moe_expert_tile_amd as m
+    c, share, _, _ = planned("tiny_unit", m.MODE_SERIAL)
+    cfg, pl = c["cfg"], c["plan"]
+    sg = pl.segs
+    per_dst = np.zeros(cfg.W)
+    for q in range(pl.n_remote_segs):
+        per_dst[int(sg["dst"][q])] += int(sg["rows"][q]) * cfg.d * 2
+    rate = 2000e6
+    floor_s = per_dst.max() / rate
+    times = []
+    for _ in range(3):
+        e0, e1 = m.timing_events(2)
+        e0.record()
+        share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch, link_mbps=2000)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    assert share.status() == m.MOE_OK
+    say(f"[paced] busiest destination {per_dst.max() / 1e3:.0f} KB: floor {floor_s * 1e6:.1f} us, "
+        f"copy {min(times) * 1e6:.1f} us")
+    assert min(times) >= 0.9 * floor_s
+    assert min(times) <= 10 * floor_s + 1e-3
