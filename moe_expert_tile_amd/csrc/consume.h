@@ -136,24 +136,22 @@ __device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, c
 }
 
 // Emulated link of destination `dst` (cc.link_mbps > 0): the unit's bytes
-// take bytes / rate on it, from when both the unit is copied and the link
-// is free (the reservation is a compare-and-swap on the link's busy-until
-// time, 1/1024 tick of the 100 MHz clock); the workgroup waits until the
-// transfer would have ended.  Every thread of the workgroup calls it.
+// take bytes / rate on it, in a slot that starts no earlier than the unit's
+// arrival.  The link's busy-until time L (1/1024 tick of the 100 MHz clock)
+// only grows: the unit first raises it to its arrival time (atomic max),
+// then takes [L, L + dur) with an atomic add.  Slots handed out by the adds
+// never overlap, a max in between only opens an idle gap, and neither step
+// retries: a compare-and-swap loop measured ~20x slower, with hundreds of
+// workgroups retrying one device-scope word at one memory-side round trip
+// per attempt.  The workgroup waits until its slot ends.  Every thread of
+// the workgroup calls it.
 __device__ __forceinline__ void pace_unit(const CopyCtl& cc, int dst, int64_t bytes) {
   if (cc.link_mbps == 0) return;
   if (threadIdx.x == 0) {
     const uint64_t dur = (uint64_t)bytes * 102400u / cc.link_mbps;   // 100 ticks per us, x1024
     uint64_t* link = cc.link_free + dst;
-    uint64_t old = __hip_atomic_load(link, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint64_t end;
-    for (;;) {
-      const uint64_t now = wall_clock64() << 10;
-      end = (old > now ? old : now) + dur;
-      if (__hip_atomic_compare_exchange_strong(link, &old, end, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT))
-        break;
-    }
+    __hip_atomic_fetch_max(link, (uint64_t)wall_clock64() << 10, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t end = __hip_atomic_fetch_add(link, dur, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + dur;
     while ((wall_clock64() << 10) < end) __builtin_amdgcn_s_sleep(1);
   }
   __syncthreads();
