@@ -73,7 +73,7 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->dn_tpb = L->dn_ntn;
   L->gu_ntn = f / (kGuBN / 2);
   L->gu_mt_cap = (int)(rows_cap / kGuBM + E_l + 1);
-  L->build_stage = 0;  // decided at launch, against the device's LDS limit
+  L->band_lds = 0;  // decided at launch, against the device's LDS limit
 
   int64_t off = 0;
   auto take = [&](int64_t n) {
@@ -97,12 +97,9 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->o_src = take(rows_cap);
   L->o_pos = take((int64_t)L->T_r * k);
   L->o_bh = take((int64_t)L->NB * (E_l + 2));
-  L->o_bp = take((int64_t)L->NB * (E_l + 1));
-  L->o_brecv = take(L->NB);
   L->o_bhr = take((int64_t)L->NB_r * L->E);
-  L->o_bpr = take((int64_t)L->NB_r * L->E);
-  L->o_baser = take(L->E);
-  L->o_pad = take(2 * EW);
+  L->o_obase = take(W + 1);
+  L->o_btmp = take(6 * (B + 1));
   L->o_gumt_row = take(L->gu_mt_cap);
   L->o_gumt_exp = take(L->gu_mt_cap);
   L->o_dnt_row = take(B); L->o_dnt_exp = take(B); L->o_dnt_band = take(B); L->o_dnt_nb = take(B);
@@ -277,13 +274,10 @@ int moe_plan(const moe_shape* s, const int32_t* topk_ids, const uint16_t* x_recv
   int dev;
   rc = prepare(&dev);
   if (rc) return rc;
-  // the plan builder copies the per-block histograms into LDS only when the
-  // whole request fits well inside the device's per-workgroup LDS
+  // the plan builder keeps its per-band tables in LDS when they fit the
+  // device's per-workgroup LDS (every shape here but the largest)
   const int64_t lds_cap = std::min<int64_t>(g_dev[dev].lds_per_block, kBuildLdsBytes);
-  L.band_table = (L.bands_cap <= kBandTableMax &&
-                  (int64_t)build_lds(L.W, L.E_l, L.E, 0, 0, L.bands_cap, false).total * 4 <= lds_cap)
-                     ? L.bands_cap : 0;
-  L.build_stage = (int64_t)build_lds(L.W, L.E_l, L.E, L.NB, L.NB_r, L.band_table, true).total * 4 <= lds_cap;
+  L.band_lds = (int64_t)build_lds(L.W, L.E_l, L.bands_cap, true).total * 4 <= lds_cap;
   return hip_rc(launch_plan(L, topk_ids, x_recv, (int32_t*)plan_ws, x_layout, (hipStream_t)stream));
 }
 

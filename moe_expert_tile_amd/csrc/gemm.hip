@@ -41,11 +41,18 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Tile shapes (compile-time; the defaults are the measured best on MI355X).
 #ifndef MOE_XCD_ROWS
-// XCDs sharing a weight block in the two-level tile order (1, 2, 4, 8).
-// Measured: 2 takes 2% off the Mixtral-like down GEMM; the gate/up GEMMs and
-// the other workloads are within noise of 1; 8 is slower on the
-// DeepSeek-like GEMMs.
+// XCDs sharing a weight block in the two-level tile order (1, 2, 4, 8), for
+// the gate/up GEMM.  Measured: the gate/up GEMMs are within noise of 1; 8
+// is slower on the DeepSeek-like share.
 #define MOE_XCD_ROWS 2
+#endif
+#ifndef MOE_XCD_ROWS_DN
+// The same for the down GEMM.  Measured over packed down tiles (same box,
+// serial mode, two passes): 1 takes the DeepSeek-like down GEMM from
+// 1663-1693 to 1621-1636 us and leaves the Mixtral- and Qwen3-like ones
+// within noise; 4 and 8 are 2-4% slower there, and per-XCD blocks of 4 x 8,
+// 2 x 16, 16 x 2 or 32 x 1 tiles are no better than 8 x 4.
+#define MOE_XCD_ROWS_DN 1
 #endif
 #ifndef MOE_GU_WAVES_M
 #define MOE_GU_WAVES_M 4
@@ -87,8 +94,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #define MOE_LOAD_AUX 0   // cache-policy bits of the operand loads (default policy measured best)
 #endif
 constexpr int kDeviceScope = 16;   // sc1 cache-policy bit: device scope, written through the XCD's L2
-constexpr int kXcdRows = MOE_XCD_ROWS;
-static_assert(kXcdRows == 1 || kXcdRows == 2 || kXcdRows == 4 || kXcdRows == 8, "XCD rows");
+constexpr int kXcdRowsGu = MOE_XCD_ROWS;
+constexpr int kXcdRowsDn = MOE_XCD_ROWS_DN;
+static_assert(kXcdRowsGu == 1 || kXcdRowsGu == 2 || kXcdRowsGu == 4 || kXcdRowsGu == 8, "XCD rows");
+static_assert(kXcdRowsDn == 1 || kXcdRowsDn == 2 || kXcdRowsDn == 4 || kXcdRowsDn == 8, "XCD rows");
 
 // BM x BN output tile, WAVES_M x WAVES_N wavefronts, K step BK; the A and B
 // operands have their own global -> LDS rings, SA and SB stages deep (2 or
@@ -204,8 +213,9 @@ __device__ __forceinline__ void xcd_block_shape(int per_xcd, int& SR, int& SC) {
   }
 }
 
+template <int XR>
 __device__ __forceinline__ void decode_tile(int t, int n_mt, int n_nt, int SR, int SC, int& mt, int& nt) {
-  constexpr int XR = kXcdRows, XC = 8 / kXcdRows;
+  constexpr int XC = 8 / XR;
   const int BR = SR * XR, BC = SC * XC;
   const int full_rg = n_mt / BR;
   int rg, rr, t1;
@@ -420,9 +430,9 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     ++items;
     int mt, nt;
     if (t < n_mt_r * n_nt) {
-      decode_tile(t, n_mt_r, n_nt, blk_r, blk_c, mt, nt);
+      decode_tile<SWIGLU ? kXcdRowsGu : kXcdRowsDn>(t, n_mt_r, n_nt, blk_r, blk_c, mt, nt);
     } else {
-      decode_tile(t - n_mt_r * n_nt, n_mt - n_mt_r, n_nt, blk_r, blk_c, mt, nt);
+      decode_tile<SWIGLU ? kXcdRowsGu : kXcdRowsDn>(t - n_mt_r * n_nt, n_mt - n_mt_r, n_nt, blk_r, blk_c, mt, nt);
       mt += n_mt_r;
     }
     // row tile.  gate/up: 256 compacted rows of one expert (row0 their

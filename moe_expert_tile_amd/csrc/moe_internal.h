@@ -12,7 +12,6 @@ namespace moe {
 constexpr int kMaxWorld = 64;
 constexpr int kPairsPerBlock = 512;    // (token, slot) pairs per planner workgroup
 constexpr int kPlanThreads = 256;
-constexpr int kBuildThreads = 256;     // the single-workgroup plan builder
 constexpr int kCopyChunk = 32768;      // bytes per consumer copy unit
 constexpr int kGuBM = 256;             // gate/up GEMM tile rows
 constexpr int kGuBN = 256;             // gate/up GEMM tile cols (128 gate + 128 up)
@@ -54,6 +53,9 @@ enum Hdr {
   // producers that have started (the default Scratch::claim); both zeroed by
   // the gate/up launch, which precedes every down GEMM on the same stream
   H_CLAIM = 18, H_STARTED = 19,
+  // planner: set by the plan builder once the group tables the pair placers
+  // need are in memory; cleared by the counting launch that precedes it
+  H_READY = 20,
   H_WORDS = 64
 };
 
@@ -64,16 +66,16 @@ struct PlanLayout {
   int R, rows_cap, bands_cap, T_r, NB, NB_r, gu_mt_cap;
   int dn_ntn, dn_tpb;                  // down GEMM: column tiles, flags per band (= column tiles)
   int gu_ntn;                          // gate/up GEMM n tiles (f / 128)
-  int build_stage;                     // plan_build copies the block histograms into LDS
-  int band_table;                      // plan_build's band -> group table in LDS (bands_cap, or 0)
+  int band_lds;                        // the plan builder keeps its per-band tables in LDS (else in btmp)
   int sk_slots;                        // stream-K partial-sum slots (256x256 fp32 each) in the workspace
   int64_t o_hdr, o_c, o_low, o_grp, o_me, o_rowoff, o_rb, o_order, o_base;
   int64_t o_bexp, o_bdst, o_bsrc, o_bdoff, o_bval;
   int64_t o_sfirst, o_snb, o_sdst, o_sdoff, o_ssrc, o_srows, o_sunit;
   int64_t o_src, o_pos;
-  int64_t o_bh, o_bp, o_brecv, o_bhr, o_bpr, o_baser;
+  int64_t o_bh, o_bhr;                 // per-block histograms (plan_count)
+  int64_t o_obase;                     // [W + 1]: received rows from the owners before each owner
+  int64_t o_btmp;                      // [6 * bands_cap + 2]: the builder's per-band tables when not in LDS
   int64_t o_gumt_row, o_gumt_exp;
-  int64_t o_pad;                       // [2][E_l*W]: first padding row and padding rows of every remote group
   int64_t o_dnt_row, o_dnt_exp, o_dnt_band, o_dnt_nb;
   // compacted rows (the layout without its padding rows, in layout order):
   // start of every expert, offset of every group inside its expert, first
@@ -126,47 +128,73 @@ struct CopyCtl {
   const uint64_t* gready;
 };
 
-// LDS carve-out of plan_build_kernel, in int words: the expert x owner tables
-// and the per-group scratch stay on chip, and when `stage` is set the
-// per-block histograms are copied in too.  The host sizes the launch's
-// dynamic LDS with the same function the kernel carves it with.
+// LDS carve-outs of the planner's second launch, in int words; the host
+// sizes the launch's dynamic LDS with the same functions the kernel carves
+// it with.  The builder keeps its expert x owner tables on chip and, when
+// `bands` is set, six per-band tables of bands_cap (+1) words.
 struct BuildLds {
-  int c, grp, base, gstart, low, me, rowoff, rb, order, baser, gupre, dnpre, sh, misc, ccum, ce, crowoff;
-  int band_g, stage_bh, stage_bhr, total;
+  int c, grp, ccum, base, gstart, low, bad, obase, me, ce, rowoff, crowoff, rb, order, gupre, sh, misc;
+  int bg, vv, nx, ja, jb, on, total;
 };
 #if defined(__HIPCC__)
 __host__ __device__
 #endif
-inline BuildLds build_lds(int W, int E_l, int E, int NB, int NB_r, int band_table, bool stage) {
+inline BuildLds build_lds(int W, int E_l, int bands_cap, bool bands) {
   BuildLds s;
   const int EW = E_l * W;
   int o = 0;
   s.c = o; o += EW;
   s.grp = o; o += EW;
+  s.ccum = o; o += EW;
   s.base = o; o += EW;
   s.gstart = o; o += EW + 1;
   s.low = o; o += W;
+  s.bad = o; o += W;
+  s.obase = o; o += W + 1;
   s.me = o; o += E_l;
+  s.ce = o; o += E_l;
   s.rowoff = o; o += E_l + 1;
+  s.crowoff = o; o += E_l + 1;
   s.rb = o; o += E_l;
   s.order = o; o += E_l;
-  s.baser = o; o += E;
   s.gupre = o; o += E_l + 1;
-  s.dnpre = o; o += 2 * E_l + 1;
-  s.sh = o; o += 16;
+  s.sh = o; o += 32;
   s.misc = o; o += 8;
-  s.ccum = o; o += EW;
-  s.ce = o; o += E_l;
-  s.crowoff = o; o += E_l + 1;
-  s.band_g = o; o += band_table;              // group of every band (0: not kept)
-  o = (o + 3) & ~3;                           // 16-byte aligned staging
-  s.stage_bh = o; if (stage) o += (NB * (E_l + 2) + 3) & ~3;
-  s.stage_bhr = o; if (stage) o += NB_r * E;
+  const int nb = bands ? bands_cap + 1 : 0;
+  s.bg = o; o += nb;    // group of every band
+  s.vv = o; o += nb;    // valid rows of every band, then their exclusive prefix over S
+  s.nx = o; o += nb;    // end of the down tile that would start at the band
+  s.ja = o; o += nb;    // pointer-doubling jumps (two buffers)
+  s.jb = o; o += nb;
+  s.on = o; o += nb;    // the band starts a down tile
   s.total = o;
   return s;
 }
-constexpr int kBuildLdsBytes = 64 * 1024;   // cap on plan_build's dynamic LDS (the default dynamic limit)
-constexpr int kBandTableMax = 8192;          // plan_build keeps a band -> group table up to this many bands
+// pair placers (workgroups 1.. of the second launch)
+struct PlaceLds {
+  int run, wc, run_g, wc_g, bp, pre_g, base_g, srow, scrow, sh, misc, total;
+};
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline PlaceLds place_lds(int E_l, int E, int nw) {
+  PlaceLds s;
+  int o = 0;
+  s.run = o; o += E_l + 1;
+  s.wc = o; o += nw * (E_l + 1);
+  s.run_g = o; o += E;
+  s.wc_g = o; o += nw * E;
+  s.bp = o; o += E_l;
+  s.pre_g = o; o += E;
+  s.base_g = o; o += E;
+  s.srow = o; o += E_l;
+  s.scrow = o; o += E_l;
+  s.sh = o; o += 32;
+  s.misc = o; o += 8;
+  s.total = o;
+  return s;
+}
+constexpr int kBuildLdsBytes = 64 * 1024;   // cap on the planner's dynamic LDS (the default dynamic limit)
 
 // host-side helpers (api.cpp)
 bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb,

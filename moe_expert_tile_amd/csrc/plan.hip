@@ -5,17 +5,22 @@
 //                   LDS histograms of the local experts, of "below this rank's
 //                   experts" (for receive offsets) and, for the rank's own
 //                   tokens, of all experts (for the owner-side slot table).
-//   K2 plan_build   one workgroup of 256 threads: scans over the histograms
-//                   -> group counts, padded group offsets, X_e sizes, rule
-//                   (ii) expert order, band list S (remote bands first),
-//                   combine plan, segments and their copy units, GEMM row-tile
-//                   tables, padding extent of every remote group.  Its tables
-//                   live in LDS; nothing it writes to memory is read back.
-//   K3 plan_place   one workgroup per pair block again: stable rank of every
-//                   pair inside its (expert, owner) group with bit-sliced wave
-//                   ballots + LDS carries -> src_index of every real layout
-//                   row, and the owner-side slot of each of the rank's own
-//                   pairs; the blocks also write the padding entries (-1).
+//   K2 plan_build_place, one launch of 1 + NB workgroups:
+//     workgroup 0, the builder: sums the histograms into group counts, lays
+//                   out the groups (padded offsets in X_e, compacted offsets,
+//                   expert starts), hands those few tables to the placers and
+//                   raises a ready word, then builds the rule (ii) expert
+//                   order, the band list S (remote bands first), the combine
+//                   plan, segments and their copy units, and the GEMMs'
+//                   row-tile tables -- every step a parallel pass or a scan.
+//     workgroups 1..NB, the placers, one per pair block: prefixes of their
+//                   own from the histograms, then (once the builder's tables
+//                   are ready) the stable rank of every pair inside its
+//                   (expert, owner) group with bit-sliced wave ballots + LDS
+//                   carries -> src_index of every real layout row, the
+//                   compacted-row tables, and the owner-side slot of each of
+//                   the rank's own pairs; they also write the padding entries
+//                   (-1) of src_index.
 //   K4 plan_gather  one wavefront per layout row: X[row] = x_recv[src] or 0,
 //                   16-byte coalesced loads and stores.
 //
@@ -46,7 +51,7 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 }
 
 // Exclusive scan of a pair of ints per thread over the workgroup (at most
-// kBuildThreads threads): wavefront scans, then every thread adds the totals
+// 16 wavefronts): wavefront scans, then every thread adds the totals
 // of the wavefronts below its own (read in parallel from LDS).  `sh` holds
 // 2 ints per wavefront.  Two barriers; `sh` is free again on return.
 __device__ int2 block_scan2(int a, int b, int* sh, int2* total) {
@@ -137,6 +142,31 @@ __device__ __forceinline__ int owner_of_block(const PlanLayout& L, int b) {
   return o;
 }
 
+// Relaxed agent-scope (device-wide) accesses to the words the builder hands
+// to the placers: the stores write through this XCD's L2 to the memory side
+// and the loads do not return lines another XCD's L2 cached earlier.
+__device__ __forceinline__ void agent_store(int32_t* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int agent_load(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Sum of a[(b) * stride + x] over b in [b0, b1), eight independent loads in
+// flight per thread.
+__device__ __forceinline__ int sum_blocks(const int32_t* __restrict__ a, int64_t stride, int x, int b0, int b1) {
+  int s = 0;
+  for (int b = b0; b < b1; b += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (b + u < b1) ? a[(int64_t)(b + u) * stride + x] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  return s;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(PlanLayout L, const int32_t* __restrict__ topk,
                                                                  int32_t* __restrict__ ws) {
   extern __shared__ int sh[];
@@ -146,6 +176,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(PlanLayout L, 
   const int p1 = min(p0 + kPairsPerBlock, L.pair_off[o + 1]);
   const bool own = (o == L.r);
   const int nb = L.E_l + 2 + (own ? L.E : 0);
+  // the next launch's placers wait for the builder to raise this word
+  if (b == 0 && threadIdx.x == 0) agent_store(ws + L.o_hdr + H_READY, 0);
   for (int i = threadIdx.x; i < nb; i += blockDim.x) sh[i] = 0;
   __syncthreads();
   const int lo = L.r * L.E_l;
@@ -169,127 +201,70 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(PlanLayout L, 
   }
 }
 
-__global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L, int32_t* __restrict__ ws) {
+// The plan builder (workgroup 0 of the second launch).  kBandLds: its
+// per-band tables live in LDS, else in the workspace's btmp region.
+template <bool kBandLds>
+__device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
   extern __shared__ int smem[];
   const int tid = threadIdx.x, nt = blockDim.x;
-  const int W = L.W, r = L.r, E_l = L.E_l, E = L.E, tb = L.tb_m;
+  const int W = L.W, r = L.r, E_l = L.E_l, tb = L.tb_m;
   const int HB = E_l + 2;
   const int EW = E_l * W;
-  const BuildLds S = build_lds(W, E_l, E, L.NB, L.NB_r, L.band_table, L.build_stage != 0);
+  const BuildLds S = build_lds(W, E_l, L.bands_cap, kBandLds);
   int32_t* hdr = ws + L.o_hdr;
   int* c = smem + S.c;             // [E_l][W] group sizes
   int* grp = smem + S.grp;         // [E_l][W] group offsets inside X_e
+  int* ccum = smem + S.ccum;       // [E_l][W] group offsets inside X_e's compacted rows
   int* base = smem + S.base;       // [W][E_l] receive-buffer bases
   int* gstart = smem + S.gstart;   // [E_l*W + 1] first band of every group in S order
-  int* low = smem + S.low;         // [W]
-  int* me = smem + S.me;           // [E_l]
-  int* rowoff = smem + S.rowoff;   // [E_l + 1]
-  int* rb = smem + S.rb;           // [E_l]
-  int* order = smem + S.order;     // [E_l]
-  int* baser = smem + S.baser;     // [E]
-  int* gupre = smem + S.gupre;     // [E_l + 1] gate/up row tiles before each expert (rule (ii) order)
-  int* dnpre = smem + S.dnpre;     // [2 E_l + 1] down row tiles before each run
-  int* sh = smem + S.sh;           // scan scratch
-  int* misc = smem + S.misc;       // [0] remote segments
-  int* ccum = smem + S.ccum;       // [E_l][W] group offsets inside X_e's compacted rows
+  int* low = smem + S.low;         // [W] pairs of owner o with an expert below this rank's
+  int* bad = smem + S.bad;         // [W] expert ids out of range, per owner
+  int* obase = smem + S.obase;     // [W + 1] received rows from the owners before o
+  int* me = smem + S.me;           // [E_l] rows of X_e
   int* ce = smem + S.ce;           // [E_l] real rows of X_e
+  int* rowoff = smem + S.rowoff;   // [E_l + 1]
   int* crowoff = smem + S.crowoff; // [E_l + 1] first compacted row of X_e
-  const int32_t* bh = ws + L.o_bh;
-  int32_t* bp = ws + L.o_bp;
-  int32_t* brecv = ws + L.o_brecv;
-  const int32_t* bhr = ws + L.o_bhr;
-  int32_t* bpr = ws + L.o_bpr;
-  if (L.build_stage) {
-    // the per-block histograms are read many times below: one coalesced
-    // parallel copy into LDS (the host sized the LDS for it)
-    int* s_bh = smem + S.stage_bh;
-    int* s_bhr = smem + S.stage_bhr;
-    // 16-byte loads, 8 in flight per thread (both ends 16-byte aligned);
-    // the last n mod 4 words one by one
-    auto stage = [&](int* dst, const int32_t* src, int n) {
-      const int n4 = n >> 2;
-      const int4* s4 = (const int4*)src;
-      int4* d4 = (int4*)dst;
-      for (int i0 = tid; i0 < n4; i0 += 8 * nt) {
-        int4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (i0 + u * nt < n4) v[u] = s4[i0 + u * nt];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (i0 + u * nt < n4) d4[i0 + u * nt] = v[u];
-      }
-      for (int i = 4 * n4 + tid; i < n; i += nt) dst[i] = src[i];
-    };
-    stage(s_bh, bh, L.NB * HB);
-    stage(s_bhr, bhr, L.NB_r * E);
-    __syncthreads();
-    bh = s_bh;
-    bhr = s_bhr;
-  }
+  int* rb = smem + S.rb;           // [E_l] remote bands of every expert
+  int* order = smem + S.order;     // [E_l] rule (ii) order
+  int* gupre = smem + S.gupre;     // [E_l + 1] gate/up row tiles before each expert (rule (ii) order)
+  int* sh = smem + S.sh;           // scan scratch
+  int* misc = smem + S.misc;
+  const int32_t* __restrict__ bh = ws + L.o_bh;
 
-  // (a) received-row base of every block (owners in order) and routing
-  //     errors, in one scan over the blocks
-  const int2 rtot = scan_items2(
-      L.NB,
-      [&](int b) {
-        int s = 0;
-        for (int e = 0; e < E_l; ++e) s += bh[(int64_t)b * HB + e];
-        return make_int2(s, bh[(int64_t)b * HB + E_l + 1]);
-      },
-      [&](int b, int2 pre) { brecv[b] = pre.x; }, sh);
-  const int rcount = rtot.x, bad_total = rtot.y;
-
-  // (b) group counts c[e][o], low[o], per-block prefixes within each owner
-  // (the histogram entries are loaded 8 at a time ahead of the dependent
-  // stores, which the compiler cannot move past loads from the same workspace)
-  for (int it = tid; it < W * (E_l + 1); it += nt) {
-    const int o = it / (E_l + 1), x = it % (E_l + 1);
-    int run = 0;
-    for (int b0 = L.blk_off[o]; b0 < L.blk_off[o + 1]; b0 += 8) {
-      int v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (b0 + u < L.blk_off[o + 1]) ? bh[(int64_t)(b0 + u) * HB + x] : 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (b0 + u < L.blk_off[o + 1]) bp[(int64_t)(b0 + u) * (E_l + 1) + x] = run;
-        run += v[u];
-      }
-    }
-    if (x < E_l) c[x * W + o] = run; else low[o] = run;
-  }
-  // (c) the rank's own tokens: per-expert counts and per-block prefixes
-  for (int g = tid; g < E; g += nt) {
-    int run = 0;
-    for (int b0 = 0; b0 < L.NB_r; b0 += 8) {
-      int v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (b0 + u < L.NB_r) ? bhr[(int64_t)(b0 + u) * E + g] : 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (b0 + u < L.NB_r) bpr[(int64_t)(b0 + u) * E + g] = run;
-        run += v[u];
-      }
-    }
-    baser[g] = run;  // count for now, turned into a prefix below
+  // (a) group counts c[e][o], low[o] and bad ids per owner: one thread per
+  //     (owner, histogram column), summing the owner's blocks
+  for (int it = tid; it < W * HB; it += nt) {
+    const int o = it / HB, x = it - o * HB;
+    const int s = sum_blocks(bh, HB, x, L.blk_off[o], L.blk_off[o + 1]);
+    if (x < E_l) c[x * W + o] = s;
+    else if (x == E_l) low[o] = s;
+    else bad[o] = s;
   }
   __syncthreads();
-  (void)scan_items(
-      E, [&](int g) { return baser[g]; }, [&](int g, int pre) { baser[g] = pre; }, sh);
-
+  int lr = 0, lb = 0;
+  for (int i = tid; i < EW; i += nt) lr += c[i];
+  for (int o = tid; o < W; o += nt) lb += bad[o];
+  int2 tot;
+  (void)block_scan2(lr, lb, sh, &tot);
+  const int rcount = tot.x, bad_total = tot.y;
   if (bad_total > 0 || rcount != L.R) {
     if (tid == 0) {
-      hdr[H_ERROR] = 5;  // MOE_EROUTING
-      for (int i = 1; i < H_WORDS; ++i) hdr[i] = 0;
+      for (int i = 1; i < H_WORDS; ++i)
+        if (i != H_READY) hdr[i] = 0;
       hdr[H_RCOUNT] = rcount;
+      agent_store(hdr + H_ERROR, 5);  // MOE_EROUTING
+      wait_stores();
+      agent_store(hdr + H_READY, 1);  // the placers see the error and leave
     }
     return;
   }
 
-  // (d) layout: padded group offsets inside X_e, remote owners ascending then
-  //     r; receive-buffer bases: owner o's pairs below global expert r*E_l + e
+  // (b) layout of every expert: padded group offsets inside X_e (remote
+  //     owners ascending, then r) and compacted ones; receive-buffer bases
+  //     (owner o's pairs below global expert r*E_l + e); remote bands per
+  //     expert (rule (ii)); received rows per owner
   for (int e = tid; e < E_l; e += nt) {
-    int run = 0, crun = 0;
+    int run = 0, crun = 0, nb = 0;
     for (int q = 0; q < W; ++q) {
       const int o = (q < W - 1) ? (q < r ? q : q + 1) : r;
       grp[e * W + o] = run;
@@ -297,20 +272,22 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
       const int n = c[e * W + o];
       run += (o == r) ? n : ((n + tb - 1) / tb) * tb;
       crun += n;
+      if (o != r) nb += (n + tb - 1) / tb;
     }
     me[e] = run;
     ce[e] = crun;
+    rb[e] = nb;
   }
+  int rsum = 0;   // received rows from owner `tid` (wave 0 holds the owners)
   for (int o = tid; o < W; o += nt) {
     int run = low[o];
     for (int e = 0; e < E_l; ++e) { base[o * E_l + e] = run; run += c[e * W + o]; }
+    rsum = run - low[o];
   }
-  // remote bands per expert, for rule (ii)
-  for (int e = tid; e < E_l; e += nt) {
-    int n = 0;
-    for (int o = 0; o < W; ++o)
-      if (o != r) n += (c[e * W + o] + tb - 1) / tb;
-    rb[e] = n;
+  if (tid < 64) {   // W <= 64: one wavefront scans the owners
+    const int incl = wave_incl_scan(tid < W ? rsum : 0);
+    if (tid < W) obase[tid] = incl - rsum;
+    if (tid == W - 1) obase[W] = incl;
   }
   __syncthreads();
   const int2 mtot = scan_items2(
@@ -321,6 +298,10 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
       },
       sh);
   const int M = mtot.x;
+  if (tid == 0) {
+    rowoff[E_l] = M;
+    crowoff[E_l] = mtot.y;   // = rcount
+  }
   // rule (ii) order: more remote bands first, ties to the lower id
   for (int e = tid; e < E_l; e += nt) {
     int rank = 0;
@@ -331,14 +312,39 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     }
     order[rank] = e;
   }
-  if (tid == 0) {
-    rowoff[E_l] = M;
-    crowoff[E_l] = mtot.y;   // = rcount
-  }
   __syncthreads();
 
-  // (e) groups in schedule order: remote groups of experts in rule (ii) order
-  //     (owners ascending, r skipped), then the local group of every expert.
+  // (c) hand the placers what they need -- group sizes, padded and
+  //     compacted group offsets, expert starts, owner receive bases -- with
+  //     device-scope stores, wait for them, then raise the ready word
+  for (int i = tid; i < EW; i += nt) {
+    agent_store(ws + L.o_c + i, c[i]);
+    agent_store(ws + L.o_grp + i, grp[i]);
+    agent_store(ws + L.o_ccum + i, ccum[i]);
+  }
+  for (int i = tid; i <= E_l; i += nt) {
+    agent_store(ws + L.o_rowoff + i, rowoff[i]);
+    agent_store(ws + L.o_crowoff + i, crowoff[i]);
+  }
+  for (int i = tid; i <= W; i += nt) agent_store(ws + L.o_obase + i, obase[i]);
+  if (tid == 0) agent_store(hdr + H_ERROR, 0);
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) agent_store(hdr + H_READY, 1);
+
+  // the rest is read by the GEMMs, the consumer and the scale, all later
+  // launches, and by inspection
+  for (int i = tid; i < EW; i += nt) ws[L.o_base + i] = base[i];
+  for (int i = tid; i < W; i += nt) ws[L.o_low + i] = low[i];
+  for (int i = tid; i < E_l; i += nt) {
+    ws[L.o_me + i] = me[i];
+    ws[L.o_rb + i] = rb[i];
+    ws[L.o_order + i] = order[i];
+  }
+
+  // (d) groups in schedule order: remote groups of experts in rule (ii)
+  //     order (owners ascending, r skipped), then the local group of every
+  //     expert
   const int NGR = E_l * (W - 1);
   const int NG = E_l * W;
   auto group_eo = [&](int gi, int& e, int& o) {
@@ -360,60 +366,66 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
       },
       [&](int gi, int pre) { gstart[gi] = pre; }, sh);
   if (B > L.bands_cap) {
-    if (tid == 0) { hdr[H_ERROR] = 2; for (int i = 1; i < H_WORDS; ++i) hdr[i] = 0; }
+    if (tid == 0) {
+      for (int i = 1; i < H_WORDS; ++i)
+        if (i != H_READY) hdr[i] = 0;
+      hdr[H_ERROR] = 2;
+    }
     return;
   }
   const int n_remote = NGR < NG ? gstart[NGR] : B;
+  if (tid == 0) gstart[NG] = B;
 
-  // (f) bands in S order, one thread per group (a group's bands are
-  //     consecutive in S), a band -> group table in LDS when it fits, and
-  //     the padding rows of every remote group
+  // per-band tables
+  int* bg;   // [B] group of every band
+  int* vv;   // [B + 1] valid rows, then their exclusive prefix over S
+  int* nx;   // [B] end of the down tile that would start at the band
+  int* ja;   // [B] pointer-doubling jumps
+  int* jb;
+  int* on;   // [B] the band starts a down tile
+  if constexpr (kBandLds) {
+    bg = smem + S.bg; vv = smem + S.vv; nx = smem + S.nx; ja = smem + S.ja; jb = smem + S.jb; on = smem + S.on;
+  } else {
+    int* t = ws + L.o_btmp;
+    const int nb = L.bands_cap + 1;
+    bg = t; vv = t + nb; nx = t + 2 * nb; ja = t + 3 * nb; jb = t + 4 * nb; on = t + 5 * nb;
+  }
+
+  // (e) bands in S order, one thread per band
   int32_t* bexp = ws + L.o_bexp;
   int32_t* bdst = ws + L.o_bdst;
   int32_t* bsrc = ws + L.o_bsrc;
   int32_t* bdoff = ws + L.o_bdoff;
   int32_t* bval = ws + L.o_bval;
   int32_t* bcrow = ws + L.o_bcrow;
-  int* band_g = L.band_table > 0 ? smem + S.band_g : nullptr;
-  int32_t* pad_st = ws + L.o_pad;         // read by plan_place, which writes the padding entries
-  int32_t* pad_ct = pad_st + EW;
-  for (int gi = tid; gi < NG; gi += nt) {
+  __syncthreads();   // gstart complete
+  for (int b = tid; b < B; b += nt) {
+    const int gi = upper_index(gstart, NG, b);   // the non-empty group holding band b
     int e, o;
     group_eo(gi, e, o);
+    const int q = b - gstart[gi];
     const int n = c[e * W + o];
-    const int nb = (n + tb - 1) / tb;
-    const int gs = gstart[gi];
-    const int rowb = rowoff[e] + grp[e * W + o];
-    const int dstb = base[o * E_l + e];
-    const int crowb = crowoff[e] + ccum[e * W + o];
-    for (int q = 0; q < nb; ++q) {
-      if (band_g) band_g[gs + q] = gi;
-      bcrow[gs + q] = crowb + q * tb;
-      bexp[gs + q] = e;
-      bdst[gs + q] = o;
-      bsrc[gs + q] = rowb + q * tb;
-      bdoff[gs + q] = dstb + q * tb;
-      bval[gs + q] = min(tb, n - q * tb);
-    }
-    if (gi < NGR) {
-      pad_st[gi] = rowb + n;
-      pad_ct[gi] = nb * tb - n;
-    }
+    const int v = min(tb, n - q * tb);
+    bg[b] = gi;
+    vv[b] = v;
+    bexp[b] = e;
+    bdst[b] = o;
+    bsrc[b] = rowoff[e] + grp[e * W + o] + q * tb;
+    bdoff[b] = base[o * E_l + e] + q * tb;
+    bval[b] = v;
+    bcrow[b] = crowoff[e] + ccum[e * W + o] + q * tb;
   }
+  __syncthreads();
 
-  // (g) segments (§5.2): the first and the last remote band alone; otherwise
-  //     runs of <= mgb bands that restart at every group boundary.  Every
-  //     band decides whether it starts a segment and, if so, the segment's
-  //     bands, rows and copy units (a segment never crosses a group, so they
-  //     are read off the group); one pair scan over the bands numbers the
-  //     segments and places their copy units.
+  // (f) segments (§5.2): the first and the last remote band alone;
+  //     otherwise runs of <= mgb bands that restart at every group
+  //     boundary.  Every band decides whether it starts a segment and, if
+  //     so, the segment's bands, rows and copy units (a segment never
+  //     crosses a group, so they are read off the group); one pair scan
+  //     over the bands numbers the segments and places their copy units.
   const int mgb = L.mgb;
   const int64_t row_bytes = (int64_t)L.d * 2;
   auto units_of = [&](int rows) { return (int)((rows * row_bytes + kCopyChunk - 1) / kCopyChunk); };
-  if (tid == 0) gstart[NG] = B;
-  __syncthreads();   // band table, gstart[NG]
-  auto group_of = [&](int b) { return band_g ? band_g[b] : upper_index(gstart, NG, b); };
-  // does band b (of group gi, first band gs) start a segment
   auto starts = [&](int b, int gi, int gs) {
     if (b == gs) return true;
     if (gi < NGR) {
@@ -422,9 +434,8 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     }
     return ((b - gs) % mgb) == 0;
   };
-  // segment starting at band b: its bands and rows (false if b starts none)
   auto seg_at = [&](int b, int& gi, int& nb, int& rows) {
-    gi = group_of(b);
+    gi = bg[b];
     const int gs = gstart[gi];
     if (!starts(b, gi, gs)) return false;
     const int ge = gstart[gi + 1];
@@ -472,7 +483,7 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
   const int n_rsegs = misc[0] >= 0 ? misc[0] : NS;
   if (tid == 0) sunit[NS] = U;
 
-  // (i) gate/up m-tiles: the compacted rows of every X_e (its real rows,
+  // (g) gate/up m-tiles: the compacted rows of every X_e (its real rows,
   //     padding left out) cut into kGuBM-row tiles, experts in rule (ii)
   //     order; one thread per tile.  The GEMM computes no padding row.
   int32_t* mt_row = ws + L.o_gumt_row;
@@ -487,91 +498,86 @@ __global__ __launch_bounds__(kBuildThreads) void plan_build_kernel(PlanLayout L,
     mt_exp[t] = e;
   }
 
-  // (j) down tiles: the runs of row-contiguous bands in S order -- the
-  //     remote bands of each expert in rule (ii) order (its remote groups
-  //     follow one another at the start of X_e), then the local bands of
-  //     each expert -- each cut greedily into tiles of whole bands whose
-  //     real rows add up to at most kDnBM (and at most kDnMaxBands bands).
-  //     The GEMM multiplies a tile's real rows only, packed, so a tile of
-  //     two half-empty bands costs one band's work.  One thread per run:
-  //     count, scan, then write.
+  // (h) down tiles.  The bands of S form runs of row-contiguous bands --
+  //     the remote bands of each expert in rule (ii) order (its remote
+  //     groups follow one another at the start of X_e), then the local
+  //     bands of each expert -- and each run is cut greedily into tiles of
+  //     whole bands whose real rows add up to at most kDnBM (and at most
+  //     kDnMaxBands bands).  The GEMM multiplies a tile's real rows only,
+  //     packed, so a tile of two half-empty bands costs one band's work.
+  //     In parallel: nx[b] is where a tile starting at band b would end
+  //     (a binary search over the prefix of valid rows), and the tiles'
+  //     first bands are the chain run start -> nx -> nx ..., marked by
+  //     pointer doubling: after round k every first band within 2^k tiles
+  //     of its run's start is marked.
+  (void)scan_items(
+      B, [&](int b) { return vv[b]; }, [&](int b, int pre) { vv[b] = pre; }, sh);
+  if (tid == 0) vv[B] = rcount;   // the valid rows of all bands
+  __syncthreads();
+  auto run_of = [&](int gi, int& rs, int& re) {
+    if (gi < NGR) {
+      const int q = gi / (W - 1);
+      rs = gstart[q * (W - 1)];
+      re = gstart[(q + 1) * (W - 1)];
+    } else {
+      rs = gstart[gi];
+      re = gstart[gi + 1];
+    }
+  };
+  for (int b = tid; b < B; b += nt) {
+    int rs, re;
+    run_of(bg[b], rs, re);
+    int lo = b + 1, hi = min(re, b + kDnMaxBands);   // a band alone always fits
+    const int p0 = vv[b];
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (vv[mid] - p0 <= kDnBM) lo = mid; else hi = mid - 1;
+    }
+    nx[b] = lo;
+    ja[b] = lo < re ? lo : -1;
+    on[b] = (b == rs);
+  }
+  __syncthreads();
+  for (;;) {
+    for (int b = tid; b < B; b += nt)
+      if (on[b] && ja[b] >= 0) on[ja[b]] = 1;   // only first bands are ever marked
+    __syncthreads();
+    int more = 0;
+    for (int b = tid; b < B; b += nt) {
+      const int j = ja[b];
+      const int jj = j >= 0 ? ja[j] : -1;
+      jb[b] = jj;
+      more |= jj >= 0;
+    }
+    int* t = ja; ja = jb; jb = t;
+    if (!__syncthreads_or(more)) break;
+  }
+  // a last marking pass with the final jumps
+  for (int b = tid; b < B; b += nt)
+    if (on[b] && ja[b] >= 0) on[ja[b]] = 1;
+  __syncthreads();
   int32_t* dt_row = ws + L.o_dnt_row;
   int32_t* dt_exp = ws + L.o_dnt_exp;
   int32_t* dt_band = ws + L.o_dnt_band;
   int32_t* dt_nb = ws + L.o_dnt_nb;
-  // greedy packing of run q; with `at` >= 0 the tiles are written from
-  // index `at` on; returns the number of tiles
-  auto pack_run = [&](int q, int at) {
-    const bool remote_run = q < E_l;
-    const int e = remote_run ? order[q] : q - E_l;
-    int b = remote_run ? (W > 1 ? gstart[q * (W - 1)] : 0) : gstart[NGR + e];
-    int ntiles = 0, rows = 0, nbt = 0, tfirst = b, trow = 0;
-    for (int qq = 0; qq < W; ++qq) {
-      int o;
-      if (remote_run) {
-        if (qq >= W - 1) break;
-        o = qq < r ? qq : qq + 1;
-      } else {
-        if (qq > 0) break;
-        o = r;
-      }
-      const int n = c[e * W + o];
-      const int row_g = rowoff[e] + grp[e * W + o];
-      for (int j = 0; j * tb < n; ++j, ++b) {
-        const int v = min(tb, n - j * tb);
-        if (nbt > 0 && (rows + v > kDnBM || nbt == kDnMaxBands)) {
-          if (at >= 0) {
-            dt_row[at + ntiles] = trow;
-            dt_exp[at + ntiles] = e;
-            dt_band[at + ntiles] = tfirst;
-            dt_nb[at + ntiles] = nbt;
-          }
-          ++ntiles;
-          rows = 0;
-          nbt = 0;
-        }
-        if (nbt == 0) {
-          tfirst = b;
-          trow = row_g + j * tb;
-        }
-        rows += v;
-        ++nbt;
-      }
-    }
-    if (nbt > 0) {
-      if (at >= 0) {
-        dt_row[at + ntiles] = trow;
-        dt_exp[at + ntiles] = e;
-        dt_band[at + ntiles] = tfirst;
-        dt_nb[at + ntiles] = nbt;
-      }
-      ++ntiles;
-    }
-    return ntiles;
-  };
+  if (tid == 0) misc[1] = -1;
+  __syncthreads();
   const int NDT = scan_items(
-      2 * E_l, [&](int q) { return pack_run(q, -1); }, [&](int q, int pre) { dnpre[q] = pre; }, sh);
-  const int ndt_r = dnpre[E_l];   // the remote runs come first
-  for (int q = tid; q < 2 * E_l; q += nt) (void)pack_run(q, dnpre[q]);
+      B, [&](int b) { return on[b]; },
+      [&](int b, int pre) {
+        if (b == n_remote) misc[1] = pre;   // down tiles of remote bands (they come first)
+        if (!on[b]) return;
+        int e, o;
+        group_eo(bg[b], e, o);
+        dt_row[pre] = rowoff[e] + grp[e * W + o] + (b - gstart[bg[b]]) * tb;
+        dt_exp[pre] = e;
+        dt_band[pre] = b;
+        dt_nb[pre] = nx[b] - b;
+      },
+      sh);
+  const int ndt_r = misc[1] >= 0 ? misc[1] : NDT;
 
-  // results used by later kernels and by inspection
-  for (int i = tid; i < EW; i += nt) {
-    ws[L.o_c + i] = c[i];
-    ws[L.o_grp + i] = grp[i];
-    ws[L.o_base + i] = base[i];
-    ws[L.o_ccum + i] = ccum[i];
-  }
-  for (int i = tid; i <= E_l; i += nt) ws[L.o_crowoff + i] = crowoff[i];
-  for (int i = tid; i < W; i += nt) ws[L.o_low + i] = low[i];
-  for (int i = tid; i < E_l; i += nt) {
-    ws[L.o_me + i] = me[i];
-    ws[L.o_rb + i] = rb[i];
-    ws[L.o_order + i] = order[i];
-  }
-  for (int i = tid; i <= E_l; i += nt) ws[L.o_rowoff + i] = rowoff[i];
-  for (int i = tid; i < E; i += nt) ws[L.o_baser + i] = baser[i];
   if (tid == 0) {
-    hdr[H_ERROR] = 0;
     hdr[H_M] = M;
     hdr[H_BANDS] = B;
     hdr[H_REMOTE] = n_remote;
@@ -614,54 +620,113 @@ __device__ __forceinline__ int bits_for(int n) {
   return b;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_place_kernel(PlanLayout L, const int32_t* __restrict__ topk,
-                                                                 int32_t* __restrict__ ws) {
-  extern __shared__ int sh[];
-  const int32_t* hdr = ws + L.o_hdr;
-  if (hdr[H_ERROR] != 0) return;
-  const int b = blockIdx.x;
+// wait for the builder's tables: 2 s on the 100 MHz clock at most (the
+// builder raises the word within microseconds; the bound only guarantees
+// that every wave ends)
+constexpr int64_t kPlanWaitTicks = 200000000;
+
+// A pair placer (workgroups 1.. of the second launch): pair block b.  It
+// first computes, from the histograms alone, its prefixes inside its owner
+// (and, for the rank's own tokens, the owner-side slot bases); then it waits
+// for the builder's group tables and gives every pair its stable rank inside
+// its (expert, owner) group.
+__device__ void place_pairs(const PlanLayout& L, const int32_t* __restrict__ topk, int32_t* __restrict__ ws,
+                            int b) {
+  extern __shared__ int smem[];
+  const int tid = threadIdx.x, nt = blockDim.x, w = tid >> 6;
   const int o = owner_of_block(L, b);
   const int p0 = L.pair_off[o] + (b - L.blk_off[o]) * kPairsPerBlock;
   const int p1 = min(p0 + kPairsPerBlock, L.pair_off[o + 1]);
   const bool own = (o == L.r);
-  const int E_l = L.E_l, E = L.E, W = L.W;
+  const int E_l = L.E_l, E = L.E, W = L.W, HB = E_l + 2;
   const int NX = E_l + 1;              // local experts + "any local"
   const int nw = kPlanThreads / 64;
-  int* run = sh;                       // [NX]
-  int* wc = run + NX;                  // [nw][NX]
-  int* run_g = wc + nw * NX;           // [E] (own only)
-  int* wc_g = run_g + E;               // [nw][E]
-  const int tid = threadIdx.x, w = tid >> 6;
-  for (int i = tid; i < NX * (nw + 1); i += blockDim.x) sh[i] = 0;
+  const PlaceLds S = place_lds(E_l, E, nw);
+  int* run = smem + S.run;             // [NX] running counts over the block's rounds
+  int* wc = smem + S.wc;               // [nw][NX] per-wave counts of one round
+  int* run_g = smem + S.run_g;         // [E] (own only)
+  int* wc_g = smem + S.wc_g;           // [nw][E]
+  int* bp = smem + S.bp;               // [E_l] pairs of the owner's earlier blocks per local expert
+  int* pre_g = smem + S.pre_g;         // [E] own: pairs of the earlier own blocks per expert
+  int* base_g = smem + S.base_g;       // [E] own: first slot of every expert's pairs
+  int* srow = smem + S.srow;           // [E_l] first layout row of group (e, o)
+  int* scrow = smem + S.scrow;         // [E_l] its first compacted row
+  int* sh = smem + S.sh;
+  int* misc = smem + S.misc;
+  int32_t* hdr = ws + L.o_hdr;
+  const int32_t* __restrict__ bh = ws + L.o_bh;
+  const int32_t* __restrict__ bhr = ws + L.o_bhr;
+
+  for (int i = tid; i < NX * (nw + 1); i += nt) smem[S.run + i] = 0;   // run and wc are adjacent
   if (own)
-    for (int i = tid; i < E * (nw + 1); i += blockDim.x) run_g[i] = 0;
+    for (int i = tid; i < E * (nw + 1); i += nt) smem[S.run_g + i] = 0;
+  // (a) before the builder is ready: prefixes from the histograms
+  int loc = 0;
+  for (int e = tid; e < E_l; e += nt) {
+    const int s = sum_blocks(bh, HB, e, L.blk_off[o], b);
+    bp[e] = s;
+    loc += s;
+  }
+  int before;   // local pairs in the owner's earlier blocks
+  (void)block_scan(loc, sh, &before);
+  if (own) {
+    const int bo = b - L.blk_off[L.r];
+    for (int g = tid; g < E; g += nt) {
+      const int pre = sum_blocks(bhr, E, g, 0, bo);
+      pre_g[g] = pre;
+      base_g[g] = pre + sum_blocks(bhr, E, g, bo, L.NB_r);   // the own tokens' count of expert g
+    }
+    __syncthreads();
+    (void)scan_items(
+        E, [&](int g) { return base_g[g]; }, [&](int g, int pre) { base_g[g] = pre; }, sh);
+  }
+  // (b) wait for the builder
+  if (tid == 0) {
+    const uint64_t t0 = wall_clock64();
+    int err = 0;
+    while (agent_load(hdr + H_READY) == 0) {
+      __builtin_amdgcn_s_sleep(2);
+      if ((int64_t)(wall_clock64() - t0) > kPlanWaitTicks) { err = 4; break; }   // MOE_ETIMEOUT
+    }
+    if (err) agent_store(hdr + H_ERROR, err);
+    else err = agent_load(hdr + H_ERROR);
+    misc[0] = err;
+  }
   __syncthreads();
-  const int32_t* rowoff = ws + L.o_rowoff;
-  const int32_t* grp = ws + L.o_grp;
-  const int32_t* crowoff = ws + L.o_crowoff;
-  const int32_t* ccum = ws + L.o_ccum;
-  int32_t* cmp_row = ws + L.o_cmprow;
-  int32_t* cmp_src = ws + L.o_cmpsrc;
-  const int32_t* bp = ws + L.o_bp + (int64_t)b * (E_l + 1);
-  const int recv_base = ws[L.o_brecv + b];
+  if (misc[0] != 0) return;
+  // (c) the builder's tables for this owner's groups
+  const int32_t* gc = ws + L.o_c;
+  const int32_t* ggrp = ws + L.o_grp;
+  const int32_t* gccum = ws + L.o_ccum;
+  const int32_t* growoff = ws + L.o_rowoff;
+  const int32_t* gcrowoff = ws + L.o_crowoff;
+  for (int e = tid; e < E_l; e += nt) {
+    srow[e] = agent_load(growoff + e) + agent_load(ggrp + e * W + o);
+    scrow[e] = agent_load(gcrowoff + e) + agent_load(gccum + e * W + o);
+  }
+  const int recv_base = agent_load(ws + L.o_obase + o) + before;
   int32_t* src = ws + L.o_src;
-  const int32_t* bpr = ws + L.o_bpr + (int64_t)(b - L.blk_off[L.r]) * E;
-  const int32_t* baser = ws + L.o_baser;
-  int32_t* pos = ws + L.o_pos;
   // the padding entries of src_index: the tail of every remote group, the
-  // groups shared out over the blocks
+  // groups shared out over the placers
   {
     const int NGR = E_l * (W - 1);
-    const int32_t* pad_st = ws + L.o_pad;
-    const int32_t* pad_ct = pad_st + E_l * W;
-    for (int gi = blockIdx.x; gi < NGR; gi += gridDim.x) {
-      const int st = pad_st[gi], ct = pad_ct[gi];
-      for (int q = threadIdx.x; q < ct; q += blockDim.x) src[st + q] = -1;
+    const int tb = L.tb_m;
+    for (int gi = b; gi < NGR; gi += L.NB) {
+      const int e = gi / (W - 1), q = gi % (W - 1);
+      const int og = q < L.r ? q : q + 1;
+      const int n = agent_load(gc + e * W + og);
+      const int st = agent_load(growoff + e) + agent_load(ggrp + e * W + og) + n;
+      const int ct = ((n + tb - 1) / tb) * tb - n;
+      for (int x = tid; x < ct; x += nt) src[st + x] = -1;
     }
   }
+  __syncthreads();
+  int32_t* cmp_row = ws + L.o_cmprow;
+  int32_t* cmp_src = ws + L.o_cmpsrc;
+  int32_t* pos = ws + L.o_pos;
   const int lo = L.r * E_l;
   const int bits_e = bits_for(E_l + 1), bits_g = bits_for(E);
-  for (int p_base = p0; p_base < p1; p_base += blockDim.x) {
+  for (int p_base = p0; p_base < p1; p_base += nt) {
     const int p = p_base + tid;
     const int g = (p < p1) ? topk[p] : -1;
     const int e = (g >= lo && g < lo + E_l) ? g - lo : -1;
@@ -673,8 +738,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_place_kernel(PlanLayout L, 
     if (e >= 0) {
       int rank_e = run[e] + re, rank_l = run[E_l] + rl;
       for (int x = 0; x < w; ++x) { rank_e += wc[x * NX + e]; rank_l += wc[x * NX + E_l]; }
-      const int dest = rowoff[e] + grp[e * W + o] + bp[e] + rank_e;
-      const int cdest = crowoff[e] + ccum[e * W + o] + bp[e] + rank_e;
+      const int dest = srow[e] + bp[e] + rank_e;
+      const int cdest = scrow[e] + bp[e] + rank_e;
       const int i = recv_base + rank_l;
       if (dest < L.rows_cap && i < L.R) src[dest] = i;
       if (cdest < L.R && i < L.R) {
@@ -685,21 +750,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_place_kernel(PlanLayout L, 
     if (own && g >= 0 && g < E) {
       int rank_g = run_g[g] + rg;
       for (int x = 0; x < w; ++x) rank_g += wc_g[x * E + g];
-      pos[p - L.pair_off[L.r]] = baser[g] + bpr[g] + rank_g;
+      pos[p - L.pair_off[L.r]] = base_g[g] + pre_g[g] + rank_g;
     }
     __syncthreads();
-    for (int x = tid; x < NX; x += blockDim.x) {
+    for (int x = tid; x < NX; x += nt) {
       int s = 0;
       for (int y = 0; y < nw; ++y) { s += wc[y * NX + x]; wc[y * NX + x] = 0; }
       run[x] += s;
     }
     if (own)
-      for (int x = tid; x < E; x += blockDim.x) {
+      for (int x = tid; x < E; x += nt) {
         int s = 0;
         for (int y = 0; y < nw; ++y) { s += wc_g[y * E + x]; wc_g[y * E + x] = 0; }
         run_g[x] += s;
       }
     __syncthreads();
+  }
+}
+
+// The second launch: workgroup 0 builds the plan, workgroups 1..NB place
+// the pairs of one block each.  The builder has the lowest id, so it is
+// dispatched first and never waits for a placer.
+__global__ __launch_bounds__(kPlanThreads) void plan_build_place_kernel(PlanLayout L, const int32_t* __restrict__ topk,
+                                                                       int32_t* __restrict__ ws) {
+  if (blockIdx.x == 0) {
+    if (L.band_lds) build_plan<true>(L, ws);
+    else build_plan<false>(L, ws);
+  } else {
+    place_pairs(L, topk, ws, blockIdx.x - 1);
   }
 }
 
@@ -765,13 +843,10 @@ hipError_t launch_plan(const PlanLayout& L, const int32_t* topk, const uint16_t*
     const size_t sh_count = (size_t)(L.E_l + 2 + L.E) * sizeof(int);
     hipLaunchKernelGGL(plan_count_kernel, dim3(L.NB), dim3(kPlanThreads), sh_count, s, L, topk, ws);
   }
-  const int words = build_lds(L.W, L.E_l, L.E, L.NB, L.NB_r, L.band_table, L.build_stage != 0).total;
-  hipLaunchKernelGGL(plan_build_kernel, dim3(1), dim3(kBuildThreads), (size_t)words * sizeof(int), s, L, ws);
-  if (L.NB > 0) {
-    const int nw = kPlanThreads / 64;
-    const size_t sh_place = (size_t)((L.E_l + 1) * (nw + 1) + L.E * (nw + 1)) * sizeof(int);
-    hipLaunchKernelGGL(plan_place_kernel, dim3(L.NB), dim3(kPlanThreads), sh_place, s, L, topk, ws);
-  }
+  const int words = max(build_lds(L.W, L.E_l, L.bands_cap, L.band_lds != 0).total,
+                        L.NB > 0 ? place_lds(L.E_l, L.E, kPlanThreads / 64).total : 0);
+  hipLaunchKernelGGL(plan_build_place_kernel, dim3(1 + L.NB), dim3(kPlanThreads), (size_t)words * sizeof(int), s, L,
+                     topk, ws);
   if (x_layout == nullptr) return hipGetLastError();   // metadata only: the GEMM gathers its rows
   const int rows_per_block = 4;
   int grid = (L.rows_cap + rows_per_block - 1) / rows_per_block;
