@@ -74,6 +74,13 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->gu_ntn = f / (kGuBN / 2);
   L->gu_mt_cap = (int)(rows_cap / kGuBM + E_l + 1);
   L->band_lds = 0;  // decided at launch, against the device's LDS limit
+  // the planner's divisors: row counts (below 2^31), band and group indices
+  L->div_tb = make_fastdiv(tb_m, 31);
+  L->div_mgb = make_fastdiv(mgb, 31);
+  L->div_wm1 = make_fastdiv(W > 1 ? W - 1 : 1, 31);
+  L->div_hb = make_fastdiv(E_l + 2, 31);
+  L->div_w = make_fastdiv(W, 31);
+  L->div_el = make_fastdiv(E_l, 31);
 
   int64_t off = 0;
   auto take = [&](int64_t n) {
@@ -99,6 +106,8 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->o_bh = take((int64_t)L->NB * (E_l + 2));
   L->o_bhr = take((int64_t)L->NB_r * L->E);
   L->o_obase = take(W + 1);
+  L->o_grow = take(EW);
+  L->o_gcrow = take(EW);
   L->o_btmp = take(6 * (B + 1));
   L->o_gumt_row = take(L->gu_mt_cap);
   L->o_gumt_exp = take(L->gu_mt_cap);

@@ -59,6 +59,29 @@ enum Hdr {
   H_WORDS = 64
 };
 
+// Exact division of a non-negative int below 2^nbits by a fixed divisor d,
+// with one 64-bit multiply and a shift: s = nbits + bit length of d, so
+// 2^s > n d, and m = ceil(2^s / d); then floor(n m / 2^s) = floor(n / d),
+// because n (m - 2^s / d) / 2^s < n / 2^s < 1 / d, and n / d is an integer
+// or at least 1 / d below the next one.  m n < 2^(2 nbits + 1).
+struct FastDiv {
+  uint64_t m;
+  int s, d;
+};
+inline FastDiv make_fastdiv(int d, int nbits) {
+  int len = 0;
+  while ((1 << len) <= d) ++len;
+  FastDiv f;
+  f.s = nbits + len;
+  f.m = (((uint64_t)1 << f.s) + (uint64_t)d - 1) / (uint64_t)d;
+  f.d = d;
+  return f;
+}
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline int fdiv(int n, const FastDiv& f) { return (int)(((uint64_t)(uint32_t)n * f.m) >> f.s); }
+
 // Everything a kernel needs to find the plan arrays: sizes and int32 element
 // offsets from the workspace base.  Built on the host, passed by value.
 struct PlanLayout {
@@ -67,6 +90,7 @@ struct PlanLayout {
   int dn_ntn, dn_tpb;                  // down GEMM: column tiles, flags per band (= column tiles)
   int gu_ntn;                          // gate/up GEMM n tiles (f / 128)
   int band_lds;                        // the plan builder keeps its per-band tables in LDS (else in btmp)
+  FastDiv div_tb, div_mgb, div_wm1, div_hb, div_w, div_el;   // by tb_m, mgb, max(W - 1, 1), E_l + 2, W, E_l
   int sk_slots;                        // stream-K partial-sum slots (256x256 fp32 each) in the workspace
   int64_t o_hdr, o_c, o_low, o_grp, o_me, o_rowoff, o_rb, o_order, o_base;
   int64_t o_bexp, o_bdst, o_bsrc, o_bdoff, o_bval;
@@ -74,6 +98,7 @@ struct PlanLayout {
   int64_t o_src, o_pos;
   int64_t o_bh, o_bhr;                 // per-block histograms (plan_count)
   int64_t o_obase;                     // [W + 1]: received rows from the owners before each owner
+  int64_t o_grow, o_gcrow;             // [E_l][W]: first layout row and first compacted row of every group
   int64_t o_btmp;                      // [6 * bands_cap + 2]: the builder's per-band tables when not in LDS
   int64_t o_gumt_row, o_gumt_exp;
   int64_t o_dnt_row, o_dnt_exp, o_dnt_band, o_dnt_nb;
@@ -133,7 +158,7 @@ struct CopyCtl {
 // it with.  The builder keeps its expert x owner tables on chip and, when
 // `bands` is set, six per-band tables of bands_cap (+1) words.
 struct BuildLds {
-  int c, grp, ccum, base, gstart, low, bad, obase, me, ce, rowoff, crowoff, rb, order, gupre, sh, misc;
+  int c, grow, gcrow, base, gstart, low, bad, obase, me, ce, rowoff, crowoff, rb, order, gupre, sh, misc;
   int bg, vv, nx, ja, jb, on, total;
 };
 #if defined(__HIPCC__)
@@ -144,8 +169,8 @@ inline BuildLds build_lds(int W, int E_l, int bands_cap, bool bands) {
   const int EW = E_l * W;
   int o = 0;
   s.c = o; o += EW;
-  s.grp = o; o += EW;
-  s.ccum = o; o += EW;
+  s.grow = o; o += EW;
+  s.gcrow = o; o += EW;
   s.base = o; o += EW;
   s.gstart = o; o += EW + 1;
   s.low = o; o += W;

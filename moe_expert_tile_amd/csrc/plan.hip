@@ -50,13 +50,13 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Exclusive scan of a pair of ints per thread over the workgroup (at most
-// 16 wavefronts): wavefront scans, then every thread adds the totals
+// Exclusive scan of a pair of ints per thread over the workgroup of
+// kPlanThreads threads: wavefront scans, then every thread adds the totals
 // of the wavefronts below its own (read in parallel from LDS).  `sh` holds
 // 2 ints per wavefront.  Two barriers; `sh` is free again on return.
 __device__ int2 block_scan2(int a, int b, int* sh, int2* total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nw = (blockDim.x + 63) >> 6;
+  constexpr int nw = kPlanThreads / 64;
   const int xa = wave_incl_scan(a), xb = wave_incl_scan(b);
   if (lane == 63) {
     sh[2 * w] = xa;
@@ -91,7 +91,7 @@ __device__ __forceinline__ int block_scan(int v, int* sh, int* total) {
 // Ends with a barrier: out's LDS writes are visible on return.
 template <class F, class G>
 __device__ int scan_items(int n, F val, G out, int* sh) {
-  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int per = (n + kPlanThreads - 1) / kPlanThreads;
   const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
   int local = 0;
   for (int i = lo; i < hi; ++i) local += val(i);
@@ -106,7 +106,7 @@ __device__ int scan_items(int n, F val, G out, int* sh) {
 // the exclusive int2 prefix.  Returns the int2 totals.
 template <class F, class G>
 __device__ int2 scan_items2(int n, F val, G out, int* sh) {
-  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int per = (n + kPlanThreads - 1) / kPlanThreads;
   const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
   int la = 0, lb = 0;
   for (int i = lo; i < hi; ++i) {
@@ -153,16 +153,16 @@ __device__ __forceinline__ int agent_load(const int32_t* p) {
 }
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Sum of a[(b) * stride + x] over b in [b0, b1), eight independent loads in
+// Sum of a[b * stride + x] over b in [b0, b1), 16 independent loads in
 // flight per thread.
 __device__ __forceinline__ int sum_blocks(const int32_t* __restrict__ a, int64_t stride, int x, int b0, int b1) {
   int s = 0;
-  for (int b = b0; b < b1; b += 8) {
-    int v[8];
+  for (int b = b0; b < b1; b += 16) {
+    int v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = (b + u < b1) ? a[(int64_t)(b + u) * stride + x] : 0;
+    for (int u = 0; u < 16; ++u) v[u] = (b + u < b1) ? a[(int64_t)(b + u) * stride + x] : 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
+    for (int u = 0; u < 16; ++u) s += v[u];
   }
   return s;
 }
@@ -206,15 +206,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(PlanLayout L, 
 template <bool kBandLds>
 __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
   extern __shared__ int smem[];
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x;
+  constexpr int nt = kPlanThreads;
   const int W = L.W, r = L.r, E_l = L.E_l, tb = L.tb_m;
   const int HB = E_l + 2;
   const int EW = E_l * W;
   const BuildLds S = build_lds(W, E_l, L.bands_cap, kBandLds);
   int32_t* hdr = ws + L.o_hdr;
   int* c = smem + S.c;             // [E_l][W] group sizes
-  int* grp = smem + S.grp;         // [E_l][W] group offsets inside X_e
-  int* ccum = smem + S.ccum;       // [E_l][W] group offsets inside X_e's compacted rows
+  int* grow = smem + S.grow;       // [E_l][W] first layout row of every group
+  int* gcrow = smem + S.gcrow;     // [E_l][W] first compacted row of every group
   int* base = smem + S.base;       // [W][E_l] receive-buffer bases
   int* gstart = smem + S.gstart;   // [E_l*W + 1] first band of every group in S order
   int* low = smem + S.low;         // [W] pairs of owner o with an expert below this rank's
@@ -232,9 +233,10 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
   const int32_t* __restrict__ bh = ws + L.o_bh;
 
   // (a) group counts c[e][o], low[o] and bad ids per owner: one thread per
-  //     (owner, histogram column), summing the owner's blocks
+  //     (owner, histogram column), summing the owner's blocks with up to 16
+  //     loads in flight
   for (int it = tid; it < W * HB; it += nt) {
-    const int o = it / HB, x = it - o * HB;
+    const int o = fdiv(it, L.div_hb), x = it - o * HB;
     const int s = sum_blocks(bh, HB, x, L.blk_off[o], L.blk_off[o + 1]);
     if (x < E_l) c[x * W + o] = s;
     else if (x == E_l) low[o] = s;
@@ -259,49 +261,56 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
     return;
   }
 
-  // (b) layout of every expert: padded group offsets inside X_e (remote
-  //     owners ascending, then r) and compacted ones; receive-buffer bases
-  //     (owner o's pairs below global expert r*E_l + e); remote bands per
-  //     expert (rule (ii)); received rows per owner
-  for (int e = tid; e < E_l; e += nt) {
-    int run = 0, crun = 0, nb = 0;
-    for (int q = 0; q < W; ++q) {
-      const int o = (q < W - 1) ? (q < r ? q : q + 1) : r;
-      grp[e * W + o] = run;
-      ccum[e * W + o] = crun;
-      const int n = c[e * W + o];
-      run += (o == r) ? n : ((n + tb - 1) / tb) * tb;
-      crun += n;
-      if (o != r) nb += (n + tb - 1) / tb;
-    }
-    me[e] = run;
-    ce[e] = crun;
-    rb[e] = nb;
-  }
-  int rsum = 0;   // received rows from owner `tid` (wave 0 holds the owners)
-  for (int o = tid; o < W; o += nt) {
-    int run = low[o];
-    for (int e = 0; e < E_l; ++e) { base[o * E_l + e] = run; run += c[e * W + o]; }
-    rsum = run - low[o];
-  }
-  if (tid < 64) {   // W <= 64: one wavefront scans the owners
-    const int incl = wave_incl_scan(tid < W ? rsum : 0);
-    if (tid < W) obase[tid] = incl - rsum;
-    if (tid == W - 1) obase[W] = incl;
-  }
-  __syncthreads();
-  const int2 mtot = scan_items2(
-      E_l, [&](int e) { return make_int2(me[e], ce[e]); },
-      [&](int e, int2 pre) {
-        rowoff[e] = pre.x;
-        crowoff[e] = pre.y;
+  // (b) the layout.  One pair scan over the groups in (expert, owner order)
+  //     order -- remote owners ascending, then r -- gives every group's
+  //     first row in X (remote groups padded to whole bands) and its first
+  //     compacted row; one scan over (owner, expert) order gives the
+  //     receive-buffer bases (owner o's pairs below global expert r*E_l + e)
+  //     and the received rows from the owners before each owner.
+  auto owner_at = [&](int q) { return (q < W - 1) ? (q < r ? q : q + 1) : r; };
+  const int2 xtot = scan_items2(
+      EW,
+      [&](int i) {
+        const int e = fdiv(i, L.div_w), o = owner_at(i - e * W);
+        const int n = c[e * W + o];
+        return make_int2(o == r ? n : fdiv(n + tb - 1, L.div_tb) * tb, n);
+      },
+      [&](int i, int2 pre) {
+        const int e = fdiv(i, L.div_w), o = owner_at(i - e * W);
+        grow[e * W + o] = pre.x;
+        gcrow[e * W + o] = pre.y;
       },
       sh);
-  const int M = mtot.x;
-  if (tid == 0) {
-    rowoff[E_l] = M;
-    crowoff[E_l] = mtot.y;   // = rcount
+  (void)scan_items(
+      EW,
+      [&](int i) {
+        const int o = fdiv(i, L.div_el), e = i - o * E_l;
+        return c[e * W + o];
+      },
+      [&](int i, int pre) { base[i] = pre; }, sh);
+  // expert starts, sizes, remote bands; owner bases; receive bases relative
+  // to each owner
+  for (int e = tid; e < E_l; e += nt) {
+    const int q0 = owner_at(0);
+    rowoff[e] = grow[e * W + q0];
+    crowoff[e] = gcrow[e * W + q0];
+    const int end = e + 1 < E_l ? grow[(e + 1) * W + q0] : xtot.x;
+    const int cend = e + 1 < E_l ? gcrow[(e + 1) * W + q0] : xtot.y;
+    me[e] = end - rowoff[e];
+    ce[e] = cend - crowoff[e];
+    rb[e] = fdiv(me[e] - c[e * W + r], L.div_tb);   // remote groups are whole bands
   }
+  for (int o = tid; o <= W; o += nt) obase[o] = o < W ? base[o * E_l] : rcount;
+  if (tid == 0) {
+    rowoff[E_l] = xtot.x;
+    crowoff[E_l] = xtot.y;   // = rcount
+  }
+  __syncthreads();
+  for (int i = tid; i < EW; i += nt) {
+    const int o = fdiv(i, L.div_el);
+    base[i] += low[o] - obase[o];
+  }
+  const int M = xtot.x;
   // rule (ii) order: more remote bands first, ties to the lower id
   for (int e = tid; e < E_l; e += nt) {
     int rank = 0;
@@ -312,19 +321,14 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
     }
     order[rank] = e;
   }
-  __syncthreads();
 
-  // (c) hand the placers what they need -- group sizes, padded and
-  //     compacted group offsets, expert starts, owner receive bases -- with
+  // (c) hand the placers what they need -- group sizes, first layout and
+  //     compacted rows of every group, owner receive bases -- with
   //     device-scope stores, wait for them, then raise the ready word
   for (int i = tid; i < EW; i += nt) {
     agent_store(ws + L.o_c + i, c[i]);
-    agent_store(ws + L.o_grp + i, grp[i]);
-    agent_store(ws + L.o_ccum + i, ccum[i]);
-  }
-  for (int i = tid; i <= E_l; i += nt) {
-    agent_store(ws + L.o_rowoff + i, rowoff[i]);
-    agent_store(ws + L.o_crowoff + i, crowoff[i]);
+    agent_store(ws + L.o_grow + i, grow[i]);
+    agent_store(ws + L.o_gcrow + i, gcrow[i]);
   }
   for (int i = tid; i <= W; i += nt) agent_store(ws + L.o_obase + i, obase[i]);
   if (tid == 0) agent_store(hdr + H_ERROR, 0);
@@ -334,8 +338,17 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
 
   // the rest is read by the GEMMs, the consumer and the scale, all later
   // launches, and by inspection
-  for (int i = tid; i < EW; i += nt) ws[L.o_base + i] = base[i];
+  for (int i = tid; i < EW; i += nt) {
+    const int e = fdiv(i, L.div_w);
+    ws[L.o_base + i] = base[i];
+    ws[L.o_grp + i] = grow[i] - rowoff[e];     // offsets inside X_e
+    ws[L.o_ccum + i] = gcrow[i] - crowoff[e];
+  }
   for (int i = tid; i < W; i += nt) ws[L.o_low + i] = low[i];
+  for (int i = tid; i <= E_l; i += nt) {
+    ws[L.o_rowoff + i] = rowoff[i];
+    ws[L.o_crowoff + i] = crowoff[i];
+  }
   for (int i = tid; i < E_l; i += nt) {
     ws[L.o_me + i] = me[i];
     ws[L.o_rb + i] = rb[i];
@@ -349,8 +362,9 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
   const int NG = E_l * W;
   auto group_eo = [&](int gi, int& e, int& o) {
     if (gi < NGR) {
-      e = order[gi / (W - 1)];
-      const int q = gi % (W - 1);
+      const int qe = fdiv(gi, L.div_wm1);
+      e = order[qe];
+      const int q = gi - qe * (W - 1);
       o = q < r ? q : q + 1;
     } else {
       e = gi - NGR;
@@ -362,7 +376,7 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
       [&](int gi) {
         int e, o;
         group_eo(gi, e, o);
-        return (c[e * W + o] + tb - 1) / tb;
+        return fdiv(c[e * W + o] + tb - 1, L.div_tb);
       },
       [&](int gi, int pre) { gstart[gi] = pre; }, sh);
   if (B > L.bands_cap) {
@@ -391,61 +405,64 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
     bg = t; vv = t + nb; nx = t + 2 * nb; ja = t + 3 * nb; jb = t + 4 * nb; on = t + 5 * nb;
   }
 
-  // (e) bands in S order, one thread per band
+  // (e) bands in S order, one thread per band.  Each band also decides
+  //     whether it starts a segment (§5.2): the first and the last remote
+  //     band alone; otherwise runs of <= mgb bands that restart at every
+  //     group boundary (so a segment never crosses a group and is read off
+  //     the band's own group).  A starting band keeps its segment's bands
+  //     and rows for the scan below, which numbers the segments and places
+  //     their copy units; the band tables nx, ja, jb, on hold the segment,
+  //     source row, receive offset and owner until the down tiles reuse
+  //     them.
   int32_t* bexp = ws + L.o_bexp;
   int32_t* bdst = ws + L.o_bdst;
   int32_t* bsrc = ws + L.o_bsrc;
   int32_t* bdoff = ws + L.o_bdoff;
   int32_t* bval = ws + L.o_bval;
   int32_t* bcrow = ws + L.o_bcrow;
+  const int mgb = L.mgb;
   __syncthreads();   // gstart complete
   for (int b = tid; b < B; b += nt) {
     const int gi = upper_index(gstart, NG, b);   // the non-empty group holding band b
     int e, o;
     group_eo(gi, e, o);
-    const int q = b - gstart[gi];
+    const int gs = gstart[gi];
+    const int ge = gstart[gi + 1];
+    const int q = b - gs;
     const int n = c[e * W + o];
     const int v = min(tb, n - q * tb);
+    const int src_row = grow[e * W + o] + q * tb;
+    const int dst_off = base[o * E_l + e] + q * tb;
     bg[b] = gi;
     vv[b] = v;
     bexp[b] = e;
     bdst[b] = o;
-    bsrc[b] = rowoff[e] + grp[e * W + o] + q * tb;
-    bdoff[b] = base[o * E_l + e] + q * tb;
+    bsrc[b] = src_row;
+    bdoff[b] = dst_off;
     bval[b] = v;
-    bcrow[b] = crowoff[e] + ccum[e * W + o] + q * tb;
-  }
-  __syncthreads();
-
-  // (f) segments (§5.2): the first and the last remote band alone;
-  //     otherwise runs of <= mgb bands that restart at every group
-  //     boundary.  Every band decides whether it starts a segment and, if
-  //     so, the segment's bands, rows and copy units (a segment never
-  //     crosses a group, so they are read off the group); one pair scan
-  //     over the bands numbers the segments and places their copy units.
-  const int mgb = L.mgb;
-  const int64_t row_bytes = (int64_t)L.d * 2;
-  auto units_of = [&](int rows) { return (int)((rows * row_bytes + kCopyChunk - 1) / kCopyChunk); };
-  auto starts = [&](int b, int gi, int gs) {
-    if (b == gs) return true;
+    bcrow[b] = gcrow[e * W + o] + q * tb;
+    // segment start and the first band after the segment
+    bool st;
+    int nxt;
     if (gi < NGR) {
-      const int run0 = gs > 1 ? gs : 1;
-      return b == n_remote - 1 || ((b - run0) % mgb) == 0;
+      const int off = b - (gs > 1 ? gs : 1);   // -1 only for band 0, which is alone
+      const int m = off >= 0 ? off - fdiv(off, L.div_mgb) * mgb : 0;
+      st = q == 0 || b == n_remote - 1 || (off >= 0 && m == 0);
+      nxt = off >= 0 ? b + mgb - m : b + 1;
+      if (b < n_remote - 1) nxt = min(nxt, n_remote - 1);
+      else nxt = b + 1;
+    } else {
+      const int m = q - fdiv(q, L.div_mgb) * mgb;
+      st = m == 0;
+      nxt = b + mgb - m;
     }
-    return ((b - gs) % mgb) == 0;
-  };
-  auto seg_at = [&](int b, int& gi, int& nb, int& rows) {
-    gi = bg[b];
-    const int gs = gstart[gi];
-    if (!starts(b, gi, gs)) return false;
-    const int ge = gstart[gi + 1];
-    nb = 1;
-    while (b + nb < ge && !starts(b + nb, gi, gs)) ++nb;
-    int e, o;
-    group_eo(gi, e, o);
-    rows = min(nb * tb, c[e * W + o] - (b - gs) * tb);
-    return true;
-  };
+    nxt = min(nxt, ge);
+    const int nb = nxt - b;
+    nx[b] = st ? ((min(nb * tb, n - q * tb) << 8) | nb) : 0;   // rows << 8 | bands (<= 64)
+    ja[b] = src_row;
+    jb[b] = dst_off;
+    on[b] = o;
+  }
   int32_t* sfirst = ws + L.o_sfirst;
   int32_t* snb = ws + L.o_snb;
   int32_t* sdst = ws + L.o_sdst;
@@ -453,28 +470,26 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
   int32_t* ssrc = ws + L.o_ssrc;
   int32_t* srows = ws + L.o_srows;
   int32_t* sunit = ws + L.o_sunit;
+  const int64_t row_bytes = (int64_t)L.d * 2;
+  auto units_of = [&](int rows) { return (int)((rows * row_bytes + kCopyChunk - 1) / kCopyChunk); };
   if (tid == 0) misc[0] = -1;
   __syncthreads();
   const int2 stot = scan_items2(
       B,
       [&](int b) {
-        int gi, nb, rows;
-        if (!seg_at(b, gi, nb, rows)) return make_int2(0, 0);
-        return make_int2(1, units_of(rows));
+        const int sg = nx[b];
+        return sg ? make_int2(1, units_of(sg >> 8)) : make_int2(0, 0);
       },
       [&](int b, int2 pre) {
-        int gi, nb, rows;
-        if (!seg_at(b, gi, nb, rows)) return;
-        int e, o;
-        group_eo(gi, e, o);
-        const int q = b - gstart[gi];
+        const int sg = nx[b];
+        if (!sg) return;
         const int i = pre.x;
         sfirst[i] = b;
-        snb[i] = nb;
-        sdst[i] = o;
-        sdoff[i] = base[o * E_l + e] + q * tb;
-        ssrc[i] = rowoff[e] + grp[e * W + o] + q * tb;
-        srows[i] = rows;
+        snb[i] = sg & 255;
+        sdst[i] = on[b];
+        sdoff[i] = jb[b];
+        ssrc[i] = ja[b];
+        srows[i] = sg >> 8;
         sunit[i] = pre.y;
         if (b == n_remote) misc[0] = i;   // the first local band starts a segment
       },
@@ -516,7 +531,7 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
   __syncthreads();
   auto run_of = [&](int gi, int& rs, int& re) {
     if (gi < NGR) {
-      const int q = gi / (W - 1);
+      const int q = fdiv(gi, L.div_wm1);
       rs = gstart[q * (W - 1)];
       re = gstart[(q + 1) * (W - 1)];
     } else {
@@ -537,31 +552,33 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
     ja[b] = lo < re ? lo : -1;
     on[b] = (b == rs);
   }
+  if (tid == 0) misc[2] = 0;   // round 0's word (see below)
   __syncthreads();
-  for (;;) {
-    for (int b = tid; b < B; b += nt)
-      if (on[b] && ja[b] >= 0) on[ja[b]] = 1;   // only first bands are ever marked
-    __syncthreads();
+  // One pass per round marks with the current jumps and doubles them into
+  // the other buffer.  A mark another thread sees early in the same pass is
+  // a first band all the same, so the pass needs no barrier inside.  Round
+  // k's "a jump is left" word is misc[2 + k mod 3]: it was cleared during
+  // round k - 1, after every thread had read it as round k - 3's word.
+  for (int k = 0;; k = (k == 2 ? 0 : k + 1)) {
+    if (tid == 0) misc[2 + (k == 2 ? 0 : k + 1)] = 0;
     int more = 0;
     for (int b = tid; b < B; b += nt) {
       const int j = ja[b];
+      if (j >= 0 && on[b]) on[j] = 1;
       const int jj = j >= 0 ? ja[j] : -1;
       jb[b] = jj;
       more |= jj >= 0;
     }
+    if (more) misc[2 + k] = 1;
     int* t = ja; ja = jb; jb = t;
-    if (!__syncthreads_or(more)) break;
+    __syncthreads();
+    if (!misc[2 + k]) break;
   }
-  // a last marking pass with the final jumps
-  for (int b = tid; b < B; b += nt)
-    if (on[b] && ja[b] >= 0) on[ja[b]] = 1;
-  __syncthreads();
   int32_t* dt_row = ws + L.o_dnt_row;
   int32_t* dt_exp = ws + L.o_dnt_exp;
   int32_t* dt_band = ws + L.o_dnt_band;
   int32_t* dt_nb = ws + L.o_dnt_nb;
   if (tid == 0) misc[1] = -1;
-  __syncthreads();
   const int NDT = scan_items(
       B, [&](int b) { return on[b]; },
       [&](int b, int pre) {
@@ -569,7 +586,7 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
         if (!on[b]) return;
         int e, o;
         group_eo(bg[b], e, o);
-        dt_row[pre] = rowoff[e] + grp[e * W + o] + (b - gstart[bg[b]]) * tb;
+        dt_row[pre] = grow[e * W + o] + (b - gstart[bg[b]]) * tb;
         dt_exp[pre] = e;
         dt_band[pre] = b;
         dt_nb[pre] = nx[b] - b;
@@ -633,7 +650,8 @@ constexpr int64_t kPlanWaitTicks = 200000000;
 __device__ void place_pairs(const PlanLayout& L, const int32_t* __restrict__ topk, int32_t* __restrict__ ws,
                             int b) {
   extern __shared__ int smem[];
-  const int tid = threadIdx.x, nt = blockDim.x, w = tid >> 6;
+  const int tid = threadIdx.x, w = tid >> 6;
+  constexpr int nt = kPlanThreads;
   const int o = owner_of_block(L, b);
   const int p0 = L.pair_off[o] + (b - L.blk_off[o]) * kPairsPerBlock;
   const int p1 = min(p0 + kPairsPerBlock, L.pair_off[o + 1]);
@@ -696,13 +714,11 @@ __device__ void place_pairs(const PlanLayout& L, const int32_t* __restrict__ top
   if (misc[0] != 0) return;
   // (c) the builder's tables for this owner's groups
   const int32_t* gc = ws + L.o_c;
-  const int32_t* ggrp = ws + L.o_grp;
-  const int32_t* gccum = ws + L.o_ccum;
-  const int32_t* growoff = ws + L.o_rowoff;
-  const int32_t* gcrowoff = ws + L.o_crowoff;
+  const int32_t* grow = ws + L.o_grow;
+  const int32_t* gcrow = ws + L.o_gcrow;
   for (int e = tid; e < E_l; e += nt) {
-    srow[e] = agent_load(growoff + e) + agent_load(ggrp + e * W + o);
-    scrow[e] = agent_load(gcrowoff + e) + agent_load(gccum + e * W + o);
+    srow[e] = agent_load(grow + e * W + o);
+    scrow[e] = agent_load(gcrow + e * W + o);
   }
   const int recv_base = agent_load(ws + L.o_obase + o) + before;
   int32_t* src = ws + L.o_src;
@@ -712,11 +728,11 @@ __device__ void place_pairs(const PlanLayout& L, const int32_t* __restrict__ top
     const int NGR = E_l * (W - 1);
     const int tb = L.tb_m;
     for (int gi = b; gi < NGR; gi += L.NB) {
-      const int e = gi / (W - 1), q = gi % (W - 1);
+      const int e = fdiv(gi, L.div_wm1), q = gi - e * (W - 1);
       const int og = q < L.r ? q : q + 1;
       const int n = agent_load(gc + e * W + og);
-      const int st = agent_load(growoff + e) + agent_load(ggrp + e * W + og) + n;
-      const int ct = ((n + tb - 1) / tb) * tb - n;
+      const int st = agent_load(grow + e * W + og) + n;
+      const int ct = fdiv(n + tb - 1, L.div_tb) * tb - n;
       for (int x = tid; x < ct; x += nt) src[st + x] = -1;
     }
   }
