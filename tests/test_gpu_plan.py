@@ -135,3 +135,41 @@ def test_gemm_tile_tables(name):
         for q in range(nb):
             assert int(pl.bands["src_row"][f0 + q]) == row0 + q * pl.tb_m
             assert int(pl.bands["expert"][f0 + q]) == e
+
+
+def test_plan_with_band_tables_in_the_workspace():
+    """A plan with 4070 bands (bands_cap 4247): the builder's six per-band
+    tables (6 x 4248 words, 102 KB) exceed the 64 KB of LDS it may use, so it
+    keeps them in the workspace instead.  Metadata, compacted-row tables and
+    GEMM tile tables bit-exact as on the other workloads."""
+    import moe_expert_tile_amd as m
+    import synth
+    from oracle import plan as OP
+    W, E_l, k, tb, mgb = 16, 8, 8, 32, 2
+    tokens = [16000] * W
+    cfg = synth.MoEConfig("many_bands", W, W * E_l, tuple(tokens), 256, 256, k, tb, seed=5, mgb=mgb, rank=0)
+    ids = synth.random_routing_case(np.random.default_rng(5), W, E_l, k, tokens)
+    pl = OP.build_plan(ids, tokens, 0, E_l, tb, mgb)
+    rows_cap = pl.R + E_l * (W - 1) * (tb - 1)
+    assert rows_cap // tb + E_l * W == 4247 and pl.n_bands == 4070
+    say(f"[plan] many_bands R={pl.R} M={pl.M} bands={pl.n_bands}")
+    share = m.RankShare(shape_of(cfg, pl.R))
+    xr = torch.zeros((pl.R, cfg.d), dtype=torch.bfloat16, device="cuda")
+    share.plan(torch.from_numpy(ids).cuda(), xr, materialize=False)
+    assert share.status() == m.MOE_OK
+    hdr = share.header()
+    assert hdr["M"] == pl.M and hdr["bands"] == pl.n_bands and hdr["remote_bands"] == pl.n_remote
+    assert hdr["segments"] == pl.segs["first_band"].shape[0] and hdr["remote_segments"] == pl.n_remote_segs
+    got = plan_arrays(share, hdr)
+    for key, v in expected_plan(pl).items():
+        assert np.array_equal(np.asarray(got[key]).astype(np.int64), np.asarray(v).astype(np.int64)), key
+    cx = expected_compacted(pl)
+    sizes = {"crow_off": E_l + 1, "grp_crow": E_l * W, "band_crow": pl.n_bands, "cmp_row": pl.R, "cmp_src": pl.R}
+    for key, v in cx.items():
+        assert np.array_equal(share.array(key, sizes[key]).astype(np.int64), np.asarray(v, dtype=np.int64).reshape(-1)), key
+    gu_row, gu_exp, dn = expected_tiles(pl)
+    assert hdr["gateup_row_tiles"] == len(gu_row) and hdr["down_row_tiles"] == len(dn)
+    assert share.array("gu_tile_row", len(gu_row)).tolist() == gu_row
+    got = list(zip(*(share.array(key, len(dn)).tolist() for key in
+                     ["dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands"])))
+    assert got == dn
