@@ -83,7 +83,11 @@ typedef struct moe_sizes {
  *   [12..13] uint64: 100 MHz wall clock when the last producer workgroup of
  *            the down GEMM ended (raised by every call, never reset)
  *   [14..15] uint64: the same for the last consumer workgroup
- *   [16] down row tiles of remote bands (they precede the local ones) */
+ *   [16] down row tiles of remote bands (they precede the local ones)
+ *   [18..19] copy-unit claims handed out and producers started in the
+ *            overlapped down-GEMM launch (reset by the gate/up launch)
+ *   [20] planner: raised by the plan builder once the group tables the pair
+ *        placers need are in memory, cleared by the counting launch */
 typedef struct moe_plan_view {
   size_t hdr;
   size_t c;          /* [E_l][W] rows of local expert e from owner o */
@@ -98,9 +102,11 @@ typedef struct moe_plan_view {
   size_t src_index;  /* [rows_cap] received row of each layout row, -1 for padding (first M valid) */
   size_t pos;        /* [T_r][k] row of the rank's own receive buffer holding slot (t, j) */
   /* GEMM row tiles (implementation detail, for tests): gate/up tiles of 256
-   * rows of one X_e, experts in rule (ii) order; down tiles of up to
-   * 256 / tb_M row-contiguous bands of one expert, in schedule order S
-   * (present when tb_M divides 256; first band and band count per tile) */
+   * compacted rows of one X_e, experts in rule (ii) order (first compacted
+   * row and expert per tile); down tiles of whole consecutive bands of one
+   * run of S -- the remote bands of one expert, or its local bands -- packed
+   * greedily while their real rows fit 256 (at most 64 bands), in schedule
+   * order S (layout row, expert, first band and band count per tile) */
   size_t gu_tile_row, gu_tile_expert;                              /* [hdr[10]] */
   size_t dn_tile_row, dn_tile_expert, dn_tile_band, dn_tile_nbands; /* [hdr[11]] */
   /* uint64 [sk_counters_count]: epoch-tagged tile counters of the GEMMs'
@@ -215,7 +221,10 @@ int moe_plan(const moe_shape* shape, const int32_t* topk_ids, const uint16_t* x_
  *              (gathered rows, see moe_combine_opts).
  *   w_gate_up  device bf16 [E_l, 2f, d]: rows 0..f-1 gate, f..2f-1 up (K-contiguous).
  *   w_down     device bf16 [E_l, d, f] (K-contiguous).
- *   h, y       device bf16 [rows_cap, f] and [rows_cap, d]; scratch written here.
+ *   h, y       device bf16 [rows_cap, f] and [rows_cap, d]; scratch written here:
+ *              h holds the R real rows in compacted order (moe_plan_view), y
+ *              every layout row of [0, M), zeros in the padding rows of
+ *              remote bands; padding rows are never multiplied.
  *   flags      device uint32 [flags_count]; zero them once at allocation, then
  *              pass a new epoch (never 0, increasing) on every call: no reset.
  *              An epoch value may be used again only after the flags and the
