@@ -38,6 +38,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
+// The plan's tables, written by the planner's launches and only read here:
+// loads through the constant address space with a wave-uniform index become
+// scalar loads, which the vector memory counter does not track, so the tile
+// setup never waits for the previous tile's output stores.
+typedef const int32_t __attribute__((address_space(4))) ctab_t;
 
 // Tile shapes (compile-time; the defaults are the measured best on MI355X).
 #ifndef MOE_XCD_ROWS
@@ -411,6 +416,44 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     }
   }
 
+  // Down GEMM: a tile is published -- its bands' flags set, or its bands
+  // counted on their groups' ready words -- once its output stores are
+  // acknowledged by every wave.  The wait is not at the end of the tile: the
+  // next tile's prologue first issues its loads, then waits for the stores
+  // alone (the vector memory counter retires in issue order), so the
+  // stores drain under the next tile's loads instead of stalling the waves.
+  // The last tile is published after the loop.
+  int pend_b0 = 0, pend_nb = 0, pend_nt = 0;
+  auto publish = [&](int b0, int nb, int ntile) __attribute__((always_inline)) {
+    if (g.cc.signal == 0) {
+      // one flag per band of the tile (a band has n_nt flags, one per
+      // column tile)
+      if (tid < nb)
+        __hip_atomic_store(g.flags + (int64_t)(b0 + tid) * n_nt + ntile, g.epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else if (tid == 0) {
+      // group-batched: the tile's bands, run by run of one (expert,
+      // destination) group, are counted on the group's epoch-tagged ready
+      // word; the group is ready once every band of it has been counted for
+      // every column tile
+      uint64_t* gready = g.sc.gready;
+      int b = b0;
+      while (b < b0 + nb) {
+        const int gi = g.ws[L.o_bexp + b] * L.W + g.ws[L.o_bdst + b];
+        int k = 1;
+        while (b + k < b0 + nb && g.ws[L.o_bexp + b + k] * L.W + g.ws[L.o_bdst + b + k] == gi) ++k;
+        uint64_t old = __hip_atomic_load(gready + gi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (;;) {
+          const uint32_t cnt = ((uint32_t)(old >> 32) == g.epoch ? (uint32_t)old : 0u) + (uint32_t)k;
+          const uint64_t nv = ((uint64_t)g.epoch << 32) | cnt;
+          if (__hip_atomic_compare_exchange_strong(gready + gi, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT))
+            break;
+        }
+        b += k;
+      }
+    }
+  };
   int t_dp = slot, piece = 0, items = 0;
   for (;;) {
     // next work item: a whole tile, or a piece [kb, ke) of a stream-K tile
@@ -446,12 +489,13 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       e = g.ws[L.o_gumt_exp + mt];
       lim = g.ws[L.o_crowoff + e + 1];
     } else {
-      row0 = g.ws[L.o_dnt_row + mt];
-      e = g.ws[L.o_dnt_exp + mt];
-      band0 = g.ws[L.o_dnt_band + mt];
-      nbt = g.ws[L.o_dnt_nb + mt];
-      crow0 = g.ws[L.o_bcrow + band0];
-      nrows = g.ws[L.o_bcrow + band0 + nbt - 1] + g.ws[L.o_bval + band0 + nbt - 1] - crow0;
+      const ctab_t* tab = (const ctab_t*)g.ws;
+      row0 = tab[L.o_dnt_row + mt];
+      e = tab[L.o_dnt_exp + mt];
+      band0 = __builtin_amdgcn_readfirstlane(tab[L.o_dnt_band + mt]);
+      nbt = __builtin_amdgcn_readfirstlane(tab[L.o_dnt_nb + mt]);
+      crow0 = tab[L.o_bcrow + band0];
+      nrows = tab[L.o_bcrow + band0 + nbt - 1] + tab[L.o_bval + band0 + nbt - 1] - crow0;
       lim = row0 + nrows;
     }
     // per-tile values are wave-uniform; say so, so that the buffer
@@ -470,7 +514,8 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     // consecutive rows of the unpadded local group, at both ends.
     int ldst0 = -1;
     if constexpr (FLAGS) {
-      if (g.ws[L.o_bdst + band0] == L.r) ldst0 = g.ws[L.o_bdoff + band0];
+      const ctab_t* tab = (const ctab_t*)g.ws;
+      if (tab[L.o_bdst + band0] == L.r) ldst0 = tab[L.o_bdoff + band0];
       ldst0 = __builtin_amdgcn_readfirstlane(ldst0);
     }
     const bool empty = row0 >= row_end;
@@ -508,7 +553,12 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       a_rsrc = make_rsrc(g.a + (int64_t)crow0 * g.K, (int64_t)nrows * g.K * 2);
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i) {
-        const int r = (wave + i * C::NW) * C::RPB + ld_row;
+        // recomputed per tile (an empty asm hides that it is the same every
+        // time): hoisted out of the tile loop these offsets were spilled, and
+        // reloading them from scratch would wait for the previous tile's
+        // output stores, which the next prologue is meant to overlap
+        int r = (wave + i * C::NW) * C::RPB + ld_row;
+        asm volatile("" : "+v"(r));
         a_off[i] = r < nrows ? 2u * ((uint32_t)r * (uint32_t)g.K + (uint32_t)(C::swz(r, ld_phys) * 8))
                              : 0x80000000u;
       }
@@ -536,9 +586,11 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int KTt = empty ? 0 : ke - kb;   // K steps of this work item
-    // every wave is done with the previous item's LDS stages before the
-    // prologue below refills them
-    __syncthreads();
+    // every wave is done with the previous item's LDS stages (and staged
+    // output tile) before the prologue below refills them; outstanding
+    // output stores are not waited for here
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    __builtin_amdgcn_s_barrier();
     // Stage k of A lives in A buffer k % SA, of B in B buffer k % SB.  Each
     // K step issues the shallow ring's next stage first, then the deep
     // ring's, so at a step's barrier only the deep ring's newest stage may
@@ -557,6 +609,18 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     if (KTt > 1) {
       if constexpr (C::SA == 3) issue_a(1);
       if constexpr (C::SB == 3) issue_b(1);
+    }
+    if constexpr (FLAGS) {
+      if (pend_nb > 0) {
+        // the previous tile's stores went out before the loads just issued:
+        // wait for those stores alone, in every wave, then publish the tile
+        static_assert(C::A_LOADS + C::B_LOADS <= 63, "vector memory counter range");
+        if (KTt > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(C::A_LOADS + C::B_LOADS));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        __builtin_amdgcn_s_barrier();
+        publish(pend_b0, pend_nb, pend_nt);
+        pend_nb = 0;
+      }
     }
 
     // One K step.  The barrier waits for stage kt (every later stage but
@@ -891,8 +955,9 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       // at device scope (sc1: written through this XCD's L2 to the memory
       // side, the point where all XCDs' agent-scope loads meet; the same
       // instruction form as a relaxed agent-scope atomic store), and each
-      // wave waits until its stores are acknowledged; after the barrier one
-      // lane sets the flags with relaxed agent-scope stores.  So the data is
+      // wave waits until its stores are acknowledged (at the next tile's
+      // prologue, see `publish`); after a barrier the flags are set with
+      // relaxed agent-scope stores.  So the data is
       // visible to every XCD before any flag is, without the L2 write-back an
       // agent-scope release fence would add: that write-back (buffer_wbl2)
       // only matters for ordinary write-back stores, and walking the L2 once
@@ -902,41 +967,21 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       // loads that do not return lines this XCD cached earlier; it issues no
       // acquire fence and no L2 invalidate.
       static_assert((MOE_STORE_AUX & kDeviceScope) != 0, "flag publication needs device-scope (sc1) output stores");
-      wait_vm0();
       if constexpr (FLAGS) {
-        __syncthreads();
-        if (g.cc.signal == 0) {
-          // one flag per band of the tile (a band has n_nt flags, one per
-          // column tile)
-          if (tid < nbt)
-            __hip_atomic_store(g.flags + (int64_t)(band0 + tid) * n_nt + nt, g.epoch, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        } else if (tid == 0) {
-          // group-batched: the tile's bands, run by run of one (expert,
-          // destination) group, are counted on the group's epoch-tagged
-          // ready word; the group is ready once every band of it has been
-          // counted for every column tile
-          uint64_t* gready = g.sc.gready;
-          int b = band0;
-          while (b < band0 + nbt) {
-            const int gi = g.ws[L.o_bexp + b] * L.W + g.ws[L.o_bdst + b];
-            int k = 1;
-            while (b + k < band0 + nbt && g.ws[L.o_bexp + b + k] * L.W + g.ws[L.o_bdst + b + k] == gi) ++k;
-            uint64_t old = __hip_atomic_load(gready + gi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (;;) {
-              const uint32_t cnt = ((uint32_t)(old >> 32) == g.epoch ? (uint32_t)old : 0u) + (uint32_t)k;
-              const uint64_t nv = ((uint64_t)g.epoch << 32) | cnt;
-              if (__hip_atomic_compare_exchange_strong(gready + gi, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT))
-                break;
-            }
-            b += k;
-          }
-        }
+        pend_b0 = band0;   // published once the stores above are acknowledged
+        pend_nb = nbt;
+        pend_nt = nt;
+      } else {
+        wait_vm0();
       }
     }
   }
   if constexpr (FLAGS) {
+    if (pend_nb > 0) {   // the last tile: its stores are the last memory operations
+      wait_vm0();
+      __builtin_amdgcn_s_barrier();
+      publish(pend_b0, pend_nb, pend_nt);
+    }
     if (tid == 0) stamp_max(hdr, H_T_PROD_END);
     if (overlapped && items > 0) {
       // out of tiles: help copy the remaining remote segments, but only once
