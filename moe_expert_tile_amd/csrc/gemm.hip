@@ -711,7 +711,18 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
         default: run_k(std::integral_constant<int, 0>{}); break;
       }
     } else {
-      run_k(std::integral_constant<int, C::FM>{});
+      // gate/up: the same over the tile's compacted rows (the last tile of
+      // an expert is partial).  A SIMD holds waves wave_m and wave_m + 2, so
+      // a tile of at most 128 rows halves the busiest SIMD's MFMA time.
+      const int rows_t = min(C::BM, row_end - row0);
+      int fe = (rows_t + 31) / 32 - wave_m * C::FM;
+      fe = __builtin_amdgcn_readfirstlane(max(0, min(C::FM, fe)));
+      static_assert(C::FM == 2, "one K-loop body per block count");
+      switch (fe) {
+        case 2: run_k(std::integral_constant<int, 2>{}); break;
+        case 1: run_k(std::integral_constant<int, 1>{}); break;
+        default: run_k(std::integral_constant<int, 0>{}); break;
+      }
     }
 
     if (sk_j >= 0) {
