@@ -173,3 +173,42 @@ def test_plan_with_band_tables_in_the_workspace():
     got = list(zip(*(share.array(key, len(dn)).tolist() for key in
                      ["dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands"])))
     assert got == dn
+
+
+@pytest.mark.parametrize("W,E_l,k,tokens_per_owner,tb", [
+    (4, 256, 8, 1500, 64),    # E_l * W = 1024, the largest group table
+    (64, 16, 4, 200, 32),     # the largest world: 64 owners, one wavefront of them
+])
+def test_plan_at_the_shape_limits(W, E_l, k, tokens_per_owner, tb):
+    """Plan metadata, compacted tables and tile tables bit-exact at the
+    limits the boundary accepts (W <= 64, W * E_l <= 1024)."""
+    import moe_expert_tile_amd as m
+    import synth
+    from oracle import plan as OP
+    tokens = [tokens_per_owner + 7 * o for o in range(W)]
+    rank = W - 1
+    cfg = synth.MoEConfig("limits", W, W * E_l, tuple(tokens), 256, 256, k, tb, seed=11, mgb=2, rank=rank)
+    ids = synth.random_routing_case(np.random.default_rng(11), W, E_l, k, tokens)
+    pl = OP.build_plan(ids, tokens, rank, E_l, tb, 2)
+    say(f"[plan] limits W={W} E_l={E_l} R={pl.R} M={pl.M} bands={pl.n_bands}")
+    share = m.RankShare(shape_of(cfg, pl.R))
+    xr = torch.zeros((max(pl.R, 1), cfg.d), dtype=torch.bfloat16, device="cuda")
+    share.plan(torch.from_numpy(ids).cuda(), xr, materialize=False)
+    assert share.status() == m.MOE_OK
+    hdr = share.header()
+    assert hdr["M"] == pl.M and hdr["bands"] == pl.n_bands and hdr["remote_bands"] == pl.n_remote
+    assert hdr["segments"] == pl.segs["first_band"].shape[0] and hdr["remote_segments"] == pl.n_remote_segs
+    got = plan_arrays(share, hdr)
+    for key, v in expected_plan(pl).items():
+        assert np.array_equal(np.asarray(got[key]).astype(np.int64), np.asarray(v).astype(np.int64)), key
+    cx = expected_compacted(pl)
+    sizes = {"crow_off": E_l + 1, "grp_crow": E_l * W, "band_crow": pl.n_bands, "cmp_row": pl.R, "cmp_src": pl.R}
+    for key, v in cx.items():
+        assert np.array_equal(share.array(key, sizes[key]).astype(np.int64), np.asarray(v, dtype=np.int64).reshape(-1)), key
+    gu_row, gu_exp, dn = expected_tiles(pl)
+    assert hdr["gateup_row_tiles"] == len(gu_row) and hdr["down_row_tiles"] == len(dn)
+    assert share.array("gu_tile_row", len(gu_row)).tolist() == gu_row
+    assert share.array("gu_tile_expert", len(gu_row)).tolist() == gu_exp
+    got = list(zip(*(share.array(key, len(dn)).tolist() for key in
+                     ["dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands"])))
+    assert got == dn
