@@ -68,7 +68,7 @@ typedef struct moe_sizes {
   int64_t rows_cap;         /* rows to allocate for x_layout [rows_cap, d], h [rows_cap, f], y [rows_cap, d]:
                                R + E_l*(W-1)*(tb_M-1), the padding bound of §4.3 per local expert */
   int64_t bands_cap;        /* upper bound on row bands: floor(rows_cap / tb_M) + E_l*W */
-  int64_t flags_count;      /* uint32 tile flags for moe_expert_combine: bands_cap * tiles per band */
+  int64_t flags_count;      /* uint32 tile flags for moe_expert_combine: 2 * bands_cap * tiles per band */
   int64_t recv_rows_self;   /* T_r * k: rows of the rank's own receive buffer (input of moe_scale) */
 } moe_sizes;
 
@@ -77,13 +77,13 @@ typedef struct moe_sizes {
  *   [0] error (moe_status of the last device-detected error, 0 if none)
  *   [1] M  total layout rows          [2] B  bands        [3] remote bands
  *   [4] segments                      [5] remote segments
- *   [6] gate/up tiles                 [7] down tile flags used (B * tiles per band)
+ *   [6] gate/up tiles                 [7] down tile flags used (2 * B * tiles per band)
  *   [8] consumer copy units           [9] received rows counted from the routing
  *   [10] gate/up row tiles            [11] down row tiles
  *   [12..13] uint64: 100 MHz wall clock when the last producer workgroup of
  *            the down GEMM ended (raised by every call, never reset)
  *   [14..15] uint64: the same for the last consumer workgroup
- *   [16] down row tiles of remote bands (they precede the local ones)
+ *   [16] down row tiles holding remote rows (they precede the others)
  *   [18..19] copy-unit claims handed out and producers started in the
  *            overlapped down-GEMM launch (reset by the gate/up launch)
  *   [20] planner: raised by the plan builder once the group tables the pair
@@ -101,14 +101,15 @@ typedef struct moe_plan_view {
   size_t seg_first, seg_nbands, seg_dst, seg_dst_off, seg_src_row, seg_rows, seg_unit; /* [segments] (+1 for seg_unit) */
   size_t src_index;  /* [rows_cap] received row of each layout row, -1 for padding (first M valid) */
   size_t pos;        /* [T_r][k] row of the rank's own receive buffer holding slot (t, j) */
-  /* GEMM row tiles (implementation detail, for tests): gate/up tiles of 256
-   * compacted rows of one X_e, experts in rule (ii) order (first compacted
-   * row and expert per tile); down tiles of whole consecutive bands of one
-   * run of S -- the remote bands of one expert, or its local bands -- packed
-   * greedily while their real rows fit 256 (at most 64 bands), in schedule
-   * order S (layout row, expert, first band and band count per tile) */
-  size_t gu_tile_row, gu_tile_expert;                              /* [hdr[10]] */
-  size_t dn_tile_row, dn_tile_expert, dn_tile_band, dn_tile_nbands; /* [hdr[11]] */
+  /* GEMM row tiles (implementation detail, for tests), as first compacted
+   * row and expert per tile.  Gate/up: X_e's compacted rows cut into pieces
+   * of 256, experts in rule (ii) order.  Down: the same pieces, those that
+   * hold remote rows first (experts in rule (ii) order), then those of local
+   * rows alone (experts ascending); a piece may end inside a band.
+   * grp_band [E_l][W]: first band of group (e, o) in S. */
+  size_t gu_tile_row, gu_tile_expert;   /* [hdr[10]] */
+  size_t dn_tile_row, dn_tile_expert;   /* [hdr[11]] */
+  size_t grp_band;
   /* uint64 [sk_counters_count]: epoch-tagged tile counters of the GEMMs'
    * K-split tails; zero them (with the flags) before an epoch is reused */
   size_t sk_counters, sk_counters_count;
@@ -156,11 +157,12 @@ typedef struct moe_combine_opts {
                                R*d*2 < 2^31 bytes; may be NULL when R = 0.  Ignored when x_layout is
                                given. */
   int32_t signal;           /* how the down GEMM tells the consumer that rows are ready:
-                               MOE_SIGNAL_TILE (0): a flag per band and column tile, set to `epoch`
-                               by the tile that computed it (the consumer polls every flag of a
-                               segment); MOE_SIGNAL_GROUP (1): one ready counter per (expert,
-                               destination) group, raised by every tile by its bands of the group
-                               and tagged with `epoch` (the consumer polls one word per segment; a
+                               MOE_SIGNAL_TILE (0): two flags per band and column tile (the band's
+                               head and tail), set to `epoch` by the tile that computed them (the
+                               consumer polls every flag of a segment); MOE_SIGNAL_GROUP (1): one
+                               ready counter per (expert, destination) group, raised by every tile by
+                               the band heads and tails of the group it holds and tagged with
+                               `epoch` (the consumer polls one word per segment; a
                                segment waits for its whole group).  COPY_ONLY must use the mode
                                the compute call used; COPY_ROWS needs MOE_SIGNAL_TILE */
   int32_t pad;              /* zero */
@@ -210,10 +212,12 @@ int moe_plan(const moe_shape* shape, const int32_t* topk_ids, const uint16_t* x_
  * (fp32 accumulation, h rounded once to bf16).  The down GEMM takes its tiles
  * in schedule order (workgroup i takes tiles i, i+g, ...; §5.1), writes
  * y = h W_down^T (bf16) and, in its epilogue, publishes the tile: its rows
- * are stored at device scope and acknowledged before flags[tile] = epoch is
- * set, so they are visible on every XCD first.  The consumer waits (bounded)
- * until every tile of a remote segment is flagged, reads the rows at device
- * scope and copies the segment's valid rows to
+ * are stored at device scope and acknowledged before the tile's flags are
+ * set to epoch, so they are visible on every XCD first.  Each band has two
+ * flags per column tile, one for its head and one for its tail, set by the
+ * tile(s) holding them (a band may straddle two row tiles).  The consumer
+ * waits (bounded) until every flag of a remote segment's bands is set, reads
+ * the rows at device scope and copies the segment's valid rows to
  * recv[dst] + dst_off*d; padding rows are never copied.  Rows of local bands
  * (destination r) never leave the rank: the down GEMM's epilogue writes them
  * into recv[r] itself, besides y.

@@ -47,7 +47,7 @@ _VIEW_FIELDS = ["hdr", "c", "grp_off", "m_e", "row_off", "rb", "order", "base",
                 "band_expert", "band_dst", "band_src_row", "band_dst_off", "band_valid",
                 "seg_first", "seg_nbands", "seg_dst", "seg_dst_off", "seg_src_row", "seg_rows",
                 "seg_unit", "src_index", "pos",
-                "gu_tile_row", "gu_tile_expert", "dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands",
+                "gu_tile_row", "gu_tile_expert", "dn_tile_row", "dn_tile_expert", "grp_band",
                 "sk_counters", "sk_counters_count",
                 "crow_off", "grp_crow", "band_crow", "cmp_row", "cmp_src"]
 

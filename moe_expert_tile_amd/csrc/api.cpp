@@ -67,8 +67,8 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->tok_off[W] = tok;
   L->NB = blk;
   L->NB_r = L->blk_off[r + 1] - L->blk_off[r];
-  // down GEMM: 256-row tiles of whole bands (their real rows packed), one
-  // flag per band and column tile
+  // down GEMM: the gate/up GEMM's 256-row tiles of compacted rows; a pair of
+  // flags (band head, band tail) per band and column tile
   L->dn_ntn = d / kDnBN;
   L->dn_tpb = L->dn_ntn;
   L->gu_ntn = f / (kGuBN / 2);
@@ -108,10 +108,11 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   L->o_obase = take(W + 1);
   L->o_grow = take(EW);
   L->o_gcrow = take(EW);
-  L->o_btmp = take(6 * (B + 1));
+  L->o_btmp = take(4 * (B + 1));
+  L->o_gband = take(EW);
   L->o_gumt_row = take(L->gu_mt_cap);
   L->o_gumt_exp = take(L->gu_mt_cap);
-  L->o_dnt_row = take(B); L->o_dnt_exp = take(B); L->o_dnt_band = take(B); L->o_dnt_nb = take(B);
+  L->o_dnt_row = take(L->gu_mt_cap); L->o_dnt_exp = take(L->gu_mt_cap);
   L->o_crowoff = take(E_l + 1);
   L->o_ccum = take(EW);
   L->o_bcrow = take(B);
@@ -124,7 +125,7 @@ bool make_layout(int W, int r, int E_l, int k, int d, int f, int tb_m, int mgb, 
   // min(G, steps / kMinSkSteps) pieces, two slots each (a piece may close
   // one tile and open the next).
   const int64_t gu_tiles_max = (int64_t)L->gu_mt_cap * L->gu_ntn;
-  const int64_t dn_tiles_max = B * L->dn_ntn;
+  const int64_t dn_tiles_max = (int64_t)L->gu_mt_cap * L->dn_ntn;
   auto sk_need = [](int64_t tiles_max, int KT) -> int64_t {
     if (KT < kMinSkKTOneRound || tiles_max <= 0) return 0;
     const int64_t split_max = KT >= kMinSkKT ? 3 * kMaxProducers / 4 : kMaxProducers / 2;
@@ -237,7 +238,7 @@ int moe_query_sizes(const moe_shape* s, moe_sizes* out) {
   out->plan_bytes = (size_t)L.total_words * 4;
   out->rows_cap = L.rows_cap;
   out->bands_cap = L.bands_cap;
-  out->flags_count = (int64_t)L.bands_cap * L.dn_tpb;
+  out->flags_count = 2 * (int64_t)L.bands_cap * L.dn_tpb;
   out->recv_rows_self = (int64_t)L.T_r * L.k;
   return MOE_OK;
 }
@@ -259,7 +260,7 @@ int moe_plan_offsets(const moe_shape* s, moe_plan_view* v) {
   v->seg_unit = L.o_sunit * 4; v->src_index = L.o_src * 4; v->pos = L.o_pos * 4;
   v->gu_tile_row = L.o_gumt_row * 4; v->gu_tile_expert = L.o_gumt_exp * 4;
   v->dn_tile_row = L.o_dnt_row * 4; v->dn_tile_expert = L.o_dnt_exp * 4;
-  v->dn_tile_band = L.o_dnt_band * 4; v->dn_tile_nbands = L.o_dnt_nb * 4;
+  v->grp_band = L.o_gband * 4;
   v->sk_counters = L.o_skc * 4; v->sk_counters_count = 2 * kMaxProducers;
   v->crow_off = L.o_crowoff * 4; v->grp_crow = L.o_ccum * 4; v->band_crow = L.o_bcrow * 4;
   v->cmp_row = L.o_cmprow * 4; v->cmp_src = L.o_cmpsrc * 4;

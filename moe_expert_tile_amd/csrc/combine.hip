@@ -45,13 +45,15 @@ __global__ __launch_bounds__(kConsumerThreads) void consumer_rows_kernel(PlanLay
   for (int64_t i = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6); i < n_pairs; i += (int64_t)gridDim.x * WPB) {
     const int b = (int)(i / L.tb_m), r = (int)(i - (int64_t)b * L.tb_m);
     if (r >= bval[b]) continue;
-    // this row's band: every one of its tile flags must equal epoch
+    // this row's band: every one of its tile flags (head and tail per
+    // column tile) must equal epoch
     const uint64_t t0 = wall_clock64();
     int naps = 1;
     for (;;) {
       bool ok = true;
-      for (int j = lane; j < tpb; j += 64)
-        ok &= (__hip_atomic_load(flags + (int64_t)b * tpb + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch);
+      for (int j = lane; j < 2 * tpb; j += 64)
+        ok &= (__hip_atomic_load(flags + (int64_t)b * 2 * tpb + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               epoch);
       if (__ballot(!ok) == 0) break;
       if ((int64_t)(wall_clock64() - t0) > timeout) {
         if (lane == 0)

@@ -4,7 +4,8 @@
 // the overlapped down-GEMM launch.
 //
 // The remote segments are walked in schedule order: each waits until every
-// tile flag of its bands equals this call's epoch, then its valid rows --
+// tile flag of its bands equals this call's epoch (a band has a head and a
+// tail flag per column tile: a row tile may end inside it), then its valid rows --
 // contiguous in the layout and contiguous at the destination -- are copied
 // into the owner's receive buffer.  The W owners are W buffers in HBM; the
 // pages' one-sided remote put becomes a device-memory copy.  Local segments
@@ -13,8 +14,8 @@
 //
 // Memory ordering: the producer stores a tile's rows at device scope (sc1,
 // written through its XCD's L2), waits until every store is acknowledged and
-// only then sets flags[tile] = epoch with a relaxed agent-scope store (no
-// release fence).  Here wave 0 polls the flags with relaxed agent-scope
+// only then sets the tile's flags to epoch with relaxed agent-scope stores
+// (no release fence).  Here wave 0 polls the flags with relaxed agent-scope
 // loads; the tile's rows are read only after the flags were seen, with
 // agent-scope (sc1) loads, 16 bytes per lane, which do not return lines this
 // XCD cached earlier, so no acquire fence or cache-wide invalidation is
@@ -75,9 +76,10 @@ __device__ __forceinline__ int segment_of_unit(const int32_t* sunit, int n_rs, i
   return lo;
 }
 
-// Wave 0 waits until segment `seg` is ready: every tile flag of its bands
-// equals `epoch` (signal 0), or its group's ready counter reads (epoch,
-// bands of the group * column tiles) (signal 1).  Bounded by `timeout`
+// Wave 0 waits until segment `seg` is ready: both tile flags (band head and
+// band tail) of its bands for every column tile equal `epoch` (signal 0), or
+// its group's ready counter reads (epoch, 2 * bands of the group * column
+// tiles) (signal 1).  Bounded by `timeout`
 // ticks of the 100 MHz clock; on timeout the plan's error word becomes
 // MOE_ETIMEOUT.  Returns 0 if the workgroup must stop.  Every thread of the
 // workgroup calls it.
@@ -87,7 +89,8 @@ __device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, c
   const int tid = threadIdx.x, lane = tid & 63;
   const int tpb = L.dn_tpb;
   if (tid < 64) {
-    const int f0 = sfirst[seg] * tpb, f1 = (sfirst[seg] + snb[seg]) * tpb;
+    // flag words [2 tpb b, 2 tpb (b + 1)) belong to band b
+    const int f0 = 2 * sfirst[seg] * tpb, f1 = 2 * (sfirst[seg] + snb[seg]) * tpb;
     int gi = 0;
     uint64_t want = 0;
     if (cc.signal) {
@@ -95,7 +98,7 @@ __device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, c
       const int e = ws[L.o_bexp + sfirst[seg]], o = ws[L.o_sdst + seg];
       const int n = ws[L.o_c + e * L.W + o];
       gi = e * L.W + o;
-      want = ((uint64_t)epoch << 32) | (uint32_t)(((n + L.tb_m - 1) / L.tb_m) * tpb);
+      want = ((uint64_t)epoch << 32) | (uint32_t)(2 * ((n + L.tb_m - 1) / L.tb_m) * tpb);
     }
     const uint64_t t0 = wall_clock64();
     int go = 1;

@@ -302,13 +302,28 @@ __device__ __forceinline__ void issue_operand(lds_void_t* dst, __amdgpu_buffer_r
   }
 }
 
+// The down GEMM's epilogue tables in LDS, past the operand rings (int
+// words): per group k of the tile's expert (kMaxWorld each) its first tile
+// row, its layout-row offset, its padding rows (first, count), and what the
+// tile publishes for it (first and last band, head/tail bits and the group
+// index); then misc words (layout row of tile row 0, layout rows written,
+// the local group's tile rows and first receive row).  The publication
+// words are read at the next tile's prologue.
+struct DnTabs {
+  static constexpr int kLo = 0, kAdd = kMaxWorld, kPad0 = 2 * kMaxWorld, kNpad = 3 * kMaxWorld;
+  static constexpr int kB0 = 4 * kMaxWorld, kB1 = 5 * kMaxWorld, kHF = 6 * kMaxWorld;
+  static constexpr int kMisc = 7 * kMaxWorld;
+  static constexpr int kInts = kMisc + 8;
+};
+static_assert(kMaxWorld == 64, "one lane of wave 0 per group");
+
 template <class C, bool SWIGLU, bool FLAGS>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
 void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
-  // one LDS object: the operand rings, and for the down GEMM two small
-  // epilogue tables past them (a second object made the compiler wait for
-  // every outstanding load at each K step)
-  constexpr int kExtraElems = SWIGLU ? 0 : 2 * (kDnMaxBands + 1 + C::BM);
+  // one LDS object: the operand rings, and for the down GEMM the epilogue's
+  // small tables past them (a second object made the compiler wait for every
+  // outstanding load at each K step)
+  constexpr int kExtraElems = SWIGLU ? 0 : 2 * (DnTabs::kInts + C::BM);
   __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS + kExtraElems];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int WAVES_N = C::BN / C::WN;
@@ -423,41 +438,42 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     }
   }
 
-  // Down GEMM: a tile is published -- its bands' flags set, or its bands
-  // counted on their groups' ready words -- once its output stores are
+  // Down GEMM: a tile is published -- its band heads' and tails' flags set,
+  // or counted on their groups' ready words -- once its output stores are
   // acknowledged by every wave.  The wait is not at the end of the tile: the
   // next tile's prologue first issues its loads, then waits for the stores
   // alone (the vector memory counter retires in issue order), so the
   // stores drain under the next tile's loads instead of stalling the waves.
-  // The last tile is published after the loop.
-  int pend_b0 = 0, pend_nb = 0, pend_nt = 0;
-  auto publish = [&](int b0, int nb, int ntile) __attribute__((always_inline)) {
+  // The last tile is published after the loop.  What to publish, per group
+  // of the tile's expert, is in LDS (DnTabs: written by the epilogue).
+  int pend_nt = -1;
+  auto publish = [&](int ntile) __attribute__((always_inline)) {
+    if (tid >= L.W) return;
+    const int* tabs = (const int*)(lds + C::LDS_ELEMS);
+    const int b0 = tabs[DnTabs::kB0 + tid];
+    if (b0 < 0) return;
+    const int b1 = tabs[DnTabs::kB1 + tid], hf = tabs[DnTabs::kHF + tid];
     if (g.cc.signal == 0) {
-      // one flag per band of the tile (a band has n_nt flags, one per
-      // column tile)
-      if (tid < nb)
-        __hip_atomic_store(g.flags + (int64_t)(b0 + tid) * n_nt + ntile, g.epoch, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    } else if (tid == 0) {
-      // group-batched: the tile's bands, run by run of one (expert,
-      // destination) group, are counted on the group's epoch-tagged ready
-      // word; the group is ready once every band of it has been counted for
-      // every column tile
-      uint64_t* gready = g.sc.gready;
-      int b = b0;
-      while (b < b0 + nb) {
-        const int gi = g.ws[L.o_bexp + b] * L.W + g.ws[L.o_bdst + b];
-        int k = 1;
-        while (b + k < b0 + nb && g.ws[L.o_bexp + b + k] * L.W + g.ws[L.o_bdst + b + k] == gi) ++k;
-        uint64_t old = __hip_atomic_load(gready + gi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (;;) {
-          const uint32_t cnt = ((uint32_t)(old >> 32) == g.epoch ? (uint32_t)old : 0u) + (uint32_t)k;
-          const uint64_t nv = ((uint64_t)g.epoch << 32) | cnt;
-          if (__hip_atomic_compare_exchange_strong(gready + gi, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT))
-            break;
-        }
-        b += k;
+      // bands b0..b1 of one group: both flags of each, except the first
+      // one's head or the last one's tail when they lie in another tile
+      for (int b = b0; b <= b1; ++b) {
+        uint32_t* f = g.flags + 2 * ((int64_t)b * n_nt + ntile);
+        if (b > b0 || (hf & 1)) __hip_atomic_store(f, g.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (b < b1 || (hf & 2)) __hip_atomic_store(f + 1, g.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      // group-batched: the heads and tails counted on the group's
+      // epoch-tagged ready word; the group is ready once every band's head
+      // and tail have been counted for every column tile
+      const uint32_t k = (uint32_t)(2 * (b1 - b0 + 1) - ((hf & 1) ? 0 : 1) - ((hf & 2) ? 0 : 1));
+      uint64_t* gready = g.sc.gready + (hf >> 2);
+      uint64_t old = __hip_atomic_load(gready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (;;) {
+        const uint32_t cnt = ((uint32_t)(old >> 32) == g.epoch ? (uint32_t)old : 0u) + k;
+        const uint64_t nv = ((uint64_t)g.epoch << 32) | cnt;
+        if (__hip_atomic_compare_exchange_strong(gready, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+          break;
       }
     }
   };
@@ -485,46 +501,29 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       decode_tile<SWIGLU ? kXcdRowsGu : kXcdRowsDn>(t - n_mt_r * n_nt, n_mt - n_mt_r, n_nt, blk_r, blk_c, mt, nt);
       mt += n_mt_r;
     }
-    // row tile.  gate/up: 256 compacted rows of one expert (row0 their
-    // first, row_end the expert's end).  down: nbt whole bands of one run
-    // from band0 on, whose nrows real rows are consecutive compacted rows of
-    // h from crow0 on; row0 is the layout row of the first band (the run's
-    // bands follow one another in the layout, tb_M rows apart)
-    int e, row0, lim, band0 = 0, nbt = 1, crow0 = 0, nrows = 0;
+    // row tile: up to 256 compacted rows of one expert.  gate/up: row0 the
+    // first, row_end the expert's end.  down: its nrows rows of h from crow0
+    // on (row0 = 0, row_end = nrows)
+    int e, row0, lim, crow0 = 0, nrows = 0;
     if constexpr (SWIGLU) {
       row0 = g.ws[L.o_gumt_row + mt];
       e = g.ws[L.o_gumt_exp + mt];
       lim = g.ws[L.o_crowoff + e + 1];
     } else {
       const ctab_t* tab = (const ctab_t*)g.ws;
-      row0 = tab[L.o_dnt_row + mt];
-      e = tab[L.o_dnt_exp + mt];
-      band0 = __builtin_amdgcn_readfirstlane(tab[L.o_dnt_band + mt]);
-      nbt = __builtin_amdgcn_readfirstlane(tab[L.o_dnt_nb + mt]);
-      crow0 = tab[L.o_bcrow + band0];
-      nrows = tab[L.o_bcrow + band0 + nbt - 1] + tab[L.o_bval + band0 + nbt - 1] - crow0;
-      lim = row0 + nrows;
+      crow0 = tab[L.o_dnt_row + mt];
+      e = __builtin_amdgcn_readfirstlane(tab[L.o_dnt_exp + mt]);
+      nrows = min(C::BM, tab[L.o_crowoff + e + 1] - crow0);
+      row0 = 0;
+      lim = nrows;
     }
     // per-tile values are wave-uniform; say so, so that the buffer
     // descriptors built from them live in scalar registers
     e = __builtin_amdgcn_readfirstlane(e);
     row0 = __builtin_amdgcn_readfirstlane(row0);
-    band0 = __builtin_amdgcn_readfirstlane(band0);
-    nbt = __builtin_amdgcn_readfirstlane(nbt);
     crow0 = __builtin_amdgcn_readfirstlane(crow0);
     nrows = __builtin_amdgcn_readfirstlane(nrows);
     const int row_end = __builtin_amdgcn_readfirstlane(lim);
-    // local bands (destination r) never leave the rank: the epilogue also
-    // writes their rows into r's own receive buffer at the combine plan's
-    // destination rows, so the consumer moves only remote segments.  A run,
-    // so a tile, is all remote or all local; a local run's bands are
-    // consecutive rows of the unpadded local group, at both ends.
-    int ldst0 = -1;
-    if constexpr (FLAGS) {
-      const ctab_t* tab = (const ctab_t*)g.ws;
-      if (tab[L.o_bdst + band0] == L.r) ldst0 = tab[L.o_bdoff + band0];
-      ldst0 = __builtin_amdgcn_readfirstlane(ldst0);
-    }
     const bool empty = row0 >= row_end;
     // A operand.  Every load is bounded by a buffer descriptor, and a lane
     // whose row holds no data gets an offset past the bound (2^31 > the
@@ -618,15 +617,15 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       if constexpr (C::SB == 3) issue_b(1);
     }
     if constexpr (FLAGS) {
-      if (pend_nb > 0) {
+      if (pend_nt >= 0) {
         // the previous tile's stores went out before the loads just issued:
         // wait for those stores alone, in every wave, then publish the tile
         static_assert(C::A_LOADS + C::B_LOADS <= 63, "vector memory counter range");
         if (KTt > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(C::A_LOADS + C::B_LOADS));
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
         __builtin_amdgcn_s_barrier();
-        publish(pend_b0, pend_nb, pend_nt);
-        pend_nb = 0;
+        publish(pend_nt);
+        pend_nt = -1;
       }
     }
 
@@ -875,30 +874,31 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       constexpr int NCH = OUT_TC / 8;   // 16-byte chunks per output row
       static_assert(C::BM * OUT_TC <= C::LDS_ELEMS, "output tile fits the LDS ring");
       static_assert((NCH & (NCH - 1)) == 0 && NCH >= 16, "power-of-two chunk count");
-      // Row map: row m < nrows of the tile is row j of its band bi, which is
-      // layout row row0 + bi * tb_M + j in a remote run (whose bands follow
-      // one another tb_M rows apart) and row0 + m in a local one (its bands
-      // are consecutive rows of the unpadded local group).  boff[bi] is the
-      // first packed row of band bi; both tables sit past the LDS ring.
-      int* boff = (int*)(lds + C::LDS_ELEMS);   // [kDnMaxBands + 1]
-      int* rowmap = boff + kDnMaxBands + 1;     // [BM]
-      if (tid <= nbt) boff[tid] = (tid < nbt ? g.ws[L.o_bcrow + band0 + tid] : crow0 + nrows) - crow0;
-      __syncthreads();   // every wave is done with the ring; boff is complete
-      const bool remote_tile = ldst0 < 0;
-      if (tid < C::BM) {
-        const int m = tid;
-        int dst = -1;
-        if (m < nrows) {
-          if (remote_tile) {
-            int bi = 0;
-            while (boff[bi + 1] <= m) ++bi;
-            dst = bi * L.tb_m + (m - boff[bi]);
-          } else {
-            dst = m;
-          }
-        }
-        rowmap[m] = dst;
+      // The tile's rows run through the groups of X_e in layout order
+      // (remote owners ascending, r skipped, then r), each group's rows
+      // consecutive in both h and the layout (a remote group's padding rows
+      // follow its last real row).  Lane k < W of wave 0 takes group k: the
+      // tile rows [lo, hi) it holds, the layout row of each (tile row m ->
+      // m + add, counted from the layout row of tile row 0), the padding
+      // rows to zero when the tile holds the end of a remote group, and the
+      // bands to publish -- with whether the first one's head and the last
+      // one's tail lie in this tile.  A lane past W, or a group with no row
+      // here, has lo = hi (and b0 = -1), so tile row m belongs to the last
+      // group k < W with lo <= m.
+      int* tabs = (int*)(lds + C::LDS_ELEMS);
+      int* rowmap = tabs + DnTabs::kInts;   // [BM] layout row of each tile row (relative), or -1
+      int k_o = 0, k_n = 0, k_gc = 0, k_grow = 0, k_band = 0, k_base = 0;
+      const bool k_on = tid < L.W;
+      if (k_on) {
+        k_o = tid < L.W - 1 ? (tid < L.r ? tid : tid + 1) : L.r;
+        const int gi = e * L.W + k_o;
+        k_n = g.ws[L.o_c + gi];
+        k_gc = g.ws[L.o_gcrow + gi] - crow0;   // the group's first row, relative to the tile
+        k_grow = g.ws[L.o_grow + gi];
+        k_band = g.ws[L.o_gband + gi];
+        if (k_o == L.r) k_base = g.ws[L.o_base + L.r * L.E_l + e];
       }
+      __syncthreads();   // every wave is done with the ring
       char* tl = (char*)lds;
 #pragma unroll
       for (int j = 0; j < C::FM; ++j) {
@@ -914,20 +914,79 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
             *(uint2*)(tl + m * (OUT_TC * 2) + 16 * (ch ^ (m & (NCH - 1))) + 8 * lhalf) = pk;
           }
       }
+      if (tid < 64) {
+        const int lo = k_on ? min(max(k_gc, 0), nrows) : nrows;
+        const int hi = k_on ? min(max(k_gc + k_n, 0), nrows) : nrows;
+        // tile row 0 lies in exactly one group (nrows >= 1)
+        const uint64_t at0 = __ballot(k_on && lo == 0 && hi > 0);
+        const int lbase = __shfl(k_grow - k_gc, (int)__builtin_ctzll(at0));
+        const int add = k_grow - k_gc - lbase;
+        const bool ends = hi > lo && k_gc + k_n <= nrows;   // the group's last row is in the tile
+        const int npad = (ends && k_o != L.r) ? fdiv(k_n + L.tb_m - 1, L.div_tb) * L.tb_m - k_n : 0;
+        int end_rel = hi > lo ? hi + add + npad : 0;   // layout rows written, from tile row 0's
+#pragma unroll
+        for (int xs = 1; xs < 64; xs <<= 1) end_rel = max(end_rel, __shfl_xor(end_rel, xs));
+        int b0 = -1, b1 = -1, hf = 0;
+        if (hi > lo) {
+          const int q0 = fdiv(lo - k_gc, L.div_tb), q1 = fdiv(hi - 1 - k_gc, L.div_tb);
+          b0 = k_band + q0;
+          b1 = k_band + q1;
+          const bool head0 = lo - k_gc == q0 * L.tb_m;
+          const bool tail1 = hi - k_gc == min((q1 + 1) * L.tb_m, k_n);
+          hf = (head0 ? 1 : 0) | (tail1 ? 2 : 0) | ((e * L.W + k_o) << 2);
+        }
+        tabs[DnTabs::kLo + tid] = lo;
+        tabs[DnTabs::kAdd + tid] = add;
+        tabs[DnTabs::kPad0 + tid] = npad > 0 ? hi + add : 0;
+        tabs[DnTabs::kNpad + tid] = npad;
+        tabs[DnTabs::kB0 + tid] = b0;
+        tabs[DnTabs::kB1 + tid] = b1;
+        tabs[DnTabs::kHF + tid] = hf;
+        if (tid == 0) {
+          tabs[DnTabs::kMisc + 0] = lbase;
+          tabs[DnTabs::kMisc + 1] = end_rel;
+        }
+        if (k_on && k_o == L.r) {
+          tabs[DnTabs::kMisc + 2] = lo;
+          tabs[DnTabs::kMisc + 3] = hi;
+          tabs[DnTabs::kMisc + 4] = k_base + (lo - k_gc);   // receive row of the first local row here
+        }
+      }
       __syncthreads();
-      // the stores: the tile's real rows to their layout rows (and, in a
-      // local run, to the rank's own receive buffer), then zeros into the
-      // padding rows of every remote band; the descriptors end past the
-      // last row written
+      if (tid < C::BM) {
+        const int m = tid;
+        int dst = -1;
+        if (m < nrows) {
+          int lo = 0, hi = L.W - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tabs[DnTabs::kLo + mid] <= m) lo = mid; else hi = mid - 1;
+          }
+          dst = m + tabs[DnTabs::kAdd + lo];
+        }
+        rowmap[m] = dst;
+      }
+      __syncthreads();
+      // the stores: the tile's real rows to their layout rows (and its rows
+      // of the local group also to the rank's own receive buffer), then
+      // zeros into the padding rows of every remote group that ends here;
+      // the descriptors end past the last row written
       const int64_t out_row_bytes = (int64_t)g.out_cols * 2;
       const int col0 = nt * OUT_TC;
-      const int span = remote_tile ? nbt * L.tb_m : nrows;   // layout rows from row0
+      const int lbase = __builtin_amdgcn_readfirstlane(tabs[DnTabs::kMisc + 0]);
+      const int span = __builtin_amdgcn_readfirstlane(tabs[DnTabs::kMisc + 1]);
+      // the local group's rows here and the receive row of the first (the
+      // local group's lane writes them for every tile; lo = hi if none)
+      const int llo = __builtin_amdgcn_readfirstlane(tabs[DnTabs::kMisc + 2]);
+      const int lhi = __builtin_amdgcn_readfirstlane(tabs[DnTabs::kMisc + 3]);
+      const int lrecv = __builtin_amdgcn_readfirstlane(tabs[DnTabs::kMisc + 4]);
       if (nrows > 0) {
         const __amdgpu_buffer_rsrc_t o_rsrc =
-            make_rsrc(g.out + (int64_t)row0 * g.out_cols + col0, (int64_t)span * out_row_bytes);
+            make_rsrc(g.out + (int64_t)lbase * g.out_cols + col0, (int64_t)span * out_row_bytes);
+        const bool has_local = lhi > llo;
         __amdgpu_buffer_rsrc_t l_rsrc = o_rsrc;
-        if (ldst0 >= 0)
-          l_rsrc = make_rsrc(recv.p[L.r] + (int64_t)ldst0 * g.out_cols + col0, (int64_t)nrows * out_row_bytes);
+        if (has_local)
+          l_rsrc = make_rsrc(recv.p[L.r] + (int64_t)lrecv * g.out_cols + col0, (int64_t)(lhi - llo) * out_row_bytes);
         constexpr int RPP = C::NT / NCH;   // rows per pass
         constexpr int PASSES = C::BM / RPP;
         constexpr int UNR = PASSES >= 4 ? 4 : PASSES;
@@ -949,23 +1008,23 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
             const int m = (p0 + u) * RPP + r_in;
             const uint32_t off = dst[u] >= 0 ? (uint32_t)((int64_t)dst[u] * out_row_bytes + ch * 16) : 0xFFFFFFF0u;
             __builtin_amdgcn_raw_buffer_store_b128(v[u], o_rsrc, off, 0, MOE_STORE_AUX);
-            if (ldst0 >= 0) {
-              const uint32_t loff = m < nrows ? (uint32_t)((int64_t)m * out_row_bytes + ch * 16) : 0xFFFFFFF0u;
+            if (has_local) {
+              const uint32_t loff =
+                  (m >= llo && m < lhi) ? (uint32_t)((int64_t)(m - llo) * out_row_bytes + ch * 16) : 0xFFFFFFF0u;
               __builtin_amdgcn_raw_buffer_store_b128(v[u], l_rsrc, loff, 0, MOE_STORE_AUX);
             }
           }
         }
-        if (remote_tile) {
-          // padding rows of the tile's bands: [valid, tb_M) of each
-          const v4u32 z = {0u, 0u, 0u, 0u};
-          for (int bi = 0; bi < nbt; ++bi) {
-            const int v = boff[bi + 1] - boff[bi];
-            const int npad = L.tb_m - v;
-            for (int idx = tid; idx < npad * NCH; idx += C::NT) {
-              const int row = bi * L.tb_m + v + idx / NCH;
-              __builtin_amdgcn_raw_buffer_store_b128(z, o_rsrc, (uint32_t)((int64_t)row * out_row_bytes + (idx % NCH) * 16),
-                                                     0, MOE_STORE_AUX);
-            }
+        // padding rows of the remote groups that end in this tile
+        const v4u32 z = {0u, 0u, 0u, 0u};
+        for (int k = 0; k < L.W; ++k) {
+          const int npad = tabs[DnTabs::kNpad + k];
+          if (npad == 0) continue;
+          const int pad0 = tabs[DnTabs::kPad0 + k];
+          for (int idx = tid; idx < npad * NCH; idx += C::NT) {
+            const int row = pad0 + idx / NCH;
+            __builtin_amdgcn_raw_buffer_store_b128(z, o_rsrc, (uint32_t)((int64_t)row * out_row_bytes + (idx % NCH) * 16),
+                                                   0, MOE_STORE_AUX);
           }
         }
       }
@@ -986,19 +1045,17 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       // acquire fence and no L2 invalidate.
       static_assert((MOE_STORE_AUX & kDeviceScope) != 0, "flag publication needs device-scope (sc1) output stores");
       if constexpr (FLAGS) {
-        pend_b0 = band0;   // published once the stores above are acknowledged
-        pend_nb = nbt;
-        pend_nt = nt;
+        pend_nt = nt;   // published once the stores above are acknowledged
       } else {
         wait_vm0();
       }
     }
   }
   if constexpr (FLAGS) {
-    if (pend_nb > 0) {   // the last tile: its stores are the last memory operations
+    if (pend_nt >= 0) {   // the last tile: its stores are the last memory operations
       wait_vm0();
       __builtin_amdgcn_s_barrier();
-      publish(pend_b0, pend_nb, pend_nt);
+      publish(pend_nt);
     }
     if (tid == 0) stamp_max(hdr, H_T_PROD_END);
     if (overlapped && items > 0) {

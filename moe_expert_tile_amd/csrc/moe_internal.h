@@ -16,8 +16,7 @@ constexpr int kCopyChunk = 32768;      // bytes per consumer copy unit
 constexpr int kGuBM = 256;             // gate/up GEMM tile rows
 constexpr int kGuBN = 256;             // gate/up GEMM tile cols (128 gate + 128 up)
 constexpr int kDnBN = 256;             // down GEMM tile cols
-constexpr int kDnBM = 256;             // down GEMM tile rows: whole bands of one run, their real rows packed
-constexpr int kDnMaxBands = 64;        // bands packed into one down tile at most
+constexpr int kDnBM = 256;             // down GEMM tile rows: 256 compacted rows of one X_e, as gate/up's
 // K steps of the GEMM configurations (gemm.hip asserts them); the host sizes
 // the stream-K scratch with them
 constexpr int kGuBK = 64;              // gate/up
@@ -48,7 +47,7 @@ enum Hdr {
   // workgroup of the down-GEMM launch as it ends (atomic max, so no reset is
   // needed between calls): words 12-13 and 14-15
   H_T_PROD_END = 12, H_T_CONS_END = 14,
-  H_DN_MT_R = 16,   // down row tiles of remote bands (they come first)
+  H_DN_MT_R = 16,   // down row tiles holding remote rows (they come first)
   // overlapped down-GEMM launch: copy-unit claims handed out so far, and
   // producers that have started (the default Scratch::claim); both zeroed by
   // the gate/up launch, which precedes every down GEMM on the same stream
@@ -87,7 +86,7 @@ inline int fdiv(int n, const FastDiv& f) { return (int)(((uint64_t)(uint32_t)n *
 struct PlanLayout {
   int W, r, E_l, E, k, d, f, tb_m, mgb;
   int R, rows_cap, bands_cap, T_r, NB, NB_r, gu_mt_cap;
-  int dn_ntn, dn_tpb;                  // down GEMM: column tiles, flags per band (= column tiles)
+  int dn_ntn, dn_tpb;                  // down GEMM: column tiles, flag pairs per band (= column tiles)
   int gu_ntn;                          // gate/up GEMM n tiles (f / 128)
   int band_lds;                        // the plan builder keeps its per-band tables in LDS (else in btmp)
   FastDiv div_tb, div_mgb, div_wm1, div_hb, div_w, div_el;   // by tb_m, mgb, max(W - 1, 1), E_l + 2, W, E_l
@@ -99,9 +98,10 @@ struct PlanLayout {
   int64_t o_bh, o_bhr;                 // per-block histograms (plan_count)
   int64_t o_obase;                     // [W + 1]: received rows from the owners before each owner
   int64_t o_grow, o_gcrow;             // [E_l][W]: first layout row and first compacted row of every group
-  int64_t o_btmp;                      // [6 * bands_cap + 2]: the builder's per-band tables when not in LDS
+  int64_t o_btmp;                      // [4 * (bands_cap + 1)]: the builder's per-band tables when not in LDS
+  int64_t o_gband;                     // [E_l][W]: first band of every group in S
   int64_t o_gumt_row, o_gumt_exp;
-  int64_t o_dnt_row, o_dnt_exp, o_dnt_band, o_dnt_nb;
+  int64_t o_dnt_row, o_dnt_exp;
   // compacted rows (the layout without its padding rows, in layout order):
   // start of every expert, offset of every group inside its expert, first
   // compacted row of every band, and per compacted row its layout row and
@@ -139,8 +139,8 @@ constexpr int kMaxGroups = 1024;       // E_l * W at most
 // How the consumer waits and copies (moe_combine_opts):
 //   signal 0: per-band tile flags, equal to the call's epoch when ready;
 //   signal 1: one ready counter per (expert, destination) group, raised by
-//             each down tile by its bands of the group and ready when it
-//             reads (epoch, bands * column tiles);
+//             each down tile by the band heads and tails of the group it
+//             holds and ready when it reads (epoch, 2 * bands * column tiles);
 //   link_mbps > 0: every copy unit to owner o also takes bytes / rate on an
 //             emulated link of owner o (reserved in order on the device
 //             clock), and the copying workgroup waits until its transfer
@@ -156,10 +156,10 @@ struct CopyCtl {
 // LDS carve-outs of the planner's second launch, in int words; the host
 // sizes the launch's dynamic LDS with the same functions the kernel carves
 // it with.  The builder keeps its expert x owner tables on chip and, when
-// `bands` is set, six per-band tables of bands_cap (+1) words.
+// `bands` is set, four per-band tables of bands_cap + 1 words.
 struct BuildLds {
-  int c, grow, gcrow, base, gstart, low, bad, obase, me, ce, rowoff, crowoff, rb, order, gupre, sh, misc;
-  int bg, vv, nx, ja, jb, on, total;
+  int c, grow, gcrow, base, gstart, low, bad, obase, me, ce, rowoff, crowoff, rb, order, gupre, dpre, sh, misc;
+  int nx, ja, jb, on, total;
 };
 #if defined(__HIPCC__)
 __host__ __device__
@@ -183,15 +183,14 @@ inline BuildLds build_lds(int W, int E_l, int bands_cap, bool bands) {
   s.rb = o; o += E_l;
   s.order = o; o += E_l;
   s.gupre = o; o += E_l + 1;
+  s.dpre = o; o += 2 * (E_l + 1);
   s.sh = o; o += 32;
   s.misc = o; o += 8;
   const int nb = bands ? bands_cap + 1 : 0;
-  s.bg = o; o += nb;    // group of every band
-  s.vv = o; o += nb;    // valid rows of every band, then their exclusive prefix over S
-  s.nx = o; o += nb;    // end of the down tile that would start at the band
-  s.ja = o; o += nb;    // pointer-doubling jumps (two buffers)
-  s.jb = o; o += nb;
-  s.on = o; o += nb;    // the band starts a down tile
+  s.nx = o; o += nb;    // segment started at the band: rows << 8 | bands, or 0
+  s.ja = o; o += nb;    // the band's source row
+  s.jb = o; o += nb;    // the band's receive offset
+  s.on = o; o += nb;    // the band's owner
   s.total = o;
   return s;
 }

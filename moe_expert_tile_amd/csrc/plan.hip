@@ -389,20 +389,24 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
   }
   const int n_remote = NGR < NG ? gstart[NGR] : B;
   if (tid == 0) gstart[NG] = B;
+  // every group's first band in S, for the down GEMM's epilogue
+  for (int gi = tid; gi < NG; gi += nt) {
+    int e, o;
+    group_eo(gi, e, o);
+    ws[L.o_gband + e * W + o] = gstart[gi];
+  }
 
-  // per-band tables
-  int* bg;   // [B] group of every band
-  int* vv;   // [B + 1] valid rows, then their exclusive prefix over S
-  int* nx;   // [B] end of the down tile that would start at the band
-  int* ja;   // [B] pointer-doubling jumps
-  int* jb;
-  int* on;   // [B] the band starts a down tile
+  // per-band tables of the segment scan
+  int* nx;   // [B] segment started at the band: rows << 8 | bands, or 0
+  int* ja;   // [B] source row
+  int* jb;   // [B] receive offset
+  int* on;   // [B] owner
   if constexpr (kBandLds) {
-    bg = smem + S.bg; vv = smem + S.vv; nx = smem + S.nx; ja = smem + S.ja; jb = smem + S.jb; on = smem + S.on;
+    nx = smem + S.nx; ja = smem + S.ja; jb = smem + S.jb; on = smem + S.on;
   } else {
     int* t = ws + L.o_btmp;
     const int nb = L.bands_cap + 1;
-    bg = t; vv = t + nb; nx = t + 2 * nb; ja = t + 3 * nb; jb = t + 4 * nb; on = t + 5 * nb;
+    nx = t; ja = t + nb; jb = t + 2 * nb; on = t + 3 * nb;
   }
 
   // (e) bands in S order, one thread per band.  Each band also decides
@@ -412,8 +416,7 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
   //     the band's own group).  A starting band keeps its segment's bands
   //     and rows for the scan below, which numbers the segments and places
   //     their copy units; the band tables nx, ja, jb, on hold the segment,
-  //     source row, receive offset and owner until the down tiles reuse
-  //     them.
+  //     source row, receive offset and owner.
   int32_t* bexp = ws + L.o_bexp;
   int32_t* bdst = ws + L.o_bdst;
   int32_t* bsrc = ws + L.o_bsrc;
@@ -433,8 +436,6 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
     const int v = min(tb, n - q * tb);
     const int src_row = grow[e * W + o] + q * tb;
     const int dst_off = base[o * E_l + e] + q * tb;
-    bg[b] = gi;
-    vv[b] = v;
     bexp[b] = e;
     bdst[b] = o;
     bsrc[b] = src_row;
@@ -513,86 +514,38 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
     mt_exp[t] = e;
   }
 
-  // (h) down tiles.  The bands of S form runs of row-contiguous bands --
-  //     the remote bands of each expert in rule (ii) order (its remote
-  //     groups follow one another at the start of X_e), then the local
-  //     bands of each expert -- and each run is cut greedily into tiles of
-  //     whole bands whose real rows add up to at most kDnBM (and at most
-  //     kDnMaxBands bands).  The GEMM multiplies a tile's real rows only,
-  //     packed, so a tile of two half-empty bands costs one band's work.
-  //     In parallel: nx[b] is where a tile starting at band b would end
-  //     (a binary search over the prefix of valid rows), and the tiles'
-  //     first bands are the chain run start -> nx -> nx ..., marked by
-  //     pointer doubling: after round k every first band within 2^k tiles
-  //     of its run's start is marked.
-  (void)scan_items(
-      B, [&](int b) { return vv[b]; }, [&](int b, int pre) { vv[b] = pre; }, sh);
-  if (tid == 0) vv[B] = rcount;   // the valid rows of all bands
-  __syncthreads();
-  auto run_of = [&](int gi, int& rs, int& re) {
-    if (gi < NGR) {
-      const int q = fdiv(gi, L.div_wm1);
-      rs = gstart[q * (W - 1)];
-      re = gstart[(q + 1) * (W - 1)];
-    } else {
-      rs = gstart[gi];
-      re = gstart[gi + 1];
-    }
-  };
-  for (int b = tid; b < B; b += nt) {
-    int rs, re;
-    run_of(bg[b], rs, re);
-    int lo = b + 1, hi = min(re, b + kDnMaxBands);   // a band alone always fits
-    const int p0 = vv[b];
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (vv[mid] - p0 <= kDnBM) lo = mid; else hi = mid - 1;
-    }
-    nx[b] = lo;
-    ja[b] = lo < re ? lo : -1;
-    on[b] = (b == rs);
-  }
-  if (tid == 0) misc[2] = 0;   // round 0's word (see below)
-  __syncthreads();
-  // One pass per round marks with the current jumps and doubles them into
-  // the other buffer.  A mark another thread sees early in the same pass is
-  // a first band all the same, so the pass needs no barrier inside.  Round
-  // k's "a jump is left" word is misc[2 + k mod 3]: it was cleared during
-  // round k - 1, after every thread had read it as round k - 3's word.
-  for (int k = 0;; k = (k == 2 ? 0 : k + 1)) {
-    if (tid == 0) misc[2 + (k == 2 ? 0 : k + 1)] = 0;
-    int more = 0;
-    for (int b = tid; b < B; b += nt) {
-      const int j = ja[b];
-      if (j >= 0 && on[b]) on[j] = 1;
-      const int jj = j >= 0 ? ja[j] : -1;
-      jb[b] = jj;
-      more |= jj >= 0;
-    }
-    if (more) misc[2 + k] = 1;
-    int* t = ja; ja = jb; jb = t;
-    __syncthreads();
-    if (!misc[2 + k]) break;
-  }
+  // (h) down tiles: the same 256-row pieces of every X_e's compacted rows
+  //     as the gate/up tiles (X_e's remote groups first, then its local
+  //     group), in schedule order: first every piece that holds remote rows,
+  //     experts in rule (ii) order, then the pieces of local rows alone,
+  //     experts ascending.  A piece may hold an expert's last remote rows and
+  //     its first local rows, and a band may straddle two pieces: the GEMM's
+  //     epilogue publishes the head and the tail of a band separately.  So
+  //     the down GEMM runs as many row tiles as the gate/up GEMM, and none of
+  //     them holds a padding row.
   int32_t* dt_row = ws + L.o_dnt_row;
   int32_t* dt_exp = ws + L.o_dnt_exp;
-  int32_t* dt_band = ws + L.o_dnt_band;
-  int32_t* dt_nb = ws + L.o_dnt_nb;
-  if (tid == 0) misc[1] = -1;
-  const int NDT = scan_items(
-      B, [&](int b) { return on[b]; },
-      [&](int b, int pre) {
-        if (b == n_remote) misc[1] = pre;   // down tiles of remote bands (they come first)
-        if (!on[b]) return;
-        int e, o;
-        group_eo(bg[b], e, o);
-        dt_row[pre] = grow[e * W + o] + (b - gstart[bg[b]]) * tb;
-        dt_exp[pre] = e;
-        dt_band[pre] = b;
-        dt_nb[pre] = nx[b] - b;
-      },
+  int* dr = smem + S.dpre;    // [E_l]: pieces with remote rows before the q-th expert of rule (ii)
+  int* dl = dr + E_l + 1;     // [E_l]: pieces of local rows alone before expert e
+  auto rpieces = [&](int e) { return (ce[e] - c[e * W + r] + kDnBM - 1) / kDnBM; };
+  const int NDR = scan_items(
+      E_l, [&](int q) { return rpieces(order[q]); }, [&](int q, int pre) { dr[q] = pre; }, sh);
+  const int NDT = NDR + scan_items(
+      E_l, [&](int e) { return (ce[e] + kDnBM - 1) / kDnBM - rpieces(e); }, [&](int e, int pre) { dl[e] = pre; },
       sh);
-  const int ndt_r = misc[1] >= 0 ? misc[1] : NDT;
+  for (int t = tid; t < NDT; t += nt) {
+    int e, j;
+    if (t < NDR) {
+      const int q = upper_index(dr, E_l, t);
+      e = order[q];
+      j = t - dr[q];
+    } else {
+      e = upper_index(dl, E_l, t - NDR);
+      j = rpieces(e) + (t - NDR - dl[e]);
+    }
+    dt_row[t] = crowoff[e] + j * kDnBM;
+    dt_exp[t] = e;
+  }
 
   if (tid == 0) {
     hdr[H_M] = M;
@@ -601,12 +554,12 @@ __device__ void build_plan(const PlanLayout& L, int32_t* __restrict__ ws) {
     hdr[H_SEGS] = NS;
     hdr[H_RSEGS] = n_rsegs;
     hdr[H_GU_TILES] = NMT * L.gu_ntn;
-    hdr[H_DN_TILES] = B * L.dn_tpb;
+    hdr[H_DN_TILES] = 2 * B * L.dn_tpb;
     hdr[H_UNITS] = U;
     hdr[H_RCOUNT] = rcount;
     hdr[H_GU_MT] = NMT;
     hdr[H_DN_MT] = NDT;
-    hdr[H_DN_MT_R] = ndt_r;
+    hdr[H_DN_MT_R] = NDR;
   }
 }
 

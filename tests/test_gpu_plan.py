@@ -78,68 +78,68 @@ def test_replanning_reuses_the_workspace():
 
 
 def expected_tiles(pl):
-    """GEMM row tiles implied by the oracle plan: gate/up tiles cut the real
-    rows of every X_e (its compacted rows, experts in rule (ii) order) into
-    256-row pieces; down tiles cut each maximal run of bands in S order with
-    one expert and one side (remote or local) greedily into tiles of whole
-    bands whose real rows add up to at most 256 (at most 64 bands)."""
+    """GEMM row tiles implied by the oracle plan, as (first compacted row,
+    expert): gate/up tiles cut the real rows of every X_e (its compacted rows,
+    remote groups first and the local group last) into 256-row pieces,
+    experts in rule (ii) order; the down tiles are the same pieces in
+    schedule order -- first every piece that holds remote rows (experts in
+    rule (ii) order), then the pieces of local rows alone (experts
+    ascending)."""
     gu_row, gu_exp = [], []
     crow_off = expected_compacted(pl)["crow_off"]
+    n_real = [int(crow_off[e + 1] - crow_off[e]) for e in range(pl.E_l)]
+    n_remote = [n_real[e] - int(pl.c[e, pl.r]) for e in range(pl.E_l)]
     for e in pl.expert_order:
-        n = int(crow_off[e + 1] - crow_off[e])
-        for i in range(-(-n // 256)):
+        for i in range(-(-n_real[e] // 256)):
             gu_row.append(int(crow_off[e]) + 256 * i)
             gu_exp.append(int(e))
-    b = pl.bands
     dn = []
-    s0 = 0
-    while s0 < pl.n_bands:
-        s1 = s0
-        while (s1 + 1 < pl.n_bands and b["expert"][s1 + 1] == b["expert"][s0]
-               and b["remote"][s1 + 1] == b["remote"][s0]):
-            s1 += 1
-        # greedy: whole bands while their real rows fit 256 (at most 64 bands)
-        f0, rows = s0, 0
-        for s in range(s0, s1 + 1):
-            v = int(b["valid"][s])
-            if s > f0 and (rows + v > 256 or s - f0 == 64):
-                dn.append((int(b["src_row"][f0]), int(b["expert"][f0]), f0, s - f0))
-                f0, rows = s, 0
-            rows += v
-        dn.append((int(b["src_row"][f0]), int(b["expert"][f0]), f0, s1 + 1 - f0))
-        s0 = s1 + 1
+    for e in pl.expert_order:
+        for i in range(-(-n_remote[e] // 256)):
+            dn.append((int(crow_off[e]) + 256 * i, int(e)))
+    for e in range(pl.E_l):
+        for i in range(-(-n_remote[e] // 256), -(-n_real[e] // 256)):
+            dn.append((int(crow_off[e]) + 256 * i, int(e)))
     return gu_row, gu_exp, dn
 
 
-@pytest.mark.parametrize("name", WORKLOADS)
-def test_gemm_tile_tables(name):
-    """The planner's GEMM row-tile tables equal the ones the oracle plan
-    implies, and every down tile's bands are consecutive rows of one expert."""
-    c, share = run_plan(name, 1)
-    pl = c["plan"]
-    hdr = share.header()
+def expected_group_bands(pl):
+    """First band in S of every non-empty (expert, owner) group."""
+    out = {}
+    for s in range(pl.n_bands):
+        key = (int(pl.bands["expert"][s]), int(pl.bands["dst"][s]))
+        out.setdefault(key, s)
+    return out
+
+
+def check_tiles(share, pl, hdr):
     gu_row, gu_exp, dn = expected_tiles(pl)
     assert hdr["gateup_row_tiles"] == len(gu_row)
     assert hdr["down_row_tiles"] == len(dn)
     assert share.array("gu_tile_row", len(gu_row)).tolist() == gu_row
     assert share.array("gu_tile_expert", len(gu_row)).tolist() == gu_exp
-    got = list(zip(*(share.array(k, len(dn)).tolist() for k in
-                     ["dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands"])))
+    got = list(zip(*(share.array(k, len(dn)).tolist() for k in ["dn_tile_row", "dn_tile_expert"])))
     assert got == dn
     o = share.offsets["hdr"] // 4
-    n_remote_tiles = sum(1 for _, _, f0, _ in dn if pl.bands["remote"][f0])
+    crow_off = expected_compacted(pl)["crow_off"]
+    n_remote_tiles = sum(1 for row, e in dn if row - crow_off[e] < crow_off[e + 1] - crow_off[e] - pl.c[e, pl.r])
     assert int(share.plan_ws[o + 16]) == n_remote_tiles
-    covered = [f0 + q for _, _, f0, nb in dn for q in range(nb)]
-    assert covered == list(range(pl.n_bands))
-    for row0, e, f0, nb in dn:
-        for q in range(nb):
-            assert int(pl.bands["src_row"][f0 + q]) == row0 + q * pl.tb_m
-            assert int(pl.bands["expert"][f0 + q]) == e
+    gb = share.array("grp_band", pl.E_l * pl.W).reshape(pl.E_l, pl.W)
+    for (e, d), s in expected_group_bands(pl).items():
+        assert int(gb[e, d]) == s, (e, d)
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_gemm_tile_tables(name):
+    """The planner's GEMM row-tile tables and group first bands equal the
+    ones the oracle plan implies."""
+    c, share = run_plan(name, 1)
+    check_tiles(share, c["plan"], share.header())
 
 
 def test_plan_with_band_tables_in_the_workspace():
-    """A plan with 4070 bands (bands_cap 4247): the builder's six per-band
-    tables (6 x 4248 words, 102 KB) exceed the 64 KB of LDS it may use, so it
+    """A plan with 4070 bands (bands_cap 4247): the builder's four per-band
+    tables (4 x 4248 words, 68 KB) exceed the 64 KB of LDS it may use, so it
     keeps them in the workspace instead.  Metadata, compacted-row tables and
     GEMM tile tables bit-exact as on the other workloads."""
     import moe_expert_tile_amd as m
@@ -167,12 +167,7 @@ def test_plan_with_band_tables_in_the_workspace():
     sizes = {"crow_off": E_l + 1, "grp_crow": E_l * W, "band_crow": pl.n_bands, "cmp_row": pl.R, "cmp_src": pl.R}
     for key, v in cx.items():
         assert np.array_equal(share.array(key, sizes[key]).astype(np.int64), np.asarray(v, dtype=np.int64).reshape(-1)), key
-    gu_row, gu_exp, dn = expected_tiles(pl)
-    assert hdr["gateup_row_tiles"] == len(gu_row) and hdr["down_row_tiles"] == len(dn)
-    assert share.array("gu_tile_row", len(gu_row)).tolist() == gu_row
-    got = list(zip(*(share.array(key, len(dn)).tolist() for key in
-                     ["dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands"])))
-    assert got == dn
+    check_tiles(share, pl, hdr)
 
 
 @pytest.mark.parametrize("W,E_l,k,tokens_per_owner,tb", [
@@ -205,10 +200,4 @@ def test_plan_at_the_shape_limits(W, E_l, k, tokens_per_owner, tb):
     sizes = {"crow_off": E_l + 1, "grp_crow": E_l * W, "band_crow": pl.n_bands, "cmp_row": pl.R, "cmp_src": pl.R}
     for key, v in cx.items():
         assert np.array_equal(share.array(key, sizes[key]).astype(np.int64), np.asarray(v, dtype=np.int64).reshape(-1)), key
-    gu_row, gu_exp, dn = expected_tiles(pl)
-    assert hdr["gateup_row_tiles"] == len(gu_row) and hdr["down_row_tiles"] == len(dn)
-    assert share.array("gu_tile_row", len(gu_row)).tolist() == gu_row
-    assert share.array("gu_tile_expert", len(gu_row)).tolist() == gu_exp
-    got = list(zip(*(share.array(key, len(dn)).tolist() for key in
-                     ["dn_tile_row", "dn_tile_expert", "dn_tile_band", "dn_tile_nbands"])))
-    assert got == dn
+    check_tiles(share, pl, hdr)
