@@ -22,7 +22,8 @@
 // issued and the producer's L2 contents on the same XCD survive.
 //
 // Work split: each segment is cut into units of kCopyChunk bytes, numbered
-// in schedule order.  The standalone consumer kernel gives unit u to
+// in schedule order.  A workgroup keeps two units in flight: the next
+// unit's loads go out before the current unit's stores.  The standalone consumer kernel gives unit u to
 // workgroup u mod n_cons.  In the overlapped down-GEMM launch the units are
 // claimed from a counter in schedule order, by the launch's consumer
 // workgroups and by producers that have run out of tiles (consume_claimed).
@@ -37,6 +38,12 @@
 namespace moe {
 
 typedef unsigned int cv4u32 __attribute__((ext_vector_type(4)));
+// The plan's tables, written by the planner's launches and only read by the
+// combine's kernels: loads through the constant address space with a
+// wave-uniform index become scalar loads, which the vector memory counter
+// does not track, so reading a table never waits for outstanding loads and
+// stores (the GEMM's tile setup, the copy's next unit).
+typedef const int32_t __attribute__((address_space(4))) ctab_t;
 
 // Raw buffer resource over [base, base + bytes): accesses past the end read
 // zero and drop their stores (gfx9-family word 3: 32-bit data format).
@@ -62,7 +69,7 @@ constexpr int kStreamStore = 18;
 
 // Segment of copy unit u, searching forward from `seg` (units only grow):
 // a few steps ahead, then a binary search over the rest.
-__device__ __forceinline__ int segment_of_unit(const int32_t* sunit, int n_rs, int seg, int u) {
+__device__ __forceinline__ int segment_of_unit(const ctab_t* sunit, int n_rs, int seg, int u) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (sunit[seg + 1] > u) return seg;
@@ -83,8 +90,8 @@ __device__ __forceinline__ int segment_of_unit(const int32_t* sunit, int n_rs, i
 // ticks of the 100 MHz clock; on timeout the plan's error word becomes
 // MOE_ETIMEOUT.  Returns 0 if the workgroup must stop.  Every thread of the
 // workgroup calls it.
-__device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, const int32_t* sfirst,
-                                            const int32_t* snb, const uint32_t* __restrict__ flags, uint32_t epoch,
+__device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, const ctab_t* sfirst,
+                                            const ctab_t* snb, const uint32_t* __restrict__ flags, uint32_t epoch,
                                             const CopyCtl& cc, const int32_t* ws, int seg, int* s_go) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int tpb = L.dn_tpb;
@@ -160,28 +167,100 @@ __device__ __forceinline__ void pace_unit(const CopyCtl& cc, int dst, int64_t by
   __syncthreads();
 }
 
-// Copy unit u of segment seg: bytes [lo, lo + kCopyChunk) of the segment,
-// clipped to its end by the buffer bounds, every load before the first store.
-// Returns the unit's bytes.
+// One copy unit in flight: its bytes in registers (VPT 16-byte vectors per
+// thread), where they go, how many there are and the destination rank.
 template <int NT>
-__device__ __forceinline__ int64_t copy_unit(const PlanLayout& L, const int32_t* ssrc, const int32_t* sdst,
-                                             const int32_t* sdoff, const int32_t* srows, const int32_t* sunit,
-                                             const uint16_t* __restrict__ y, const RecvPtrs& recv, int seg, int u) {
-  const int tid = threadIdx.x;
-  const int64_t d = L.d;
-  const int64_t bytes = (int64_t)srows[seg] * d * 2;
-  const int64_t lo = (int64_t)(u - sunit[seg]) * kCopyChunk;
-  const int64_t n = min((int64_t)kCopyChunk, bytes - lo);
-  const __amdgpu_buffer_rsrc_t src = copy_rsrc((const char*)(y + (int64_t)ssrc[seg] * d) + lo, n);
-  const __amdgpu_buffer_rsrc_t dst = copy_rsrc((char*)(recv.p[sdst[seg]] + (int64_t)sdoff[seg] * d) + lo, n);
-  constexpr int VPT = kCopyChunk / (NT * 16);
+struct CopyUnit {
+  static constexpr int VPT = kCopyChunk / (NT * 16);
   static_assert(VPT >= 1 && VPT * NT * 16 == kCopyChunk, "whole vectors per unit");
   cv4u32 v[VPT];
+  char* to;
+  int64_t n;
+  int dst;   // -1: no unit
+};
+
+// The segment tables the copy reads (constant address space, see ctab_t).
+struct SegTabs {
+  const ctab_t *sfirst, *snb, *sdst, *sdoff, *ssrc, *srows, *sunit;
+};
+__device__ __forceinline__ SegTabs seg_tabs(const PlanLayout& L, const int32_t* ws) {
+  const ctab_t* t = (const ctab_t*)ws;
+  return SegTabs{t + L.o_sfirst, t + L.o_snb, t + L.o_sdst, t + L.o_sdoff, t + L.o_ssrc, t + L.o_srows, t + L.o_sunit};
+}
+
+// Load unit u of segment seg: bytes [lo, lo + kCopyChunk) of the segment,
+// clipped to its end by the buffer bounds, read at device scope.
+template <int NT>
+__device__ __forceinline__ void load_unit(const PlanLayout& L, const SegTabs& T, const uint16_t* __restrict__ y,
+                                          const RecvPtrs& recv, int seg, int u, CopyUnit<NT>& U) {
+  const int tid = threadIdx.x;
+  const int64_t d = L.d;
+  const int64_t bytes = (int64_t)T.srows[seg] * d * 2;
+  const int64_t lo = (int64_t)(u - T.sunit[seg]) * kCopyChunk;
+  const int64_t n = min((int64_t)kCopyChunk, bytes - lo);
+  const __amdgpu_buffer_rsrc_t src = copy_rsrc((const char*)(y + (int64_t)T.ssrc[seg] * d) + lo, n);
+  U.dst = T.sdst[seg];
+  U.to = (char*)(recv.p[U.dst] + (int64_t)T.sdoff[seg] * d) + lo;
+  U.n = n;
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b128(src, (k * NT + tid) * 16, 0, kAgentLoad);
+  for (int k = 0; k < CopyUnit<NT>::VPT; ++k)
+    U.v[k] = __builtin_amdgcn_raw_buffer_load_b128(src, (k * NT + tid) * 16, 0, kAgentLoad);
+}
+
+// Store a loaded unit, then take its slot on the destination's emulated
+// link (if any).
+template <int NT>
+__device__ __forceinline__ void store_unit(const CopyCtl& cc, const CopyUnit<NT>& U) {
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t dst = copy_rsrc(U.to, U.n);
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) __builtin_amdgcn_raw_buffer_store_b128(v[k], dst, (k * NT + tid) * 16, 0, kStreamStore);
-  return n;
+  for (int k = 0; k < CopyUnit<NT>::VPT; ++k)
+    __builtin_amdgcn_raw_buffer_store_b128(U.v[k], dst, (k * NT + tid) * 16, 0, kStreamStore);
+  pace_unit(cc, U.dst, U.n);
+}
+
+// The copy loop of one workgroup, software-pipelined over two units in
+// flight: unit j's loads go out before unit j-1's stores, and the two units
+// alternate between two register sets (A, B), so no unit's data is moved
+// between registers.  next(u) gives the workgroup's next unit (-1 when done;
+// it may wait, and must be called by every thread).  Returns 0 if the
+// workgroup must stop (timeout or error).
+template <int NT, class Next>
+__device__ __forceinline__ int copy_units(const PlanLayout& L, int32_t* hdr, const int32_t* ws, const SegTabs& T,
+                                          const uint16_t* __restrict__ y, const uint32_t* __restrict__ flags,
+                                          uint32_t epoch, const RecvPtrs& recv, const CopyCtl& cc, int n_rs,
+                                          int* s_go, Next next) {
+  int seg = 0, ready = -1;
+  CopyUnit<NT> A, B;
+  A.dst = -1;
+  B.dst = -1;
+  // find unit u's segment, waiting for it if it is not the one already
+  // waited for
+  auto enter = [&](int u) __attribute__((always_inline)) {
+    seg = __builtin_amdgcn_readfirstlane(segment_of_unit(T.sunit, n_rs, seg, u));
+    if (seg != ready) {
+      if (!wait_segment(L, hdr, T.sfirst, T.snb, flags, epoch, cc, ws, seg, s_go)) return false;
+      ready = seg;
+    }
+    return true;
+  };
+  for (;;) {
+    int u = next();
+    if (u < 0) break;
+    if (!enter(u)) return 0;
+    load_unit<NT>(L, T, y, recv, seg, u, A);
+    if (B.dst >= 0) store_unit<NT>(cc, B);
+    B.dst = -1;
+    u = next();
+    if (u < 0) break;
+    if (!enter(u)) return 0;
+    load_unit<NT>(L, T, y, recv, seg, u, B);
+    store_unit<NT>(cc, A);
+    A.dst = -1;
+  }
+  if (A.dst >= 0) store_unit<NT>(cc, A);
+  if (B.dst >= 0) store_unit<NT>(cc, B);
+  return 1;
 }
 
 // One consumer workgroup of NT threads; `cid` in [0, n_cons), units assigned
@@ -193,28 +272,16 @@ __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_
                                  const CopyCtl& cc, int cid, int n_cons, int* s_go) {
   int32_t* hdr = ws + L.o_hdr;
   if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
-  const int32_t* sfirst = ws + L.o_sfirst;
-  const int32_t* snb = ws + L.o_snb;
-  const int32_t* sdst = ws + L.o_sdst;
-  const int32_t* sdoff = ws + L.o_sdoff;
-  const int32_t* ssrc = ws + L.o_ssrc;
-  const int32_t* srows = ws + L.o_srows;
-  const int32_t* sunit = ws + L.o_sunit;
+  const SegTabs T = seg_tabs(L, ws);
   // remote segments come first in schedule order; their units end where the
   // first local segment's begin
   const int n_rs = hdr[H_RSEGS];
-  const int U = sunit[n_rs];
-  if (cid >= U) return;
-  int seg = 0, ready = -1;
-  for (int u = cid; u < U; u += n_cons) {
-    seg = segment_of_unit(sunit, n_rs, seg, u);
-    if (seg != ready) {
-      if (!wait_segment(L, hdr, sfirst, snb, flags, epoch, cc, ws, seg, s_go)) return;
-      ready = seg;
-    }
-    const int64_t n = copy_unit<NT>(L, ssrc, sdst, sdoff, srows, sunit, y, recv, seg, u);
-    pace_unit(cc, sdst[seg], n);
-  }
+  const int U = T.sunit[n_rs];
+  int u = cid - n_cons;
+  copy_units<NT>(L, hdr, ws, T, y, flags, epoch, recv, cc, n_rs, s_go, [&]() __attribute__((always_inline)) {
+    u += n_cons;
+    return u < U ? u : -1;
+  });
 }
 
 // Consumer with claimed work, for the overlapped down-GEMM launch: the
@@ -238,42 +305,30 @@ __device__ void consume_claimed(const PlanLayout& L, int32_t* ws, int32_t* claim
                                 const CopyCtl& cc, int* s_word) {
   int32_t* hdr = ws + L.o_hdr;
   if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
-  const int32_t* sfirst = ws + L.o_sfirst;
-  const int32_t* snb = ws + L.o_snb;
-  const int32_t* sdst = ws + L.o_sdst;
-  const int32_t* sdoff = ws + L.o_sdoff;
-  const int32_t* ssrc = ws + L.o_ssrc;
-  const int32_t* srows = ws + L.o_srows;
-  const int32_t* sunit = ws + L.o_sunit;
+  const SegTabs T = seg_tabs(L, ws);
   const int n_rs = hdr[H_RSEGS];
-  const int U = sunit[n_rs];
+  const int U = T.sunit[n_rs];
   const int cu = max(1, min(kClaimUnitsMax, U / (2 * (int)gridDim.x)));   // units per claim
   const int n_claims = (U + cu - 1) / cu;
   const int tid = threadIdx.x;
+  // the claim being copied (k) and the next one, asked for while k is
+  // copied; j: the next unit of claim k
+  int k = -1, j = cu;
   if (tid == 0) s_word[1] = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  int k = s_word[1];
-  __syncthreads();
-  int seg = 0, ready = -1;
-  while (k < n_claims) {
-    // the next claim is in flight while this one is copied
-    if (tid == 0) s_word[1] = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int j = 0; j < cu; ++j) {
-      const int u = k * cu + j;
-      if (u < U) {
-        seg = segment_of_unit(sunit, n_rs, seg, u);
-        if (seg != ready) {
-          if (!wait_segment(L, hdr, sfirst, snb, flags, epoch, cc, ws, seg, s_word)) return;
-          ready = seg;
-        }
-        const int64_t n = copy_unit<NT>(L, ssrc, sdst, sdoff, srows, sunit, y, recv, seg, u);
-        pace_unit(cc, sdst[seg], n);
+  copy_units<NT>(L, hdr, ws, T, y, flags, epoch, recv, cc, n_rs, s_word, [&]() __attribute__((always_inline)) {
+    for (;;) {
+      if (j < cu) {
+        const int u = k * cu + j++;
+        if (u < U) return u;
       }
+      __syncthreads();
+      k = __builtin_amdgcn_readfirstlane(s_word[1]);
+      __syncthreads();
+      if (k >= n_claims) return -1;
+      if (tid == 0) s_word[1] = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      j = 0;
     }
-    __syncthreads();
-    k = s_word[1];
-    __syncthreads();
-  }
+  });
 }
 
 }  // namespace moe

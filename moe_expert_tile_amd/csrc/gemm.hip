@@ -40,11 +40,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
-// The plan's tables, written by the planner's launches and only read here:
-// loads through the constant address space with a wave-uniform index become
-// scalar loads, which the vector memory counter does not track, so the tile
-// setup never waits for the previous tile's output stores.
-typedef const int32_t __attribute__((address_space(4))) ctab_t;
 
 // Tile shapes (compile-time; the defaults are the measured best on MI355X).
 #ifndef MOE_XCD_ROWS
