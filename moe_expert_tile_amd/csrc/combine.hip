@@ -10,12 +10,13 @@ namespace {
 
 constexpr int kConsumerThreads = 256;
 
+template <bool PIPE>
 __global__ __launch_bounds__(kConsumerThreads) void consumer_kernel(PlanLayout L, int32_t* __restrict__ ws,
                                                                    const uint16_t* __restrict__ y,
                                                                    const uint32_t* __restrict__ flags, uint32_t epoch,
                                                                    RecvPtrs recv, CopyCtl cc) {
   __shared__ int s_go;
-  consume_segments<kConsumerThreads>(L, ws, y, flags, epoch, recv, cc, blockIdx.x, gridDim.x, &s_go);
+  consume_segments<kConsumerThreads, PIPE>(L, ws, y, flags, epoch, recv, cc, blockIdx.x, gridDim.x, &s_go);
 }
 
 // Per-row ablation of the copy (the alternative the tile-signal notes weigh
@@ -95,7 +96,16 @@ hipError_t launch_consumer_rows(const PlanLayout& L, int32_t* ws, const uint16_t
 
 hipError_t launch_consumer(const PlanLayout& L, int32_t* ws, const uint16_t* y, const uint32_t* flags,
                            uint32_t epoch, const RecvPtrs& recv, const CopyCtl& cc, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(consumer_kernel, dim3(grid), dim3(kConsumerThreads), 0, s, L, ws, y, flags, epoch, recv, cc);
+  // a grid of at most one workgroup per CU (a consumer budget) gives each
+  // workgroup many units: two in flight per workgroup.  Larger grids (the
+  // default, one workgroup per unit) take the variant with half the
+  // registers, so more workgroups fit a CU.
+  if (grid <= kMaxProducers)
+    hipLaunchKernelGGL(consumer_kernel<true>, dim3(grid), dim3(kConsumerThreads), 0, s, L, ws, y, flags, epoch, recv,
+                       cc);
+  else
+    hipLaunchKernelGGL(consumer_kernel<false>, dim3(grid), dim3(kConsumerThreads), 0, s, L, ws, y, flags, epoch, recv,
+                       cc);
   return hipGetLastError();
 }
 

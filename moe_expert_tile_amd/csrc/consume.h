@@ -33,6 +33,8 @@
 // leaves.
 #pragma once
 
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -69,7 +71,8 @@ constexpr int kStreamStore = 18;
 
 // Segment of copy unit u, searching forward from `seg` (units only grow):
 // a few steps ahead, then a binary search over the rest.
-__device__ __forceinline__ int segment_of_unit(const ctab_t* sunit, int n_rs, int seg, int u) {
+template <class P>
+__device__ __forceinline__ int segment_of_unit(P sunit, int n_rs, int seg, int u) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (sunit[seg + 1] > u) return seg;
@@ -90,8 +93,9 @@ __device__ __forceinline__ int segment_of_unit(const ctab_t* sunit, int n_rs, in
 // ticks of the 100 MHz clock; on timeout the plan's error word becomes
 // MOE_ETIMEOUT.  Returns 0 if the workgroup must stop.  Every thread of the
 // workgroup calls it.
-__device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, const ctab_t* sfirst,
-                                            const ctab_t* snb, const uint32_t* __restrict__ flags, uint32_t epoch,
+template <class P>
+__device__ __forceinline__ int wait_segment(const PlanLayout& L, int32_t* hdr, P sfirst,
+                                            P snb, const uint32_t* __restrict__ flags, uint32_t epoch,
                                             const CopyCtl& cc, const int32_t* ws, int seg, int* s_go) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int tpb = L.dn_tpb;
@@ -179,19 +183,27 @@ struct CopyUnit {
   int dst;   // -1: no unit
 };
 
-// The segment tables the copy reads (constant address space, see ctab_t).
+// The segment tables the copy reads, through P: the constant address space
+// (const ctab_t*, scalar loads) where a workgroup copies many units with
+// loads and stores in flight, so that reading a table does not wait for
+// them; plain pointers (vector loads) where each workgroup copies one unit:
+// with thousands of such workgroups the scalar loads measured 7% slower.
+template <class P>
 struct SegTabs {
-  const ctab_t *sfirst, *snb, *sdst, *sdoff, *ssrc, *srows, *sunit;
+  P sfirst, snb, sdst, sdoff, ssrc, srows, sunit;
 };
-__device__ __forceinline__ SegTabs seg_tabs(const PlanLayout& L, const int32_t* ws) {
-  const ctab_t* t = (const ctab_t*)ws;
-  return SegTabs{t + L.o_sfirst, t + L.o_snb, t + L.o_sdst, t + L.o_sdoff, t + L.o_ssrc, t + L.o_srows, t + L.o_sunit};
+template <class P>
+__device__ __forceinline__ SegTabs<P> seg_tabs(const PlanLayout& L, const int32_t* ws) {
+  const P t = (P)ws;
+  return SegTabs<P>{t + L.o_sfirst, t + L.o_snb, t + L.o_sdst, t + L.o_sdoff, t + L.o_ssrc, t + L.o_srows, t + L.o_sunit};
 }
+template <bool PIPE>
+using SegPtr = typename std::conditional<PIPE, const ctab_t*, const int32_t*>::type;
 
 // Load unit u of segment seg: bytes [lo, lo + kCopyChunk) of the segment,
 // clipped to its end by the buffer bounds, read at device scope.
-template <int NT>
-__device__ __forceinline__ void load_unit(const PlanLayout& L, const SegTabs& T, const uint16_t* __restrict__ y,
+template <int NT, class P>
+__device__ __forceinline__ void load_unit(const PlanLayout& L, const SegTabs<P>& T, const uint16_t* __restrict__ y,
                                           const RecvPtrs& recv, int seg, int u, CopyUnit<NT>& U) {
   const int tid = threadIdx.x;
   const int64_t d = L.d;
@@ -219,14 +231,18 @@ __device__ __forceinline__ void store_unit(const CopyCtl& cc, const CopyUnit<NT>
   pace_unit(cc, U.dst, U.n);
 }
 
-// The copy loop of one workgroup, software-pipelined over two units in
-// flight: unit j's loads go out before unit j-1's stores, and the two units
-// alternate between two register sets (A, B), so no unit's data is moved
-// between registers.  next(u) gives the workgroup's next unit (-1 when done;
-// it may wait, and must be called by every thread).  Returns 0 if the
-// workgroup must stop (timeout or error).
-template <int NT, class Next>
-__device__ __forceinline__ int copy_units(const PlanLayout& L, int32_t* hdr, const int32_t* ws, const SegTabs& T,
+// The copy loop of one workgroup.  PIPE: software-pipelined over two units
+// in flight -- unit j's loads go out before unit j-1's stores, and the two
+// units alternate between two register sets (A, B), so no unit's data is
+// moved between registers; for a few workgroups with many units each.
+// Without PIPE each unit is stored before the next is loaded, with half the
+// registers, so more workgroups fit a CU: for grids of one unit per
+// workgroup.  next() gives the workgroup's next unit (-1 when done; it may
+// wait, and must be called by every thread).  Returns 0 if the workgroup
+// must stop (timeout or error).
+template <int NT, bool PIPE, class Next>
+__device__ __forceinline__ int copy_units(const PlanLayout& L, int32_t* hdr, const int32_t* ws,
+                                          const SegTabs<SegPtr<PIPE>>& T,
                                           const uint16_t* __restrict__ y, const uint32_t* __restrict__ flags,
                                           uint32_t epoch, const RecvPtrs& recv, const CopyCtl& cc, int n_rs,
                                           int* s_go, Next next) {
@@ -249,6 +265,11 @@ __device__ __forceinline__ int copy_units(const PlanLayout& L, int32_t* hdr, con
     if (u < 0) break;
     if (!enter(u)) return 0;
     load_unit<NT>(L, T, y, recv, seg, u, A);
+    if (!PIPE) {
+      store_unit<NT>(cc, A);
+      A.dst = -1;
+      continue;
+    }
     if (B.dst >= 0) store_unit<NT>(cc, B);
     B.dst = -1;
     u = next();
@@ -266,19 +287,19 @@ __device__ __forceinline__ int copy_units(const PlanLayout& L, int32_t* hdr, con
 // One consumer workgroup of NT threads; `cid` in [0, n_cons), units assigned
 // statically (standalone consumer kernel).  `s_go` is one int of the
 // caller's LDS.
-template <int NT>
+template <int NT, bool PIPE>
 __device__ void consume_segments(const PlanLayout& L, int32_t* ws, const uint16_t* __restrict__ y,
                                  const uint32_t* __restrict__ flags, uint32_t epoch, const RecvPtrs& recv,
                                  const CopyCtl& cc, int cid, int n_cons, int* s_go) {
   int32_t* hdr = ws + L.o_hdr;
   if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
-  const SegTabs T = seg_tabs(L, ws);
+  const SegTabs<SegPtr<PIPE>> T = seg_tabs<SegPtr<PIPE>>(L, ws);
   // remote segments come first in schedule order; their units end where the
   // first local segment's begin
   const int n_rs = hdr[H_RSEGS];
   const int U = T.sunit[n_rs];
   int u = cid - n_cons;
-  copy_units<NT>(L, hdr, ws, T, y, flags, epoch, recv, cc, n_rs, s_go, [&]() __attribute__((always_inline)) {
+  copy_units<NT, PIPE>(L, hdr, ws, T, y, flags, epoch, recv, cc, n_rs, s_go, [&]() __attribute__((always_inline)) {
     u += n_cons;
     return u < U ? u : -1;
   });
@@ -305,7 +326,7 @@ __device__ void consume_claimed(const PlanLayout& L, int32_t* ws, int32_t* claim
                                 const CopyCtl& cc, int* s_word) {
   int32_t* hdr = ws + L.o_hdr;
   if (__hip_atomic_load(hdr + H_ERROR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
-  const SegTabs T = seg_tabs(L, ws);
+  const SegTabs<SegPtr<true>> T = seg_tabs<SegPtr<true>>(L, ws);
   const int n_rs = hdr[H_RSEGS];
   const int U = T.sunit[n_rs];
   const int cu = max(1, min(kClaimUnitsMax, U / (2 * (int)gridDim.x)));   // units per claim
@@ -315,7 +336,7 @@ __device__ void consume_claimed(const PlanLayout& L, int32_t* ws, int32_t* claim
   // copied; j: the next unit of claim k
   int k = -1, j = cu;
   if (tid == 0) s_word[1] = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  copy_units<NT>(L, hdr, ws, T, y, flags, epoch, recv, cc, n_rs, s_word, [&]() __attribute__((always_inline)) {
+  copy_units<NT, true>(L, hdr, ws, T, y, flags, epoch, recv, cc, n_rs, s_word, [&]() __attribute__((always_inline)) {
     for (;;) {
       if (j < cu) {
         const int u = k * cu + j++;
