@@ -292,8 +292,8 @@ def main():
     nrs = hdr["remote_segments"]
     seg_rows = int(share.array("seg_rows", nrs).sum()) if nrs else 0
     # rows the GEMMs' tiles hold: 256-row tiles over every expert's real
-    # rows (gate/up) and over the real rows of whole bands (down); their
-    # unused rows are not multiplied in the down GEMM, but counted here
+    # rows, in both GEMMs; the 32-row blocks of a tile that hold no row are
+    # not multiplied, but counted here
     gu_rows = 256 * hdr["gateup_row_tiles"]
     dn_rows = 256 * hdr["down_row_tiles"]
     work = algorithmic(cfg, R, M, seg_rows, gu_rows, dn_rows)

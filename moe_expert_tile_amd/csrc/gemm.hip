@@ -49,11 +49,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #define MOE_XCD_ROWS 2
 #endif
 #ifndef MOE_XCD_ROWS_DN
-// The same for the down GEMM.  Measured over packed down tiles (same box,
-// serial mode, two passes): 1 takes the DeepSeek-like down GEMM from
-// 1663-1693 to 1621-1636 us and leaves the Mixtral- and Qwen3-like ones
+// The same for the down GEMM.  Measured over an earlier band-packed tiling
+// (same box, serial mode, two passes): 1 takes the DeepSeek-like down GEMM
+// from 1663-1693 to 1621-1636 us and leaves the Mixtral- and Qwen3-like ones
 // within noise; 4 and 8 are 2-4% slower there, and per-XCD blocks of 4 x 8,
-// 2 x 16, 16 x 2 or 32 x 1 tiles are no better than 8 x 4.
+// 2 x 16, 16 x 2 or 32 x 1 tiles are no better than 8 x 4.  Over the
+// current tiles 2 is 0.6-3% slower than 1 (DeepSeek- and Qwen3-like).
 #define MOE_XCD_ROWS_DN 1
 #endif
 #ifndef MOE_GU_WAVES_M
@@ -1080,7 +1081,7 @@ using GuCfg = Cfg<256, 256, MOE_GU_WAVES_M, MOE_GU_WAVES_N, MOE_GU_BK, MOE_GU_SA
 static_assert(GuCfg::BK == kGuBK, "the host sizes the stream-K scratch with this K step");
 using Dn256 = Cfg<256, 256, MOE_DN_WAVES_M, MOE_DN_WAVES_N, MOE_DN_BK, MOE_DN_SA, MOE_DN_SB>;
 static_assert(Dn256::BK == kDnBK, "the host sizes the stream-K scratch with this K step");
-static_assert(Dn256::BM == kDnBM, "the planner packs bands into tiles of this height");
+static_assert(Dn256::BM == kDnBM, "the planner cuts the down tiles at this height");
 
 __global__ __launch_bounds__(256) void clear_counters_kernel(Scratch sc) {
   for (int i = threadIdx.x; i < 2 * kMaxProducers; i += blockDim.x) sc.sk_ctr[i] = 0;
