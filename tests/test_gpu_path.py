@@ -93,6 +93,25 @@ def test_combine_writes_exactly_the_plan(name):
         assert np.array_equal(got, exp), f"owner {o}"
 
 
+@pytest.mark.parametrize("name", ["tiny_unit", "qwen3", "dsv3_skew", "decode_tb32", "decode_tb64"])
+@pytest.mark.parametrize("serial", [True, False])
+def test_every_band_head_and_tail_flag_is_set(name, serial):
+    """After a compute call both flags of every band -- head and tail, for
+    every column tile -- equal the call's epoch, remote and local bands alike
+    (a down tile may end inside a band, so a band's two flags may come from
+    two tiles; the consumer only waits on remote bands, so this is what shows
+    that no local band's flag is missed), and no flag word past the plan's
+    bands is written."""
+    import moe_expert_tile_amd as m
+    c, share, _, _ = planned(name, m.MODE_SERIAL if serial else m.MODE_OVERLAP)
+    hdr = share.header()
+    n_used = hdr["down_tiles"]
+    assert n_used == 2 * hdr["bands"] * (share.shape.hidden // 256)
+    f = share.flags.cpu().numpy().view(np.uint32)
+    assert np.all(f[:n_used] == share.epoch), np.nonzero(f[:n_used] != share.epoch)[0][:8]
+    assert np.all(f[n_used:] == 0)
+
+
 @pytest.mark.parametrize("name", ["tiny_unit", "mixtral", "qwen3", "decode_tb32", "dsv3_skew"])
 def test_per_row_copy_equals_the_segment_copy(name):
     """The per-row ablation of the copy (the notes' alternative to the
