@@ -346,8 +346,13 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     }
   }
   if (hdr[H_ERROR] != 0) return;
-  if (overlapped && tid == 0)
-    __hip_atomic_fetch_add(g.sc.claim + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // overlapped launch: each producer raises the "started" count (which
+  // lets producers that run out of tiles join the consumer once every
+  // producer holds its CU) right after its first tile's prologue loads, or
+  // when it leaves without a tile.  Raised at the start, the one word's
+  // atomics of all producers delayed their first loads (the vector memory
+  // counter retires in order): decode-size down GEMMs 44-48 -> 42-46 us.
+  bool need_start = overlapped;
 
   // Row tiles are taken in two regions, each in grouped order: for the down
   // GEMM the remote bands' tiles [0, n_mt_r) before the local bands' (so the
@@ -611,6 +616,10 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
     if (KTt > 1) {
       if constexpr (C::SA == 3) issue_a(1);
       if constexpr (C::SB == 3) issue_b(1);
+    }
+    if (need_start) {
+      if (tid == 0) __hip_atomic_fetch_add(g.sc.claim + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      need_start = false;
     }
     if constexpr (FLAGS) {
       if (pend_nt >= 0) {
@@ -1053,6 +1062,7 @@ void grouped_gemm_kernel(PlanLayout L, GemmArgs g, RecvPtrs recv) {
       __builtin_amdgcn_s_barrier();
       publish(pend_nt);
     }
+    if (need_start && tid == 0) __hip_atomic_fetch_add(g.sc.claim + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) stamp_max(hdr, H_T_PROD_END);
     if (overlapped && items > 0) {
       // out of tiles: help copy the remaining remote segments, but only once
