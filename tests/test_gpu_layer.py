@@ -8,7 +8,9 @@
   receive offsets of all ranks' plans against each other.
 * Edge cases: no tokens at all, ragged owners (one empty), a single rank
   (no remote bands), a hot expert, k = E, a band height that is not a power of
-  two, the largest band height, a large merge factor.
+  two, band heights that do not divide the 256-row GEMM tile, the largest
+  band height, a large merge factor, and 16 or 64 owners (up to 64 owner
+  groups in one down tile).
 * Failure handling forced from the host, with every kernel exiting normally:
   an expert id out of range and a received-row count that disagrees with the
   routing are reported as MOE_EROUTING and later kernels do nothing; a
@@ -98,12 +100,16 @@ EDGE_CASES = {
     "k_equals_E": dict(W=2, E_l=2, k=4, tokens=[33, 70], rank=1),
     "tb96": dict(W=3, E_l=2, k=2, tokens=[120, 80, 100], tb=96, mgb=2),
     "tb256_wide": dict(W=5, E_l=1, k=1, tokens=[300, 10, 260, 0, 513], tb=256, d=512, f=384),
-    # band heights that do not divide 256: the down GEMM cuts each band into
-    # 32-row tiles (160: five, 224: seven) or 64-row tiles (192: three, with
-    # K = 1024 long enough to split the single round of tiles along K)
+    # band heights that do not divide 256: the down GEMM's 256-row tiles end
+    # inside bands, whose head and tail flags then come from two tiles
+    # (tb192 with K = 1024, long enough to split the single round along K)
     "tb160": dict(W=3, E_l=2, k=2, tokens=[460, 190, 530], tb=160, mgb=2, rank=1),
     "tb192": dict(W=3, E_l=2, k=2, tokens=[600, 400, 500], tb=192, f=1024, mgb=2),
     "tb224": dict(W=4, E_l=1, k=2, tokens=[500, 350, 0, 610], tb=224, mgb=3, rank=3),
+    # many owner groups in one down tile: the epilogue takes one wavefront
+    # lane per group (64 at most), each with its own padding and flags
+    "w64_tb32": dict(W=64, E_l=1, k=4, tokens=[60] * 64, tb=32, mgb=2, rank=5),
+    "w16_tb64": dict(W=16, E_l=4, k=4, tokens=[100 + 13 * o for o in range(16)], tb=64, rank=15),
 }
 
 
