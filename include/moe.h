@@ -17,9 +17,11 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call is asynchronous on it; nothing synchronises with the host
  *     except moe_device_status.
- *   - The caller owns every buffer.  The library allocates no device memory,
- *     creates no streams or events, and keeps only a per-device cache of the
- *     compute-unit count and LDS limit.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     (moe_expert_combine_noalloc's scratch is a static array of the code
+ *     object), creates no streams or events, and keeps only a per-device
+ *     cache of the compute-unit count, the LDS limit and that array's
+ *     address.
  *   - Errors the device detects (an expert id out of range, a received-row
  *     count that disagrees with the routing, a consumer wait that timed out)
  *     are written to an error word inside the plan workspace and reported by
