@@ -118,7 +118,8 @@ def test_edge_case_rank_share(case_name):
     """Plan bit-exact; every layout row's y within tolerance; the receive
     buffers hold exactly the plan's rows; the rank's output within tolerance
     of the oracle fed with the same receive buffer; with gathered rows (no
-    layout X) the same y and receive buffers bit for bit."""
+    layout X), and with group-batched signals, the same y and receive
+    buffers bit for bit."""
     import moe_expert_tile_amd as m
     p = dict(EDGE_CASES[case_name])
     cfg, ids, w = _custom(**p)
@@ -171,6 +172,19 @@ def test_edge_case_rank_share(case_name):
     sh.plan(ids_d, xr, materialize=False)
     sh.combine(dev_bf16(wgu), dev_bf16(wd), mode=m.MODE_OVERLAP, consumer_cus=16,
                x_recv=xr if pl.R else None)
+    assert sh.status() == m.MOE_OK
+    if pl.M:
+        assert np.array_equal(host_bits(sh.y[: pl.M]), Y[: pl.M])
+    for o in range(cfg.W):
+        assert np.array_equal(host_bits(sh.recv[o]), recv_mat[o]), o
+    # and with group-batched signals (one ready counter per (expert,
+    # destination) group, raised by the band heads and tails each tile
+    # holds): the same y and receive buffers, bit for bit
+    for o in range(cfg.W):
+        sh.recv[o].copy_(dev_bf16(sentinel[o]))
+    sh.y.fill_(float("nan"))
+    sh.plan(ids_d, xr)
+    sh.combine(dev_bf16(wgu), dev_bf16(wd), mode=m.MODE_OVERLAP, consumer_cus=16, signal=m.SIGNAL_GROUP)
     assert sh.status() == m.MOE_OK
     if pl.M:
         assert np.array_equal(host_bits(sh.y[: pl.M]), Y[: pl.M])
