@@ -124,6 +124,9 @@ def algorithmic(cfg, R, M, n_seg_rows, gu_rows, dn_rows):
         "plan_bytes": 4.0 * N * k + 2.0 * d * R + 2.0 * d * M + 4.0 * M + 4.0 * T_r * k,
         "combine_bytes": 4.0 * d * n_seg_rows,   # valid rows read + written
         "scale_bytes": 2.0 * d * k * T_r + 2.0 * d * T_r + 8.0 * k * T_r,
+        # the bytes the gate/up GEMM must move at least: X's real rows and
+        # every local expert's W_gate_up read once, h written once
+        "gateup_bytes": 2.0 * d * R + 4.0 * cfg.E_l * f * d + 2.0 * f * R,
     }
 
 
@@ -440,6 +443,7 @@ def main():
             "algorithmic": "4*d*f*R flops per launch (R real rows; no padding row is computed)",
             "bound": "mfma", "achieved": round(gu_tflops / 1e12, 2), "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16, 4), "traffic": measured_traffic(args.workload),
+            "traffic_algorithmic": work["gateup_bytes"],
         },
         "stages_us": {
             "plan_in_step": round(t_plan * 1e6, 2), "gateup_gemm": round(t_gu * 1e6, 2),
