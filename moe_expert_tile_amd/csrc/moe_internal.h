@@ -196,7 +196,7 @@ inline BuildLds build_lds(int W, int E_l, int bands_cap, bool bands) {
 }
 // pair placers (workgroups 1.. of the second launch)
 struct PlaceLds {
-  int run, wc, run_g, wc_g, bp, pre_g, base_g, srow, scrow, sh, misc, total;
+  int run, wc, run_g, wc_g, bp, pre_g, base_g, srow, scrow, pst, pct, sh, misc, total;
 };
 #if defined(__HIPCC__)
 __host__ __device__
@@ -213,6 +213,8 @@ inline PlaceLds place_lds(int E_l, int E, int nw) {
   s.base_g = o; o += E;
   s.srow = o; o += E_l;
   s.scrow = o; o += E_l;
+  s.pst = o; o += kPlanThreads;   // padding runs of up to kPlanThreads groups: first row
+  s.pct = o; o += kPlanThreads;   // ... and length
   s.sh = o; o += 32;
   s.misc = o; o += 8;
   s.total = o;

@@ -676,20 +676,35 @@ __device__ void place_pairs(const PlanLayout& L, const int32_t* __restrict__ top
   const int recv_base = agent_load(ws + L.o_obase + o) + before;
   int32_t* src = ws + L.o_src;
   // the padding entries of src_index: the tail of every remote group, the
-  // groups shared out over the placers
+  // groups shared out over the placers (groups b, b + NB, ...).  One thread
+  // per group reads its size and first row (all of them in one round trip),
+  // then the workgroup writes the -1 entries group by group
   {
     const int NGR = E_l * (W - 1);
     const int tb = L.tb_m;
-    for (int gi = b; gi < NGR; gi += L.NB) {
-      const int e = fdiv(gi, L.div_wm1), q = gi - e * (W - 1);
-      const int og = q < L.r ? q : q + 1;
-      const int n = agent_load(gc + e * W + og);
-      const int st = agent_load(grow + e * W + og) + n;
-      const int ct = fdiv(n + tb - 1, L.div_tb) * tb - n;
-      for (int x = tid; x < ct; x += nt) src[st + x] = -1;
+    int* pst = smem + S.pst;
+    int* pct = smem + S.pct;
+    const int ng = NGR > b ? (NGR - b + L.NB - 1) / L.NB : 0;   // this placer's groups
+    for (int j0 = 0; j0 < ng; j0 += nt) {
+      const int j = j0 + tid;
+      if (j < ng) {
+        const int gi = b + j * L.NB;
+        const int e = fdiv(gi, L.div_wm1), q = gi - e * (W - 1);
+        const int og = q < L.r ? q : q + 1;
+        const int n = agent_load(gc + e * W + og);
+        pst[tid] = agent_load(grow + e * W + og) + n;
+        pct[tid] = fdiv(n + tb - 1, L.div_tb) * tb - n;
+      }
+      __syncthreads();
+      const int m = min(nt, ng - j0);
+      for (int jj = 0; jj < m; ++jj) {
+        const int st = pst[jj], ct = pct[jj];
+        for (int x = tid; x < ct; x += nt) src[st + x] = -1;
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
+  __syncthreads();   // srow, scrow complete
   int32_t* cmp_row = ws + L.o_cmprow;
   int32_t* cmp_src = ws + L.o_cmpsrc;
   int32_t* pos = ws + L.o_pos;
