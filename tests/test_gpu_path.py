@@ -136,6 +136,30 @@ def test_per_row_copy_equals_the_segment_copy(name):
         assert np.array_equal(host_bits(share.recv[o][: exp.shape[0]]), exp), f"owner {o}"
 
 
+@pytest.mark.parametrize("name,blocks", [("mixtral", 16), ("qwen3", 8), ("qwen3", 256), ("dsv3_skew", 16),
+                                         ("decode_tb32", 4)])
+def test_copy_with_few_consumer_workgroups(name, blocks):
+    """The standalone consumer on a small grid (each workgroup copies many
+    units, two in flight): after a serial call, with the receive buffers
+    refilled, a copy-only call with `blocks` workgroups writes exactly the
+    plan applied to y."""
+    import moe_expert_tile_amd as m
+    c, share, _, _ = planned(name, m.MODE_SERIAL)
+    cfg, pl = c["cfg"], c["plan"]
+    for o in range(cfg.W):
+        share.recv[o].copy_(dev_bf16(synth.foreign_rows(cfg, o)))
+    share.combine(None, None, mode=m.MODE_COPY_ONLY, epoch=share.epoch, consumer_blocks=blocks)
+    assert share.status() == m.MOE_OK
+    Y = host_bits(share.y[:pl.M])
+    written = OC.written_rows(pl)
+    for o in range(cfg.W):
+        exp = synth.foreign_rows(cfg, o)
+        if o != cfg.rank:   # the rank's own rows come from the down GEMM, not the copy
+            dst, src = written[o]
+            exp[dst] = Y[src]
+        assert np.array_equal(host_bits(share.recv[o][: exp.shape[0]]), exp), f"owner {o}"
+
+
 @pytest.mark.parametrize("name", ["tiny_unit", "mixtral", "qwen3", "decode_tb32", "dsv3_skew"])
 def test_overlapped_combine_over_epochs(name):
     """Overlapped calls, each with y poisoned by NaN and the receive buffers
