@@ -15,7 +15,10 @@ Zipf(1.2) expert popularity, tb_M=256), rank 0's share: rank 0 hosts the
 
 Prints one JSON line.  value = tokens/s = (N / W) / (time per step), with N
 the layer's tokens over all W owners: the per-GPU rate of the layer if every
-rank took as long as rank 0.  routed rows/s = R / (time per step).
+rank took as long as rank 0.  routed rows/s = R / (time per step).  The
+timed steps carry no events; per-stage times (means in stages_us, median and
+10th / 90th percentiles in stage_spread_us) come from as many steps again
+with events around every call.
 """
 from __future__ import annotations
 
@@ -282,12 +285,26 @@ def main():
     def avg(pairs):
         return float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e-3
 
+    def spread(pairs):
+        # median and 10th / 90th percentiles over the instrumented steps, us
+        v = np.array([a.elapsed_time(b) for a, b in pairs]) * 1e3
+        return {"median": round(float(np.median(v)), 2), "p10": round(float(np.percentile(v, 10)), 2),
+                "p90": round(float(np.percentile(v, 90)), 2)}
+
     t_plan = avg([(e[0], e[1]) for e in ev_plan])
     t_gu = avg([(e[0], e[1]) for e in ev_comb])
     t_dn = avg([(e[2], e[3]) for e in ev_comb])
     t_cons = avg([(e[4], e[5]) for e in ev_comb])
     t_ec = avg([(e[0], ev_scale[i][0]) for i, e in enumerate(ev_comb)])
     t_scale = avg([(e[0], e[1]) for e in ev_scale])
+    stage_spread = {
+        "plan": spread([(e[0], e[1]) for e in ev_plan]),
+        "gateup_gemm": spread([(e[0], e[1]) for e in ev_comb]),
+        "down_gemm": spread([(e[2], e[3]) for e in ev_comb]),
+        "expert_combine": spread([(e[0], ev_scale[i][0]) for i, e in enumerate(ev_comb)]),
+        "scale": spread([(e[0], e[1]) for e in ev_scale]),
+        "step": spread([(ev_plan[i][0], ev_scale[i][1]) for i in range(n_ev)]),
+    }
     hdr = share.header()
     M = hdr["M"]
     # the consumer moves the remote segments (local rows are written by the
@@ -416,6 +433,9 @@ def main():
             raise SystemExit(f"device status after gathered-row steps: {m.status_string(st)}")
 
     gu_tflops = work["gateup_flop"] / t_gu
+    # producer workgroups of the down GEMM, one per CU: the CUs the consumer
+    # does not hold in the overlapped launch (rounded down to whole XCDs)
+    n_prod = (256 - args.consumer_cus) // 8 * 8 if mode == m.MODE_OVERLAP else 256
     tokens_per_rank = cfg.N / cfg.W   # N / W: the layer's tokens per rank
     result = {
         "metric": METRIC,
@@ -459,6 +479,10 @@ def main():
             "scale_cold_cache": round(t_scale_cold * 1e6, 2),
             "plan_cold_cache": round(t_plan_cold * 1e6, 2),
         },
+        # the instrumented steps' stage times (the means above) as median
+        # and 10th / 90th percentiles; "step" runs from the plan's first
+        # event to the scale's last, so it includes the event records
+        "stage_spread_us": stage_spread,
         "rates": {
             # primary bandwidth figures: each launch alone after a 1 GiB read
             # (a cold Infinity Cache), so the bytes come from HBM
@@ -468,6 +492,9 @@ def main():
             "gateup_TFLOPs": round(gu_tflops / 1e12, 2),
             "down_TFLOPs": round(work["down_flop"] / t_dn / 1e12, 2),
             "down_frac_mfma": round(work["down_flop"] / t_dn / PEAK_BF16, 4),
+            # the overlapped down GEMM against the peak of the CUs its
+            # producers hold (the launch's other workgroups are the consumer)
+            "down_frac_mfma_producer_cus": round(work["down_flop"] / t_dn / (PEAK_BF16 * n_prod / 256), 4),
             "gateup_frac_mfma_executed": round(work["gateup_flop_executed"] / t_gu / PEAK_BF16, 4),
             "down_frac_mfma_executed": round(work["down_flop_executed"] / t_dn / PEAK_BF16, 4),
             "plan_GBs_cold": round(work["plan_bytes"] / t_plan_cold / 1e9, 1),
