@@ -83,11 +83,17 @@ def test_full_layer_equals_definition(name, mode):
     assert ratio <= 1.0
 
 
-def _custom(W, E_l, k, tokens, d=256, f=256, tb=32, mgb=1, seed=0, hot=None, rank=0):
+def _custom(W, E_l, k, tokens, d=256, f=256, tb=32, mgb=1, seed=0, hot=None, rank=0, fixed=None):
+    """A small layer; `fixed` (k expert ids) routes every token to the same
+    experts instead of drawing them."""
     assert tb % 32 == 0 and 32 <= tb <= 256 and d % 256 == 0 and f % 128 == 0
     cfg = synth.MoEConfig("custom", W, W * E_l, tuple(tokens), d, f, k, tb, seed=seed, mgb=mgb, rank=rank)
     rng = np.random.default_rng(seed)
-    ids = synth.random_routing_case(rng, W, E_l, k, list(tokens), hot=hot)
+    if fixed is not None:
+        assert len(fixed) == k and len(set(fixed)) == k
+        ids = np.tile(np.asarray(fixed, dtype=np.int32), (int(sum(tokens)), 1))
+    else:
+        ids = synth.random_routing_case(rng, W, E_l, k, list(tokens), hot=hot)
     w = rng.random((cfg.N, k)).astype(np.float32)
     return cfg, ids, w
 
@@ -110,6 +116,12 @@ EDGE_CASES = {
     # lane per group (64 at most), each with its own padding and flags
     "w64_tb32": dict(W=64, E_l=1, k=4, tokens=[60] * 64, tb=32, mgb=2, rank=5),
     "w16_tb64": dict(W=16, E_l=4, k=4, tokens=[100 + 13 * o for o in range(16)], tb=64, rank=15),
+    # every group an exact multiple of tb_M: no padding row anywhere (M = R)
+    "exact_multiples": dict(W=3, E_l=2, k=2, tokens=[64, 128, 96], fixed=[1, 0]),
+    # the rank routes nothing to itself: its local group is empty
+    "local_empty": dict(W=3, E_l=2, k=2, tokens=[200, 0, 150], rank=1),
+    # every row from one remote owner
+    "one_owner": dict(W=4, E_l=2, k=2, tokens=[0, 0, 333, 0]),
 }
 
 
