@@ -58,3 +58,14 @@ def test_host_info_names_the_cpu_share():
     info = bench.host_info()
     assert 1 <= info["threads"] <= info["affinity_cpus"]
     assert info["cpu_model"] and info["blas"]
+
+
+def test_more_than_one_gpu_is_refused():
+    """The bench measures one GPU: --gpus N > 1 exits at once with a message
+    (before torch is imported), so no multi-GPU figure is ever printed."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2", "--steps", "1", "--warmup", "0"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
