@@ -394,12 +394,17 @@ def main():
             end_prod, end_cons = share.end_stamps()
             tails.append(max(0, end_cons - end_prod) * 1e-8)
         tail = float(np.median(tails))
+    # the serial mode's warm-up steps carry events: the GEMMs alone, the
+    # down GEMM on every CU with no consumer beside it
     n_serial = 10
-    for _ in range(3):
+    ev_ser = [m.timing_events(6) for _ in range(3)]
+    for i in range(3):
         share.plan(ids_d, xr_d)
-        share.combine(wgu_d, wd_d, mode=m.MODE_SERIAL, **cx)
+        share.combine(wgu_d, wd_d, mode=m.MODE_SERIAL, events=ev_ser[i], **cx)
         share.scale(w_r)
     torch.cuda.synchronize()
+    t_gu_ser = float(np.median([e[0].elapsed_time(e[1]) for e in ev_ser])) * 1e-3
+    t_dn_ser = float(np.median([e[2].elapsed_time(e[3]) for e in ev_ser])) * 1e-3
     t0s = time.perf_counter()
     for _ in range(n_serial):
         share.plan(ids_d, xr_d)
@@ -478,6 +483,9 @@ def main():
             "device_copy_same_bytes_cold_cache": round(t_dev_copy_cold * 1e6, 2) if t_dev_copy_cold else None,
             "scale_cold_cache": round(t_scale_cold * 1e6, 2),
             "plan_cold_cache": round(t_plan_cold * 1e6, 2),
+            # serial mode (median of 3 steps): each GEMM alone on every CU
+            "gateup_gemm_serial": round(t_gu_ser * 1e6, 2),
+            "down_gemm_serial": round(t_dn_ser * 1e6, 2),
         },
         # the instrumented steps' stage times (the means above) as median
         # and 10th / 90th percentiles; "step" runs from the plan's first
@@ -495,6 +503,7 @@ def main():
             # the overlapped down GEMM against the peak of the CUs its
             # producers hold (the launch's other workgroups are the consumer)
             "down_frac_mfma_producer_cus": round(work["down_flop"] / t_dn / (PEAK_BF16 * n_prod / 256), 4),
+            "down_frac_mfma_serial": round(work["down_flop"] / t_dn_ser / PEAK_BF16, 4),
             "gateup_frac_mfma_executed": round(work["gateup_flop_executed"] / t_gu / PEAK_BF16, 4),
             "down_frac_mfma_executed": round(work["down_flop_executed"] / t_dn / PEAK_BF16, 4),
             "plan_GBs_cold": round(work["plan_bytes"] / t_plan_cold / 1e9, 1),
